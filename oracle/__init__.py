@@ -1,0 +1,37 @@
+"""Reference oracle for paged-KV decode attention — TEST INFRASTRUCTURE ONLY.
+
+This package is a plain, slow, obviously-correct CPU implementation of what the
+paged-KV decode path computes.  It exists to check the HIP library, never to
+stand in for it: only the test-suite, the smoke check in ``__graft_entry__`` and
+the ``cpu_baseline`` leg of ``bench.py`` may import it.  The product package
+(``paged_attention_amd``) never imports, links or calls anything here, and this
+package imports nothing from the product package.
+
+Floating point is carried in float64 on inputs upcast from their stored dtype;
+integer and byte work (allocator, slot mapping, scatter, block copy) is exact.
+
+Sources (the pages are cited by address and section; none carries a title line):
+
+* ``hnwysp.cn/news/103996`` — KV-cache sizing, shared pool, paging, block table
+  with refcounts and copy-on-write, ``alloc_block``/``free_block``.
+* ``icman.com.cn/news/78786`` — PagedAttention and prefix caching: byte formula,
+  block-size table, pool arithmetic, kernel notes.
+* ``m.lqnn.cn/news/240480`` — "kvcache sharemem": page pool, page table,
+  index redirection ``[page, slot, head, dim]``, ``PagePool.allocate_pages``.
+
+Modules:
+
+* :mod:`oracle.sizes` — closed forms (bytes per token, blocks, fragmentation,
+  pool capacity).
+* :mod:`oracle.allocator` — FIFO free list + refcounts + sequence helpers
+  (fork, reserve with copy-on-write, release).
+* :mod:`oracle.pool` — K/V scatter into blocks and whole-block copies.
+* :mod:`oracle.attention` — decode attention by its plain definition.
+
+Parity status: every function is pinned by ``tests/test_oracle_*.py`` against
+closed forms printed on the pages, hand-derived traces, library routines
+(``torch.nn.functional.scaled_dot_product_attention`` in float64) and
+invariants; none is "parity unpinned".
+"""
+
+from . import allocator, attention, pool, sizes  # noqa: F401
