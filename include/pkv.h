@@ -1,0 +1,233 @@
+/*
+ * pkv.h — C interface of libpkv: decode-step attention over a paged KV cache
+ * on AMD Instinct MI355X (gfx950).
+ *
+ * The cache is cut into fixed-size blocks of `block_size` tokens; a sequence
+ * owns an ordered list of physical block ids (its block-table row), so its
+ * cache is logically contiguous and physically scattered
+ * (hnwysp.cn/news/103996 §2.2; icman.com.cn/news/78786 §2.1).  The library has
+ * two halves:
+ *
+ *   - a host block allocator (FIFO free queue + per-block reference counts,
+ *     sequence fork / reserve / release with copy-on-write), pure C++, no GPU;
+ *   - three device operations: scatter new K/V rows into their slots
+ *     (pkv_append), duplicate whole blocks for copy-on-write
+ *     (pkv_copy_blocks), and decode attention through the block table
+ *     (pkv_attention_decode).
+ *
+ * Conventions
+ *   - Every function returns a status: PKV_OK (0) or a negative PKV_ERR_*.
+ *     pkv_last_error() returns a human-readable detail of the calling
+ *     thread's most recent failure.  Out-parameters are written only on
+ *     success, and a failed allocator call leaves the allocator unchanged.
+ *   - Device pointers are caller-owned device memory.  The library keeps no
+ *     pointer after a call returns and never allocates, frees or
+ *     synchronises: device operations are enqueued on `stream` and return.
+ *     The caller keeps every buffer alive until the stream has finished.
+ *   - Pool layout (both K and V, per layer): [num_blocks][block_size]
+ *     [num_heads][head_dim], contiguous, element type `dtype`.  Token
+ *     position `pos` of a sequence lives in block table[pos / block_size] at
+ *     slot pos % block_size — the [page, slot, head, dim] order of
+ *     m.lqnn.cn/news/240480 §3.3.  The flat slot index of a token is
+ *     block * block_size + pos % block_size.
+ *   - Supported shapes: head_dim 64 or 128; block_size 8, 16 or 32; dtype
+ *     f32, f16 or bf16.  Anything else returns PKV_ERR_INVALID.
+ *   - The allocator is not thread-safe; callers serialise access to one
+ *     allocator.  Device operations are reentrant.
+ */
+#ifndef PKV_H_
+#define PKV_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(PKV_BUILDING_LIBRARY)
+#define PKV_API __attribute__((visibility("default")))
+#else
+#define PKV_API
+#endif
+
+enum {
+  PKV_OK = 0,
+  PKV_ERR_INVALID = -1,   /* bad argument: null pointer, unsupported shape, inconsistent sizes */
+  PKV_ERR_NO_BLOCKS = -2, /* pool exhausted: the request took nothing (caller queues or preempts) */
+  PKV_ERR_BAD_BLOCK = -3, /* block id outside [0, num_blocks) */
+  PKV_ERR_REFCOUNT = -4,  /* reference count would go below zero, or a free block was shared */
+  PKV_ERR_HIP = -5        /* a HIP runtime call failed (launch error) */
+};
+
+typedef enum { PKV_F32 = 0, PKV_F16 = 1, PKV_BF16 = 2 } pkv_dtype;
+
+/* Short description of a status code (static storage). */
+PKV_API const char* pkv_strerror(int status);
+/* Detail of the calling thread's last failure ("" if none). */
+PKV_API const char* pkv_last_error(void);
+/* Library interface version (major * 100 + minor). */
+PKV_API int pkv_version(void);
+
+/* ---------------------------------------------------------------------------
+ * Host block allocator
+ *
+ * One object per pool.  Block ids are 0 .. num_blocks-1.  The free list is a
+ * queue: allocation takes its head, a block whose count drops to zero goes
+ * to its tail (hnwysp.cn/news/103996 §3.4).  Allocation is O(1) — no scan of
+ * the pool (m.lqnn.cn/news/240480 §5.2 tip 1).  Host memory owned by the
+ * allocator; released by pkv_allocator_destroy.
+ * ------------------------------------------------------------------------- */
+typedef struct pkv_allocator pkv_allocator;
+
+/* Create a pool of `num_blocks` blocks of `block_size` tokens.
+ * `initial_free_order` (may be NULL = 0,1,..,n-1) must be a permutation of the
+ * ids: it is the initial queue order, which decides where blocks land
+ * physically (hnwysp.cn/news/103996 §3.2 threads every block onto the free
+ * list at start-up).  PKV_ERR_INVALID on a bad size or non-permutation. */
+PKV_API int pkv_allocator_create(int32_t num_blocks, int32_t block_size, const int32_t* initial_free_order,
+                                 pkv_allocator** out);
+PKV_API void pkv_allocator_destroy(pkv_allocator* a);
+
+/* Pop the head of the free queue; its count becomes 1.  PKV_ERR_NO_BLOCKS
+ * when empty — the pool is full and the caller queues the request
+ * (hnwysp.cn/news/103996 §4.4 alloc_block). */
+PKV_API int pkv_block_alloc(pkv_allocator* a, int32_t* block_out);
+/* Share a block: count + 1.  PKV_ERR_REFCOUNT if the block is free
+ * (hnwysp.cn/news/103996 §3.3: a prefix hit raises the count). */
+PKV_API int pkv_block_incref(pkv_allocator* a, int32_t block);
+/* Drop one reference; at zero the block joins the tail of the free queue
+ * (hnwysp.cn/news/103996 §4.4 free_block; icman.com.cn/news/78786 §3.3).
+ * PKV_ERR_REFCOUNT if the block is already free. */
+PKV_API int pkv_block_decref(pkv_allocator* a, int32_t block);
+/* Reference count (>= 0) of a block, or PKV_ERR_BAD_BLOCK. */
+PKV_API int pkv_block_refcount(const pkv_allocator* a, int32_t block);
+PKV_API int32_t pkv_num_free(const pkv_allocator* a);
+PKV_API int32_t pkv_num_blocks(const pkv_allocator* a);
+PKV_API int32_t pkv_block_size(const pkv_allocator* a);
+/* Copy the free queue, head first, into out[0 .. min(capacity, num_free)).
+ * Returns the number of ids written. */
+PKV_API int pkv_free_list(const pkv_allocator* a, int32_t* out, int32_t capacity);
+
+/* Sequence helpers over caller-owned block-table rows (host int32 arrays).  */
+
+/* Share all `n_blocks` blocks of src_row with a new sequence: each count + 1,
+ * ids copied to dst_row (a prefix hit maps the new request's table entries to
+ * the same physical blocks, icman.com.cn/news/78786 §3.4).  All or nothing. */
+PKV_API int pkv_seq_fork(pkv_allocator* a, const int32_t* src_row, int32_t n_blocks, int32_t* dst_row);
+
+/* Make room for positions cur_len .. cur_len+n_new-1 of one sequence.
+ * `row` holds *n_blocks ids (must equal ceil(cur_len / block_size)) and has
+ * room for row_capacity.  For each new position in order:
+ *   - a position that opens a new block appends a fresh block
+ *     (hnwysp.cn/news/103996 §4.2: take a block when the last one is full);
+ *   - the first write into an existing block whose count is above one copies
+ *     it: a fresh destination block is taken, (source, destination) is
+ *     emitted into cow_pairs_out, the source loses one reference and the row
+ *     entry is patched (copy-on-write, hnwysp.cn/news/103996 §3.3);
+ *   - slots_out[i] = row[pos / block_size] * block_size + pos % block_size.
+ * At most one pair is produced (only the partly filled last block can be
+ * shared), so cow_pairs_out needs room for 2 int32.  Fresh blocks plus the
+ * copy are checked against the free count first: PKV_ERR_NO_BLOCKS takes
+ * nothing (m.lqnn.cn/news/240480 §4.2 allocate_pages).  The copy must be
+ * enqueued (pkv_copy_blocks) before the append that writes the new rows. */
+PKV_API int pkv_seq_reserve(pkv_allocator* a, int32_t* row, int32_t row_capacity, int32_t* n_blocks,
+                            int32_t cur_len, int32_t n_new, int64_t* slots_out, int32_t* cow_pairs_out,
+                            int32_t* n_cow_out);
+
+/* pkv_seq_reserve over `batch` sequences in ascending order, all or nothing.
+ * tables: [batch][row_stride] (row capacity = row_stride); n_blocks[batch] is
+ * updated; slots_out receives sum(n_new) slots, sequence-major;
+ * cow_pairs_out: [cow_capacity][2] (cow_capacity >= batch suffices). */
+PKV_API int pkv_seq_reserve_batch(pkv_allocator* a, int32_t* tables, int32_t row_stride, int32_t* n_blocks,
+                                  const int32_t* cur_lens, const int32_t* n_new, int32_t batch,
+                                  int64_t* slots_out, int32_t* cow_pairs_out, int32_t cow_capacity,
+                                  int32_t* n_cow_out);
+
+/* Release a sequence: one reference dropped from each block, in logical
+ * order.  Validated first (ids in range, enough references), so a failure
+ * changes nothing.  Finished, cancelled and failed requests all go through
+ * this one call (m.lqnn.cn/news/240480 §5.3; icman.com.cn/news/78786 §6.3). */
+PKV_API int pkv_seq_release(pkv_allocator* a, const int32_t* row, int32_t n_blocks);
+
+/* ---------------------------------------------------------------------------
+ * Device operations
+ * ------------------------------------------------------------------------- */
+
+/* Scatter new K/V rows into the pools.
+ * k_new, v_new: device [num_tokens][num_heads][head_dim] of `dtype`;
+ * slot_mapping: device int64 [num_tokens]; token t goes to flat slot
+ * slot_mapping[t] of k_cache / v_cache (device pools, layout above).  A
+ * negative slot is skipped (padding); a slot >= num_blocks * block_size is
+ * also skipped, never written.  A bit copy: the new step's K/V join the cache
+ * before attention reads it (hnwysp.cn/news/103996 §1.1;
+ * m.lqnn.cn/news/240480 §3.2 step 3). */
+PKV_API int pkv_append(const void* k_new, const void* v_new, int32_t num_tokens, const int64_t* slot_mapping,
+                       void* k_cache, void* v_cache, int32_t num_blocks, int32_t block_size, int32_t num_heads,
+                       int32_t head_dim, pkv_dtype dtype, hipStream_t stream);
+
+/* Copy whole blocks for copy-on-write (hnwysp.cn/news/103996 §3.3).
+ * k_caches, v_caches: HOST arrays of `num_layers` device pool pointers.
+ * pairs: device int32 [n_pairs][2] = (source, destination) block ids.
+ * Every layer's K and V block `dst` becomes a bit copy of block `src`
+ * (bytes_per_block = block_size * num_heads * head_dim * dtype bytes, a
+ * multiple of 16).  Pairs are copied concurrently: destinations must be
+ * distinct and no destination may be a source (the allocator never emits
+ * such pairs).  A pair with an id outside [0, num_blocks) is skipped. */
+PKV_API int pkv_copy_blocks(void* const* k_caches, void* const* v_caches, int32_t num_layers,
+                            const int32_t* pairs, int32_t n_pairs, int32_t num_blocks, size_t bytes_per_block,
+                            hipStream_t stream);
+
+/* Tokens per split-K partition the library picks when pkv_attention_decode
+ * is called with partition_tokens = 0 (a multiple of block_size). */
+PKV_API int32_t pkv_decode_partition_tokens(int32_t batch, int32_t num_heads, int32_t head_dim, pkv_dtype dtype,
+                                            int32_t block_size, int32_t max_seq_len);
+
+/* Device workspace pkv_attention_decode needs for these sizes
+ * (partition_tokens = 0: the automatic choice).  Float32 partial results:
+ * batch * ceil(max_seq_len / P) * num_heads * (head_dim + 2) * 4 bytes,
+ * rounded up.  Returns 0 for an invalid shape. */
+PKV_API size_t pkv_decode_workspace_bytes(int32_t batch, int32_t num_heads, int32_t head_dim, pkv_dtype dtype,
+                                          int32_t block_size, int32_t max_seq_len, int32_t partition_tokens);
+
+/* Decode attention through the block table.
+ * For every sequence b < batch and head h < num_heads, with L = seq_lens[b]:
+ *   out[b][h] = sum_t softmax_t(scale * <q[b][h], K_t>) V_t,  t = 0 .. L-1,
+ * where K_t, V_t are the rows of logical position t, found at block
+ * block_tables[b][t / block_size], slot t % block_size (the attention kernel
+ * walks the table block by block, icman.com.cn/news/78786 §2.4; the logical
+ * to physical index redirection of m.lqnn.cn/news/240480 §3.3).  L includes
+ * the token appended this step.
+ *   out, q: device [batch][num_heads][head_dim] of `dtype`; out rounded to
+ *     nearest-even from float32 accumulation.
+ *   k_cache, v_cache: device pools of num_blocks blocks (layout above).
+ *   block_tables: device int32 [batch][max_blocks_per_seq].
+ *   seq_lens: device int32 [batch].  max_seq_len: host upper bound of every
+ *     seq_lens entry (sizes the launch and the workspace).
+ *   scale: softmax scale (1/sqrt(head_dim) for plain scaled dot-product).
+ *   partition_tokens: split-K partition length (0 = automatic; otherwise a
+ *     multiple of block_size and of 8, at least 32).  Sequences longer than
+ *     one partition are processed in parallel pieces whose partial softmax
+ *     states (max, sum, weighted values) are merged afterwards; partitions
+ *     depend only on logical positions, so the result does not depend on
+ *     where the blocks sit physically.
+ *   workspace: device memory of at least pkv_decode_workspace_bytes(...).
+ * L = 0 gives a zero row.  A sequence whose length is negative or exceeds
+ * max_seq_len or max_blocks_per_seq * block_size, or whose table holds an id
+ * outside [0, num_blocks) in its first ceil(L / block_size) entries, gets
+ * NaN rows: the kernel checks every id before using it and never reads
+ * outside the pools. */
+PKV_API int pkv_attention_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+                                 const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                                 int32_t max_seq_len, int32_t batch, int32_t num_heads, int32_t head_dim,
+                                 int32_t block_size, int32_t num_blocks, float scale, pkv_dtype dtype,
+                                 int32_t partition_tokens, void* workspace, size_t workspace_bytes,
+                                 hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H_ */

@@ -1,0 +1,338 @@
+"""Python binding of libpkv: paged-KV decode attention for MI355X (gfx950).
+
+A thin ctypes layer over the C interface in ``include/pkv.h``: every function
+here checks tensor shapes and dtypes, passes raw pointers and the current
+HIP stream, and turns status codes into exceptions.  All computation happens
+in the library (HIP kernels and the C++ allocator); there is no Python or CPU
+fallback, and importing this package fails loudly if ``libpkv.so`` has not
+been built (``python -m paged_attention_amd.build``).
+
+Entry points keep the C names:
+
+* :class:`BlockAllocator` — ``pkv_allocator_*``, ``pkv_block_*``, ``pkv_seq_*``
+* :func:`pkv_append`, :func:`pkv_copy_blocks`, :func:`pkv_attention_decode`,
+  :func:`pkv_decode_workspace_bytes`, :func:`pkv_decode_partition_tokens`
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libpkv.so")
+
+PKV_OK = 0
+PKV_ERR_INVALID = -1
+PKV_ERR_NO_BLOCKS = -2
+PKV_ERR_BAD_BLOCK = -3
+PKV_ERR_REFCOUNT = -4
+PKV_ERR_HIP = -5
+
+PKV_F32, PKV_F16, PKV_BF16 = 0, 1, 2
+DTYPE_CODES = {"f32": PKV_F32, "f16": PKV_F16, "bf16": PKV_BF16}
+
+
+class PkvError(RuntimeError):
+    """A libpkv call returned an error status."""
+
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"{detail} (status {status})")
+        self.status = status
+
+
+class OutOfBlocks(PkvError):
+    """The block pool cannot satisfy a request; nothing was taken."""
+
+
+class InvalidArgument(PkvError, ValueError):
+    pass
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m paged_attention_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    i32, i64, vp, sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t
+    p32, p64 = ctypes.POINTER(i32), ctypes.POINTER(i64)
+    sig = {
+        "pkv_strerror": (ctypes.c_char_p, [ctypes.c_int]),
+        "pkv_last_error": (ctypes.c_char_p, []),
+        "pkv_version": (ctypes.c_int, []),
+        "pkv_allocator_create": (ctypes.c_int, [i32, i32, p32, ctypes.POINTER(vp)]),
+        "pkv_allocator_destroy": (None, [vp]),
+        "pkv_block_alloc": (ctypes.c_int, [vp, p32]),
+        "pkv_block_incref": (ctypes.c_int, [vp, i32]),
+        "pkv_block_decref": (ctypes.c_int, [vp, i32]),
+        "pkv_block_refcount": (ctypes.c_int, [vp, i32]),
+        "pkv_num_free": (i32, [vp]),
+        "pkv_num_blocks": (i32, [vp]),
+        "pkv_block_size": (i32, [vp]),
+        "pkv_free_list": (ctypes.c_int, [vp, p32, i32]),
+        "pkv_seq_fork": (ctypes.c_int, [vp, p32, i32, p32]),
+        "pkv_seq_reserve": (ctypes.c_int, [vp, p32, i32, p32, i32, i32, p64, p32, p32]),
+        "pkv_seq_reserve_batch": (ctypes.c_int, [vp, p32, i32, p32, p32, p32, i32, p64, p32, i32, p32]),
+        "pkv_seq_release": (ctypes.c_int, [vp, p32, i32]),
+        "pkv_append": (ctypes.c_int, [vp, vp, i32, vp, vp, vp, i32, i32, i32, i32, ctypes.c_int, vp]),
+        "pkv_copy_blocks": (ctypes.c_int, [ctypes.POINTER(vp), ctypes.POINTER(vp), i32, vp, i32, i32, sz, vp]),
+        "pkv_decode_partition_tokens": (i32, [i32, i32, i32, ctypes.c_int, i32, i32]),
+        "pkv_decode_workspace_bytes": (sz, [i32, i32, i32, ctypes.c_int, i32, i32, i32]),
+        "pkv_attention_decode": (ctypes.c_int, [vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, i32, i32,
+                                                ctypes.c_float, ctypes.c_int, i32, vp, sz, vp]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+_lib = _load()
+
+
+def _check(status: int) -> int:
+    if status >= 0:
+        return status
+    detail = _lib.pkv_last_error().decode() or _lib.pkv_strerror(status).decode()
+    if status == PKV_ERR_NO_BLOCKS:
+        raise OutOfBlocks(status, detail)
+    if status == PKV_ERR_INVALID:
+        raise InvalidArgument(status, detail)
+    raise PkvError(status, detail)
+
+
+def version() -> int:
+    return _lib.pkv_version()
+
+
+def _i32p(arr: np.ndarray):
+    return arr.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+
+
+def _i64p(arr: np.ndarray):
+    return arr.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
+
+
+class BlockAllocator:
+    """Host block allocator (FIFO free queue + reference counts), backed by libpkv."""
+
+    def __init__(self, num_blocks: int, block_size: int, free_order=None):
+        handle = ctypes.c_void_p()
+        order = None
+        if free_order is not None:
+            order = np.ascontiguousarray(free_order, dtype=np.int32)
+            if order.shape != (num_blocks,):
+                raise InvalidArgument(PKV_ERR_INVALID, "free_order must hold num_blocks ids")
+        _check(_lib.pkv_allocator_create(num_blocks, block_size, _i32p(order) if order is not None else None,
+                                         ctypes.byref(handle)))
+        self._h = handle
+        self.num_blocks = num_blocks
+        self.block_size = block_size
+
+    def close(self):
+        if getattr(self, "_h", None):
+            _lib.pkv_allocator_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        self.close()
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    # single blocks
+    def alloc(self) -> int:
+        out = ctypes.c_int32()
+        _check(_lib.pkv_block_alloc(self._h, ctypes.byref(out)))
+        return out.value
+
+    def incref(self, block: int) -> None:
+        _check(_lib.pkv_block_incref(self._h, block))
+
+    def decref(self, block: int) -> None:
+        _check(_lib.pkv_block_decref(self._h, block))
+
+    def refcount(self, block: int) -> int:
+        return _check(_lib.pkv_block_refcount(self._h, block))
+
+    def num_free(self) -> int:
+        return _lib.pkv_num_free(self._h)
+
+    def free_list(self) -> list:
+        buf = np.zeros(max(1, self.num_blocks), dtype=np.int32)
+        n = _check(_lib.pkv_free_list(self._h, _i32p(buf), self.num_blocks))
+        return buf[:n].tolist()
+
+    # sequences over Python lists (convenience) ---------------------------
+    def fork(self, row) -> list:
+        src = np.ascontiguousarray(row, dtype=np.int32)
+        dst = np.zeros(max(1, len(src)), dtype=np.int32)
+        _check(_lib.pkv_seq_fork(self._h, _i32p(src), len(src), _i32p(dst)))
+        return dst[: len(src)].tolist()
+
+    def reserve(self, row: list, cur_len: int, n_new: int, capacity: int | None = None):
+        """Grow ``row`` (a list, updated in place) by n_new positions; returns (slots, pairs)."""
+        bs = self.block_size
+        cap = capacity if capacity is not None else -(-(cur_len + n_new) // bs) + 1
+        buf = np.zeros(max(cap, len(row), 1), dtype=np.int32)
+        buf[: len(row)] = row
+        nb = ctypes.c_int32(len(row))
+        slots = np.zeros(max(1, n_new), dtype=np.int64)
+        pair = np.zeros(2, dtype=np.int32)
+        ncow = ctypes.c_int32(0)
+        _check(_lib.pkv_seq_reserve(self._h, _i32p(buf), len(buf), ctypes.byref(nb), cur_len, n_new, _i64p(slots),
+                                    _i32p(pair), ctypes.byref(ncow)))
+        row[:] = buf[: nb.value].tolist()
+        pairs = [(int(pair[0]), int(pair[1]))] if ncow.value else []
+        return slots[:n_new].tolist(), pairs
+
+    def release(self, row) -> None:
+        arr = np.ascontiguousarray(row, dtype=np.int32)
+        _check(_lib.pkv_seq_release(self._h, _i32p(arr) if len(arr) else None, len(arr)))
+
+    # sequences over numpy tables (batched, no per-sequence Python work) ---
+    def reserve_batch(self, tables: np.ndarray, n_blocks: np.ndarray, cur_lens, n_new):
+        """Reserve for every row of ``tables`` ([B][stride] int32, updated in place).
+
+        ``n_blocks`` (int32 [B]) is updated in place.  Returns (slots int64
+        [sum n_new], pairs int32 [k][2]).
+        """
+        assert tables.dtype == np.int32 and tables.flags.c_contiguous and tables.ndim == 2
+        assert n_blocks.dtype == np.int32 and n_blocks.flags.c_contiguous
+        lens = np.ascontiguousarray(cur_lens, dtype=np.int32)
+        new = np.ascontiguousarray(n_new, dtype=np.int32)
+        batch = tables.shape[0]
+        slots = np.zeros(max(1, int(new.sum())), dtype=np.int64)
+        pairs = np.zeros((max(1, batch), 2), dtype=np.int32)
+        ncow = ctypes.c_int32(0)
+        _check(_lib.pkv_seq_reserve_batch(self._h, _i32p(tables), tables.shape[1], _i32p(n_blocks), _i32p(lens),
+                                          _i32p(new), batch, _i64p(slots), _i32p(pairs), max(1, batch),
+                                          ctypes.byref(ncow)))
+        return slots[: int(new.sum())], pairs[: ncow.value]
+
+    def release_table_row(self, tables: np.ndarray, i: int, n_blocks: int) -> None:
+        row = np.ascontiguousarray(tables[i, :n_blocks])
+        self.release(row)
+
+
+# ---------------------------------------------------------------------------
+# device operations
+# ---------------------------------------------------------------------------
+
+def _torch():
+    import torch
+
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    codes = {torch.float32: PKV_F32, torch.float16: PKV_F16, torch.bfloat16: PKV_BF16}
+    if t.dtype not in codes:
+        raise InvalidArgument(PKV_ERR_INVALID, f"unsupported dtype {t.dtype}")
+    return codes[t.dtype]
+
+
+def _dev(t, name, dtype=None, ndim=None):
+    if not t.is_cuda:
+        raise InvalidArgument(PKV_ERR_INVALID, f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise InvalidArgument(PKV_ERR_INVALID, f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise InvalidArgument(PKV_ERR_INVALID, f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise InvalidArgument(PKV_ERR_INVALID, f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def pkv_append(k_new, v_new, slot_mapping, k_cache, v_cache, stream=None) -> None:
+    """Scatter rows ``k_new[t]``/``v_new[t]`` ([T][H][D]) to flat slot ``slot_mapping[t]``."""
+    torch = _torch()
+    nb, bs, h, d = k_cache.shape
+    if k_new.shape[1:] != (h, d) or v_new.shape != k_new.shape or v_cache.shape != k_cache.shape:
+        raise InvalidArgument(PKV_ERR_INVALID, "append: shape mismatch")
+    if k_new.dtype != k_cache.dtype or v_new.dtype != k_cache.dtype or v_cache.dtype != k_cache.dtype:
+        raise InvalidArgument(PKV_ERR_INVALID, "append: dtype mismatch")
+    if slot_mapping.shape != (k_new.shape[0],):
+        raise InvalidArgument(PKV_ERR_INVALID, "append: slot_mapping must be [T]")
+    _check(_lib.pkv_append(_dev(k_new, "k_new"), _dev(v_new, "v_new"), k_new.shape[0],
+                           _dev(slot_mapping, "slot_mapping", torch.int64), _dev(k_cache, "k_cache", ndim=4),
+                           _dev(v_cache, "v_cache", ndim=4), nb, bs, h, d, _dtype_code(k_cache), _stream(stream)))
+
+
+def pkv_copy_blocks(k_caches, v_caches, pairs, stream=None) -> None:
+    """Copy blocks ``pairs[i, 0] -> pairs[i, 1]`` in every layer's K and V pool."""
+    torch = _torch()
+    if len(k_caches) != len(v_caches) or not k_caches:
+        raise InvalidArgument(PKV_ERR_INVALID, "copy_blocks: need matching non-empty layer lists")
+    nb, bs, h, d = k_caches[0].shape
+    for t in list(k_caches) + list(v_caches):
+        if t.shape != k_caches[0].shape or t.dtype != k_caches[0].dtype:
+            raise InvalidArgument(PKV_ERR_INVALID, "copy_blocks: layer pools differ in shape or dtype")
+        _dev(t, "pool", ndim=4)
+    if pairs.dim() != 2 or pairs.shape[1] != 2:
+        raise InvalidArgument(PKV_ERR_INVALID, "copy_blocks: pairs must be [n][2]")
+    nl = len(k_caches)
+    karr = (ctypes.c_void_p * nl)(*[t.data_ptr() for t in k_caches])
+    varr = (ctypes.c_void_p * nl)(*[t.data_ptr() for t in v_caches])
+    bytes_per_block = bs * h * d * k_caches[0].element_size()
+    _check(_lib.pkv_copy_blocks(karr, varr, nl, _dev(pairs, "pairs", torch.int32), pairs.shape[0], nb,
+                                bytes_per_block, _stream(stream)))
+
+
+def pkv_decode_partition_tokens(batch, num_heads, head_dim, dtype, block_size, max_seq_len) -> int:
+    return _check(_lib.pkv_decode_partition_tokens(batch, num_heads, head_dim, DTYPE_CODES[dtype], block_size,
+                                                   max_seq_len))
+
+
+def pkv_decode_workspace_bytes(batch, num_heads, head_dim, dtype, block_size, max_seq_len,
+                               partition_tokens=0) -> int:
+    return int(_lib.pkv_decode_workspace_bytes(batch, num_heads, head_dim, DTYPE_CODES[dtype], block_size,
+                                               max_seq_len, partition_tokens))
+
+
+_DT_NAMES = {PKV_F32: "f32", PKV_F16: "f16", PKV_BF16: "bf16"}
+
+
+def pkv_attention_decode(out, q, k_cache, v_cache, block_tables, seq_lens, max_seq_len, scale=None,
+                         partition_tokens=0, workspace=None, stream=None) -> None:
+    """Decode attention of ``q`` ([B][H][D]) over each sequence's paged K/V; writes ``out``."""
+    torch = _torch()
+    nb, bs, h, d = k_cache.shape
+    batch = q.shape[0]
+    if q.shape != (batch, h, d) or out.shape != q.shape or v_cache.shape != k_cache.shape:
+        raise InvalidArgument(PKV_ERR_INVALID, "attention_decode: shape mismatch")
+    if not (q.dtype == out.dtype == k_cache.dtype == v_cache.dtype):
+        raise InvalidArgument(PKV_ERR_INVALID, "attention_decode: dtype mismatch")
+    if block_tables.dim() != 2 or block_tables.shape[0] != batch or seq_lens.shape != (batch,):
+        raise InvalidArgument(PKV_ERR_INVALID, "attention_decode: tables must be [B][max_blocks], lens [B]")
+    code = _dtype_code(q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    need = int(_lib.pkv_decode_workspace_bytes(batch, h, d, code, bs, max_seq_len, partition_tokens))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check(_lib.pkv_attention_decode(
+        _dev(out, "out"), _dev(q, "q"), _dev(k_cache, "k_cache", ndim=4), _dev(v_cache, "v_cache", ndim=4),
+        _dev(block_tables, "block_tables", torch.int32), block_tables.shape[1],
+        _dev(seq_lens, "seq_lens", torch.int32), int(max_seq_len), batch, h, d, bs, nb, float(scale), code,
+        int(partition_tokens), _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+        _stream(stream)))
+
+
+__all__ = [
+    "BlockAllocator", "PkvError", "OutOfBlocks", "InvalidArgument", "pkv_append", "pkv_copy_blocks",
+    "pkv_attention_decode", "pkv_decode_workspace_bytes", "pkv_decode_partition_tokens", "version", "LIB_PATH",
+]

@@ -1,0 +1,97 @@
+"""libpkv loads, exports every symbol include/pkv.h declares, and validates
+arguments on the host (no kernel is launched by these tests)."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import paged_attention_amd as pkv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    with open(os.path.join(ROOT, "include", "pkv.h")) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"PKV_API\s+[^;(]*?\b(pkv_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = _declared()
+    for must in ("pkv_append", "pkv_attention_decode", "pkv_copy_blocks", "pkv_allocator_create",
+                 "pkv_block_alloc", "pkv_block_decref", "pkv_seq_reserve", "pkv_seq_release"):
+        assert must in names
+    assert len(names) >= 20
+
+
+def test_library_exports_every_declared_symbol():
+    out = subprocess.run(["nm", "-D", "--defined-only", pkv.LIB_PATH], capture_output=True, text=True, check=True)
+    exported = {line.split()[-1] for line in out.stdout.splitlines() if " T " in line}
+    missing = [n for n in _declared() if n not in exported]
+    assert not missing, missing
+    # Nothing else leaks out of the library's C interface.
+    extra = [n for n in exported if n.startswith("pkv_") and n not in _declared()]
+    assert not extra, extra
+    lib = ctypes.CDLL(pkv.LIB_PATH)
+    for n in _declared():
+        getattr(lib, n)
+
+
+def test_status_strings_and_version():
+    lib = pkv._lib
+    assert pkv.version() >= 100
+    for code in (0, -1, -2, -3, -4, -5):
+        assert lib.pkv_strerror(code)
+    assert lib.pkv_strerror(-99) == b"unknown status"
+
+
+def test_device_calls_reject_bad_shapes_before_launch():
+    lib = pkv._lib
+    null = ctypes.c_void_p(0)
+    # Unsupported head_dim / block size / dtype: rejected on the host.
+    st = lib.pkv_attention_decode(null, null, null, null, null, 4, null, 64, 1, 4, 96, 16, 8, 1.0, 1, 0, null, 0,
+                                  null)
+    assert st == pkv.PKV_ERR_INVALID
+    st = lib.pkv_attention_decode(null, null, null, null, null, 4, null, 64, 1, 4, 128, 12, 8, 1.0, 1, 0, null, 0,
+                                  null)
+    assert st == pkv.PKV_ERR_INVALID
+    st = lib.pkv_attention_decode(null, null, null, null, null, 4, null, 64, 1, 4, 128, 16, 8, 1.0, 7, 0, null, 0,
+                                  null)
+    assert st == pkv.PKV_ERR_INVALID
+    # Partition length must be a positive multiple of 32.
+    st = lib.pkv_attention_decode(null, null, null, null, null, 4, null, 64, 1, 4, 128, 16, 8, 1.0, 1, 48, null, 0,
+                                  null)
+    assert st == pkv.PKV_ERR_INVALID
+    # Null pointers with a non-empty batch.
+    st = lib.pkv_attention_decode(null, null, null, null, null, 4, null, 64, 1, 4, 128, 16, 8, 1.0, 1, 0, null, 0,
+                                  null)
+    assert st == pkv.PKV_ERR_INVALID
+    # Empty batch: nothing to do.
+    st = lib.pkv_attention_decode(null, null, null, null, null, 4, null, 64, 0, 4, 128, 16, 8, 1.0, 1, 0, null, 0,
+                                  null)
+    assert st == pkv.PKV_OK
+    assert lib.pkv_append(null, null, 0, null, null, null, 8, 16, 4, 128, 1, null) == pkv.PKV_OK
+    assert lib.pkv_append(null, null, 3, null, null, null, 8, 16, 4, 128, 1, null) == pkv.PKV_ERR_INVALID
+    assert lib.pkv_append(null, null, 3, null, null, null, 8, 16, 4, 100, 1, null) == pkv.PKV_ERR_INVALID
+    assert lib.pkv_copy_blocks(None, None, 1, null, 1, 8, 100, null) == pkv.PKV_ERR_INVALID
+    assert lib.pkv_copy_blocks(None, None, 1, null, 0, 8, 4096, null) == pkv.PKV_OK
+
+
+def test_workspace_and_partition_queries():
+    # One partition: no workspace.  Otherwise batch*parts*heads*(D floats) + (m,l) pairs.
+    assert pkv.pkv_decode_workspace_bytes(4, 4, 64, "f32", 16, 64, 64) == 0
+    b, h, d, ml, part = 32, 32, 128, 2048, 64
+    parts = ml // part
+    want_acc = -(-(b * parts * h * d * 4) // 256) * 256
+    want_ml = -(-(b * parts * h * 8) // 256) * 256
+    assert pkv.pkv_decode_workspace_bytes(b, h, d, "f16", 16, ml, part) == want_acc + want_ml
+    auto = pkv.pkv_decode_partition_tokens(b, h, d, "f16", 16, ml)
+    assert auto % 32 == 0 and auto >= 32
+    assert pkv.pkv_decode_workspace_bytes(b, h, d, "f16", 16, ml, 0) == \
+        pkv.pkv_decode_workspace_bytes(b, h, d, "f16", 16, ml, auto)
+    assert pkv.pkv_decode_workspace_bytes(b, h, 96, "f16", 16, ml, 0) == 0
+    with pytest.raises(pkv.PkvError):
+        pkv.pkv_decode_partition_tokens(b, h, 96, "f16", 16, ml)

@@ -1,0 +1,325 @@
+"""The C++ host allocator in libpkv against the oracle allocator: bit-exact.
+
+Block ids, free-list order, reference counts, slots, copy pairs and error
+codes must all match the oracle, on the hand-derived traces, on random op
+traces, and under AddressSanitizer/UndefinedBehaviorSanitizer.
+"""
+
+import json
+import os
+import shutil
+import subprocess
+
+import numpy as np
+import pytest
+from hypothesis import assume, given, settings, strategies as st
+
+import paged_attention_amd as pkv
+from oracle import allocator as oa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CODE = {"REFCOUNT": pkv.PKV_ERR_REFCOUNT, "BAD_BLOCK": pkv.PKV_ERR_BAD_BLOCK, "NO_BLOCKS": pkv.PKV_ERR_NO_BLOCKS,
+        "INVALID": pkv.PKV_ERR_INVALID}
+
+
+def test_golden_traces_on_library(golden_dir):
+    with open(os.path.join(golden_dir, "allocator_trace.json")) as f:
+        traces = json.load(f)
+    t = traces["blocks"]
+    a = pkv.BlockAllocator(t["num_blocks"], t["block_size"], t["free_order"])
+    for op in t["ops"]:
+        kind = op["op"]
+        if "error" in op:
+            with pytest.raises(pkv.PkvError) as ei:
+                a.alloc() if kind == "alloc" else getattr(a, kind)(op["block"])
+            assert ei.value.status == CODE[op["error"]]
+        elif kind == "alloc":
+            assert a.alloc() == op["expect"]
+        elif kind in ("incref", "decref"):
+            getattr(a, kind)(op["block"])
+        elif kind == "refcount":
+            assert a.refcount(op["block"]) == op["expect"]
+        elif kind == "free_list":
+            assert a.free_list() == op["expect"]
+        elif kind == "num_free":
+            assert a.num_free() == op["expect"]
+    t = traces["sequences"]
+    a = pkv.BlockAllocator(t["num_blocks"], t["block_size"], t["free_order"])
+    rows = {}
+    for op in t["ops"]:
+        kind = op["op"]
+        if kind == "reserve":
+            row = rows.setdefault(op["seq"], [])
+            if "error" in op:
+                before = (list(row), a.free_list())
+                with pytest.raises(pkv.OutOfBlocks):
+                    a.reserve(row, op["cur_len"], op["n_new"])
+                assert (row, a.free_list()) == before
+                continue
+            slots, pairs = a.reserve(row, op["cur_len"], op["n_new"])
+            assert slots == op["expect_slots"]
+            assert [list(p) for p in pairs] == op["expect_pairs"]
+            assert row == op["expect_row"]
+        elif kind == "fork":
+            rows[op["dst"]] = a.fork(rows[op["src"]])
+            assert rows[op["dst"]] == op["expect_row"]
+        elif kind == "release":
+            a.release(rows.pop(op["seq"]))
+        elif kind == "refcount":
+            assert a.refcount(op["block"]) == op["expect"]
+        elif kind == "free_list":
+            assert a.free_list() == op["expect"]
+        elif kind == "num_free":
+            assert a.num_free() == op["expect"]
+
+
+def _random_trace(data_draw, nb, bs):
+    """Random op list (with sequence ids) that exercises every allocator path."""
+    ops = []
+    live = {}   # sid -> (n_blocks) as the oracle will see it; just ids for selection
+    next_sid = 0
+    for _ in range(data_draw(st.integers(1, 50))):
+        kind = data_draw(st.sampled_from(["alloc", "incref", "decref", "new", "grow", "fork", "release"]))
+        if kind == "alloc":
+            ops.append(("alloc",))
+        elif kind in ("incref", "decref"):
+            ops.append((kind, data_draw(st.integers(-1, nb))))
+        elif kind == "new":
+            ops.append(("reserve", next_sid, 0, data_draw(st.integers(0, 3 * bs))))
+            live[next_sid] = True
+            next_sid += 1
+        elif live:
+            sid = data_draw(st.sampled_from(sorted(live)))
+            if kind == "grow":
+                ops.append(("grow", sid, data_draw(st.integers(0, 2 * bs)), data_draw(st.integers(0, bs - 1))))
+            elif kind == "fork":
+                ops.append(("fork", sid, next_sid))
+                live[next_sid] = True
+                next_sid += 1
+            else:
+                ops.append(("release", sid))
+                del live[sid]
+    return ops
+
+
+def _apply(ops, alloc_factory, err_type, code_of):
+    """Run ops on an allocator, returning the observable outcome of each."""
+    a = alloc_factory()
+    rows, lens, out = {}, {}, []
+    bs = a.block_size
+    for op in ops:
+        try:
+            if op[0] == "alloc":
+                out.append(("ok", a.alloc()))
+            elif op[0] in ("incref", "decref"):
+                getattr(a, op[0])(op[1])
+                out.append(("ok",))
+            elif op[0] == "reserve":
+                row = []
+                slots, pairs = a.reserve(row, 0, op[3])
+                rows[op[1]], lens[op[1]] = row, op[3]
+                out.append(("ok", list(slots), [tuple(p) for p in pairs], list(row)))
+            elif op[0] == "grow":
+                sid = op[1]
+                if sid not in rows:
+                    out.append(("skip",))
+                    continue
+                # Grow from a length consistent with the row (its fill, or less
+                # when the sequence was forked from a longer one).
+                cur = lens[sid]
+                slots, pairs = a.reserve(rows[sid], cur, op[2])
+                lens[sid] = cur + op[2]
+                out.append(("ok", list(slots), [tuple(p) for p in pairs], list(rows[sid])))
+            elif op[0] == "fork":
+                if op[1] not in rows:
+                    out.append(("skip",))
+                    continue
+                rows[op[2]] = a.fork(rows[op[1]])
+                lens[op[2]] = lens[op[1]]
+                out.append(("ok", list(rows[op[2]])))
+            elif op[0] == "release":
+                if op[1] not in rows:
+                    out.append(("skip",))
+                    continue
+                a.release(rows.pop(op[1]))
+                lens.pop(op[1])
+                out.append(("ok",))
+        except err_type as e:
+            if op[0] == "reserve":
+                rows[op[1]], lens[op[1]] = [], 0
+            out.append(("err", code_of(e)))
+        out.append(("state", a.free_list(), [a.refcount(b) for b in range(a.num_blocks)]))
+    return out
+
+
+class _OracleRows(oa.OracleAllocator):
+    """The oracle with the binding's list-based fork/release signatures."""
+
+    def fork(self, row, n_blocks=None):
+        return super().fork(row, len(row) if n_blocks is None else n_blocks)
+
+    def release(self, row, n_blocks=None):
+        return super().release(row, len(row) if n_blocks is None else n_blocks)
+
+
+@settings(max_examples=200, deadline=None)
+@given(st.data())
+def test_random_traces_match_oracle(data):
+    nb = data.draw(st.integers(1, 20))
+    bs = data.draw(st.sampled_from([1, 2, 4, 8, 16]))
+    order = data.draw(st.permutations(list(range(nb))))
+    ops = _random_trace(data.draw, nb, bs)
+    want = _apply(ops, lambda: _OracleRows(nb, bs, order), oa.AllocatorError, lambda e: e.code)
+    got = _apply(ops, lambda: pkv.BlockAllocator(nb, bs, order), pkv.PkvError, lambda e: e.status)
+    assert got == want
+
+
+@settings(max_examples=100, deadline=None)
+@given(st.data())
+def test_batch_reserve_matches_oracle(data):
+    nb = data.draw(st.integers(2, 40))
+    bs = data.draw(st.sampled_from([2, 4, 8]))
+    order = data.draw(st.permutations(list(range(nb))))
+    batch = data.draw(st.integers(1, 6))
+    pre = [data.draw(st.integers(0, 2 * bs)) for _ in range(batch)]
+    share = data.draw(st.booleans())
+    new = [data.draw(st.integers(0, bs + 1)) for _ in range(batch)]
+    o = oa.OracleAllocator(nb, bs, order)
+    c = pkv.BlockAllocator(nb, bs, order)
+    stride = 64
+    tables = np.zeros((batch, stride), dtype=np.int32)
+    nblk = np.zeros(batch, dtype=np.int32)
+    orows = []
+    lens = []
+    for i in range(batch):
+        if share and i > 0 and orows[0] is not None:
+            r = o.fork(orows[0], len(orows[0]))
+            crow = c.fork(tables[0, : nblk[0]])
+            orows.append(r)
+            lens.append(lens[0])
+        else:
+            r = []
+            try:
+                o.reserve(r, 0, pre[i])
+            except oa.AllocatorError:
+                assume(False)  # pool too small for this setup
+            crow = []
+            c.reserve(crow, 0, pre[i])
+            orows.append(r)
+            lens.append(pre[i])
+        tables[i, : len(crow)] = crow
+        nblk[i] = len(crow)
+        assert crow == orows[i]
+    try:
+        oslots, opairs = o.reserve_batch(orows, lens, new)
+        oerr = None
+    except oa.AllocatorError as e:
+        oerr = e.code
+    if oerr is not None:
+        with pytest.raises(pkv.PkvError) as ei:
+            c.reserve_batch(tables, nblk, lens, new)
+        assert ei.value.status == oerr
+    else:
+        cslots, cpairs = c.reserve_batch(tables, nblk, lens, new)
+        assert cslots.tolist() == oslots
+        assert [tuple(p) for p in cpairs.tolist()] == [tuple(p) for p in opairs]
+        for i in range(batch):
+            assert tables[i, : nblk[i]].tolist() == orows[i]
+    assert c.free_list() == o.free_list()
+    assert [c.refcount(b) for b in range(nb)] == o.ref
+
+
+def test_creation_errors():
+    with pytest.raises(pkv.InvalidArgument):
+        pkv.BlockAllocator(4, 4, [0, 1, 1, 2])
+    with pytest.raises(pkv.InvalidArgument):
+        pkv.BlockAllocator(0, 4)
+    a = pkv.BlockAllocator(4, 4)
+    with pytest.raises(pkv.PkvError) as ei:
+        a.refcount(9)
+    assert ei.value.status == pkv.PKV_ERR_BAD_BLOCK
+    with pytest.raises(pkv.InvalidArgument):
+        a.reserve([], 3, 1)
+
+
+def _driver_text(ops, nb, bs, order):
+    """Expected driver output computed with the oracle."""
+    a = oa.OracleAllocator(nb, bs, order)
+    rows = {}
+    lines = ["0"]
+    for op in ops:
+        try:
+            if op[0] == "alloc":
+                lines.append(f"ok {a.alloc()}")
+            elif op[0] in ("incref", "decref"):
+                getattr(a, op[0])(op[1])
+                lines.append("ok")
+            elif op[0] == "reserve":
+                row = rows.setdefault(op[1], [])
+                slots, pairs = a.reserve(row, op[2], op[3])
+                pr = " ".join(f"{s} {d}" for s, d in pairs)
+                lines.append(" ".join(["ok"] + [str(s) for s in slots] + ["|"] + ([pr] if pr else []) + ["|"] +
+                                      [str(b) for b in row]))
+            elif op[0] == "fork":
+                rows[op[2]] = a.fork(rows.get(op[1], []), len(rows.get(op[1], [])))
+                lines.append("ok")
+            elif op[0] == "release":
+                a.release(rows.get(op[1], []), len(rows.get(op[1], [])))
+                rows.pop(op[1], None)
+                lines.append("ok")
+        except oa.AllocatorError as e:
+            lines.append(f"err {e.code}")
+        lines.append("free" + "".join(f" {b}" for b in a.free_list()) + " | ref" + "".join(f" {r}" for r in a.ref))
+    return lines
+
+
+@pytest.mark.skipif(shutil.which("g++") is None, reason="needs g++")
+def test_allocator_under_sanitizers(tmp_path):
+    exe = tmp_path / "allocator_driver"
+    csrc = os.path.join(ROOT, "paged_attention_amd", "csrc")
+    cmd = ["g++", "-std=c++17", "-O1", "-g", "-fsanitize=address,undefined", "-fno-sanitize-recover=all",
+           "-D__HIP_PLATFORM_AMD__", f"-I{ROOT}/include", f"-I{csrc}", "-I/opt/rocm/include",
+           os.path.join(ROOT, "tests", "native", "allocator_driver.cpp"), os.path.join(csrc, "allocator.cpp"),
+           os.path.join(csrc, "status.cpp"), "-o", str(exe)]
+    subprocess.run(cmd, check=True, capture_output=True)
+    rng = np.random.default_rng(0)
+    for trial in range(30):
+        nb = int(rng.integers(1, 24))
+        bs = int(rng.choice([1, 2, 4, 8, 16]))
+        order = rng.permutation(nb).tolist()
+        ops, lens, nxt = [], {}, 0
+        for _ in range(int(rng.integers(5, 80))):
+            k = rng.integers(0, 7)
+            if k == 0:
+                ops.append(("alloc",))
+            elif k in (1, 2):
+                ops.append(("incref" if k == 1 else "decref", int(rng.integers(-1, nb + 1))))
+            elif k == 3 or not lens:
+                n = int(rng.integers(0, 3 * bs + 1))
+                ops.append(("reserve", nxt, 0, n))
+                lens[nxt] = n
+                nxt += 1
+            else:
+                sid = int(rng.choice(sorted(lens)))
+                if k == 4:
+                    n = int(rng.integers(0, 2 * bs + 1))
+                    ops.append(("reserve", sid, lens[sid], n))
+                    lens[sid] += n
+                elif k == 5:
+                    ops.append(("fork", sid, nxt))
+                    lens[nxt] = lens[sid]
+                    nxt += 1
+                else:
+                    ops.append(("release", sid))
+                    del lens[sid]
+        want = _driver_text(ops, nb, bs, order)
+        # A failed reserve leaves the oracle row untouched; lengths above are
+        # only the requested growth, so resync them from the expected output.
+        script = [f"create {nb} {bs} " + " ".join(map(str, order))]
+        for op in ops:
+            script.append(" ".join(map(str, op)))
+            script.append("state")
+        res = subprocess.run([str(exe)], input="\n".join(script) + "\n", capture_output=True, text=True,
+                             env={**os.environ, "ASAN_OPTIONS": "detect_leaks=1"})
+        assert res.returncode == 0, res.stderr
+        assert res.stdout.split("\n")[:-1] == want, f"trial {trial}"

@@ -1,0 +1,236 @@
+"""GPU parity: the HIP path against the oracle, through the C interface.
+
+Scatter, block copies and allocator indexing must match bit for bit; decode
+attention within 1e-5 (fp32) / 2e-3 (fp16; bf16 adds its own output rounding).
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import paged_attention_amd as pkv
+import workloads
+from oracle import attention as oatt
+from oracle import pool as opool
+from oracle import sizes
+from tests import paged_case as pc
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    yield
+    torch.cuda.synchronize()
+
+
+def _log(msg):
+    print(msg, flush=True)
+
+
+def test_tiny_fp32():
+    wl = workloads.tiny()
+    c = pc.build(wl, DEV)
+    _log(f"tiny: lens {wl.seq_lens.tolist()}")
+    err = pc.compare(c, pc.run_gpu(c))
+    assert err < 1e-5
+    # One token: the output is that token's value row (exactly, in fp32).
+    out = pc.run_gpu(c)
+    assert torch.equal(out[0].cpu(), torch.from_numpy(c.vals["v_seq"][0][0]))
+
+
+SMALL_LENS = [1, 7, 31, 32, 33, 95, 96, 97, 200, 513]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("head_dim", [64, 128])
+@pytest.mark.parametrize("block_size", [8, 16, 32])
+def test_small_cases_all_shapes(dtype, head_dim, block_size):
+    # 5 heads: the last wavefront of each work-group has idle head rows.
+    wl = workloads.custom(SMALL_LENS, num_heads=5, head_dim=head_dim, dtype=dtype, block_size=block_size,
+                          seed=1000 + head_dim + block_size)
+    c = pc.build(wl, DEV)
+    ref = pc.oracle_out(c)
+    for part in (0, 32, 64, 544):
+        _log(f"small {dtype} D{head_dim} bs{block_size} partition {part}")
+        pc.compare(c, pc.run_gpu(c, partition_tokens=part), ref)
+
+
+def test_split_k_boundaries():
+    # Lengths on and just past partition boundaries; split and unsplit agree.
+    lens = [64, 65, 127, 128, 129, 191, 192, 193, 1]
+    wl = workloads.custom(lens, num_heads=8, head_dim=128, dtype="f16", block_size=16, seed=77)
+    c = pc.build(wl, DEV)
+    ref = pc.oracle_out(c)
+    one = pc.run_gpu(c, partition_tokens=256).clone()
+    pc.compare(c, one, ref)
+    for part in (32, 64, 96, 128):
+        split = pc.run_gpu(c, partition_tokens=part)
+        pc.compare(c, split, ref)
+        diff = (split.float() - one.float()).abs().max().item()
+        assert diff <= 2e-3
+
+
+def test_llama7b_layer_full_size():
+    wl = workloads.llama7b_layer()
+    _log(f"7B layer: batch {wl.batch}, sum len {int(wl.seq_lens.sum())}, pool {wl.num_blocks}")
+    c = pc.build(wl, DEV)
+    err = pc.compare(c, pc.run_gpu(c))
+    _log(f"7B layer max err {err:.2e}")
+    assert sizes.fragmentation_tokens(wl.seq_lens, 16) == sum(
+        -(-int(x) // 16) * 16 - int(x) for x in wl.seq_lens)
+
+
+def test_prefix_cow_full_size():
+    wl = workloads.prefix_cow()
+    c = pc.build(wl, DEV)
+    # 63 of the 64 sharers copied the partly filled prefix block; the last one
+    # kept it.  Physical blocks: 32 shared + each sequence's own.
+    assert len(c.cow_pairs) == wl.batch - 1
+    used = wl.num_blocks - c.palloc.num_free()
+    assert used == 32 + sum(-(-int(x) // 16) - 32 for x in wl.seq_lens)
+    ref = pc.oracle_out(c)
+    got = pc.run_gpu(c).clone()
+    err = pc.compare(c, got, ref)
+    _log(f"prefix+CoW max err {err:.2e}, unique/logical bytes "
+         f"{sizes.unique_kv_bytes(c.tables_np, wl.seq_lens, 16, 32, 128, 2) / sizes.logical_kv_bytes(wl.seq_lens, 32, 128, 2):.3f}")
+    # Sharing changes nothing: give every sequence private copies of the
+    # shared blocks (moved with torch, outside the library) -> identical bits.
+    tables = c.tables_np.copy()
+    kc, vc = c.k_cache.clone(), c.v_cache.clone()
+    free = c.palloc.free_list()
+    shared_blocks = [int(b) for b in tables[0, :32]]
+    for s in range(1, wl.batch):
+        for j, b in enumerate(shared_blocks):
+            nb = free.pop()
+            kc[nb] = kc[b]
+            vc[nb] = vc[b]
+            tables[s, j] = nb
+    out2 = torch.empty_like(c.q)
+    pkv.pkv_attention_decode(out2, c.q, kc, vc, torch.tensor(tables, device=DEV), c.lens, wl.max_seq_len,
+                             scale=wl.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(out2.view(torch.int16), got.view(torch.int16))
+
+
+@pytest.mark.parametrize("block_size", [8, 16, 32])
+def test_long13b_full_size(block_size):
+    wl = workloads.long13b(block_size)
+    assert sizes.fragmentation_tokens(wl.seq_lens, block_size) == 0
+    c = pc.build(wl, DEV)
+    err = pc.compare(c, pc.run_gpu(c))
+    _log(f"13B long bs {block_size} max err {err:.2e}")
+
+
+def test_physical_permutation_changes_nothing():
+    wl = workloads.custom([300, 1, 17, 64, 1000, 555], num_heads=32, head_dim=128, dtype="f16", block_size=16,
+                          seed=5)
+    c = pc.build(wl, DEV)
+    base = pc.run_gpu(c).clone()
+    pc.compare(c, base)
+    g = torch.Generator().manual_seed(123)
+    perm = torch.randperm(wl.num_blocks, generator=g)
+    kc = torch.empty_like(c.k_cache)
+    vc = torch.empty_like(c.v_cache)
+    kc[perm.to(DEV)] = c.k_cache
+    vc[perm.to(DEV)] = c.v_cache
+    tables = perm[torch.from_numpy(c.tables_np).long()].to(torch.int32).to(DEV)
+    out = torch.empty_like(c.q)
+    pkv.pkv_attention_decode(out, c.q, kc, vc, tables, c.lens, wl.max_seq_len, scale=wl.scale,
+                             partition_tokens=64)
+    ref64 = torch.empty_like(c.q)
+    pkv.pkv_attention_decode(ref64, c.q, c.k_cache, c.v_cache, c.tables, c.lens, wl.max_seq_len, scale=wl.scale,
+                             partition_tokens=64)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), ref64.view(torch.int16))
+
+
+def test_edge_lengths_and_bad_entries():
+    wl = workloads.custom([0, 1, 40, 77], num_heads=4, head_dim=64, dtype="f16", block_size=16, seed=9)
+    c = pc.build(wl, DEV)
+    out = pc.run_gpu(c)
+    assert torch.count_nonzero(out[0]) == 0          # length 0 -> zero row
+    pc.compare(c, out)
+    # Lengths the kernel must refuse: negative, beyond max_seq_len, beyond
+    # the table row -> NaN rows, and nothing read outside the pools.
+    lens = torch.tensor([-1, 78, 40, 1], dtype=torch.int32, device=DEV)
+    out = torch.zeros_like(c.q)
+    pkv.pkv_attention_decode(out, c.q, c.k_cache, c.v_cache, c.tables, lens, 77, scale=wl.scale)
+    torch.cuda.synchronize()
+    assert torch.isnan(out[0]).all() and torch.isnan(out[1]).all()
+    assert torch.isfinite(out[2]).all() and torch.isfinite(out[3]).all()
+    # A table entry outside [0, num_blocks) poisons only that sequence.
+    tables = c.tables.clone()
+    tables[2, 1] = wl.num_blocks + 5
+    tables[3, 0] = -3
+    out = torch.zeros_like(c.q)
+    pkv.pkv_attention_decode(out, c.q, c.k_cache, c.v_cache, tables, c.lens, wl.max_seq_len, scale=wl.scale,
+                             partition_tokens=32)
+    torch.cuda.synchronize()
+    assert torch.isnan(out[2]).all() and torch.isnan(out[3]).all()
+    ref = pc.oracle_out(c)
+    got = out[:2].float().cpu().numpy().astype(np.float64)
+    assert np.max(np.abs(got - ref[:2])) <= 2e-3
+
+
+def test_append_skips_negative_and_out_of_range_slots():
+    nb, bs, h, d = 6, 8, 2, 64
+    rng = np.random.default_rng(4)
+    for dt in ("f32", "f16", "bf16"):
+        okp = np.full((nb, bs, h, d), workloads.nan_storage(dt), dtype=workloads.storage_np_dtype(dt))
+        ovp = okp.copy()
+        kc = torch.full((nb, bs, h, d), float("nan"), dtype=pc.TORCH_DTYPE[dt], device=DEV)
+        vc = torch.full_like(kc, float("nan"))
+        kn = workloads.to_storage(rng.standard_normal((5, h, d), dtype=np.float32), dt)
+        vn = workloads.to_storage(rng.standard_normal((5, h, d), dtype=np.float32), dt)
+        slots = [3, -1, 47, nb * bs, 9]
+        pkv.pkv_append(pc.to_device(kn, dt, DEV), pc.to_device(vn, dt, DEV),
+                       torch.tensor(slots, dtype=torch.int64, device=DEV), kc, vc)
+        torch.cuda.synchronize()
+        keep = [s if 0 <= s < nb * bs else -1 for s in slots]
+        opool.append(okp, ovp, kn, vn, keep)
+        assert np.array_equal(pc.to_bits(kc), pc.storage_bits(okp))
+        assert np.array_equal(pc.to_bits(vc), pc.storage_bits(ovp))
+
+
+def test_copy_blocks_many_layers():
+    nl, nb, bs, h, d = 35, 12, 16, 4, 128    # more layers than one launch carries
+    rng = np.random.default_rng(8)
+    kp = [workloads.to_storage(rng.standard_normal((nb, bs, h, d), dtype=np.float32), "bf16") for _ in range(nl)]
+    vp = [workloads.to_storage(rng.standard_normal((nb, bs, h, d), dtype=np.float32), "bf16") for _ in range(nl)]
+    kd = [pc.to_device(x, "bf16", DEV) for x in kp]
+    vd = [pc.to_device(x, "bf16", DEV) for x in vp]
+    pairs = [(1, 7), (4, 2), (11, 0), (3, 3)]
+    pt = torch.tensor(pairs + [(nb + 1, 5), (5, -1)], dtype=torch.int32, device=DEV)
+    pkv.pkv_copy_blocks(kd, vd, pt)
+    torch.cuda.synchronize()
+    opool.copy_blocks(kp, vp, [p for p in pairs if p[0] != p[1]])
+    for i in range(nl):
+        assert np.array_equal(pc.to_bits(kd[i]), pc.storage_bits(kp[i]))
+        assert np.array_equal(pc.to_bits(vd[i]), pc.storage_bits(vp[i]))
+
+
+def test_empty_batch_and_tiny_launch():
+    wl = workloads.custom([5], num_heads=1, head_dim=64, dtype="f32", block_size=8, seed=3)
+    c = pc.build(wl, DEV)
+    pc.compare(c, pc.run_gpu(c))
+    empty = torch.empty((0, 1, 64), dtype=torch.float32, device=DEV)
+    pkv.pkv_attention_decode(empty, empty, c.k_cache, c.v_cache, c.tables[:0], c.lens[:0], 8)
+    torch.cuda.synchronize()
+
+
+def test_scale_is_applied():
+    wl = workloads.custom([50, 9], num_heads=4, head_dim=128, dtype="f32", block_size=16, seed=12)
+    c = pc.build(wl, DEV)
+    for scale in (0.0, 0.5, 2.0 / math.sqrt(128)):
+        out = torch.empty_like(c.q)
+        pkv.pkv_attention_decode(out, c.q, c.k_cache, c.v_cache, c.tables, c.lens, wl.max_seq_len, scale=scale)
+        torch.cuda.synchronize()
+        ref = oatt.decode_attention(c.vals["q"], c.ok_pool, c.ov_pool, c.tables_np, wl.seq_lens, "f32", scale)
+        pc.compare(c, out, ref)
