@@ -39,7 +39,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=100)
     p.add_argument("--warmup", type=int, default=10)
-    p.add_argument("--partition", type=int, default=0, help="split-K partition tokens (0 = library choice)")
+    p.add_argument("--work-groups", type=int, default=0, help="decode work-groups (0 = library choice)")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target length of the oracle timing sample")
     p.add_argument("--no-cpu", action="store_true", help="skip the cpu_baseline leg")
     p.add_argument("--copy-calibration", action="store_true",
@@ -117,9 +117,8 @@ def main():
     k_new = torch.randn((total_steps, B, H, D), generator=gen, device=dev, dtype=torch.float32).to(dt)
     v_new = torch.randn((total_steps, B, H, D), generator=gen, device=dev, dtype=torch.float32).to(dt)
     out = torch.empty((B, H, D), dtype=dt, device=dev)
-    part = args.partition or pkv.pkv_decode_partition_tokens(B, H, D, "f16", bs, max_len)
-    ws_bytes = pkv.pkv_decode_workspace_bytes(B, H, D, "f16", bs, max_len, part)
-    workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    wgs = args.work_groups or pkv.pkv_decode_work_groups()
+    workspace = pkv.decode_workspace(B, H, D, "f16", wgs, device=dev)
     # device metadata (double-buffered) and pinned host staging (ring)
     ring = 4
     d_tables = [torch.empty((B, maxb), dtype=torch.int32, device=dev) for _ in range(2)]
@@ -162,7 +161,7 @@ def main():
         pkv.pkv_append(k_new[i], v_new[i], d_slots[d], k_cache, v_cache)   # a4: scatter
         ev[i][0].record(stream)
         pkv.pkv_attention_decode(out, q_all[i], k_cache, v_cache, d_tables[d], d_lens[d], max_len,   # a5, a6
-                                 scale=wl.scale, partition_tokens=part, workspace=workspace)
+                                 scale=wl.scale, work_groups=wgs, workspace=workspace)
         ev[i][1].record(stream)
         kv_bytes.append(int(cur.astype(np.int64).sum()) * 2 * H * D * esz)
         table_entries.append(int(((cur.astype(np.int64) + bs - 1) // bs).sum()))
@@ -196,7 +195,7 @@ def main():
         s0.record(stream)
         for _ in range(args.attention_only):
             pkv.pkv_attention_decode(out, q_all[-1], k_cache, v_cache, d_tables[(total_steps - 1) % 2],
-                                     d_lens[(total_steps - 1) % 2], max_len, scale=wl.scale, partition_tokens=part,
+                                     d_lens[(total_steps - 1) % 2], max_len, scale=wl.scale, work_groups=wgs,
                                      workspace=workspace)
         s1.record(stream)
         torch.cuda.synchronize()
@@ -239,7 +238,7 @@ def main():
         "dtype": "f16",
         "data": "synthetic (seeded; K/V/Q ~ N(0,1) in fp16)",
         "config": {"workload": wl.title, "batch": B, "heads": H, "head_dim": D, "block_size": bs,
-                   "pool_blocks": wl.num_blocks, "partition_tokens": part,
+                   "pool_blocks": wl.num_blocks, "work_groups": wgs,
                    "mean_seq_len": round(mean_len_sum / B, 1)},
         "hbm_peak_frac": round(value / HBM_PEAK_GBS, 4),
         "token_steps_per_s": round(B * args.steps / elapsed, 1),

@@ -180,17 +180,19 @@ PKV_API int pkv_copy_blocks(void* const* k_caches, void* const* v_caches, int32_
                             const int32_t* pairs, int32_t n_pairs, int32_t num_blocks, size_t bytes_per_block,
                             hipStream_t stream);
 
-/* Tokens per split-K partition the library picks when pkv_attention_decode
- * is called with partition_tokens = 0 (a multiple of block_size). */
-PKV_API int32_t pkv_decode_partition_tokens(int32_t batch, int32_t num_heads, int32_t head_dim, pkv_dtype dtype,
-                                            int32_t block_size, int32_t max_seq_len);
+/* Work-groups pkv_attention_decode launches when called with
+ * num_work_groups = 0: one per compute unit of the current device (256 on
+ * MI355X).  PKV_ERR_HIP if no device is current. */
+PKV_API int32_t pkv_decode_work_groups(void);
 
-/* Device workspace pkv_attention_decode needs for these sizes
- * (partition_tokens = 0: the automatic choice).  Float32 partial results:
- * batch * ceil(max_seq_len / P) * num_heads * (head_dim + 2) * 4 bytes,
- * rounded up.  Returns 0 for an invalid shape. */
+/* Device workspace pkv_attention_decode needs for `num_work_groups` (0 = the
+ * automatic count): a per-sequence plan (2 int32 per sequence and head
+ * slice, at most 8190 per launch) and float32 partial softmax states for
+ * 2 * num_work_groups pieces of num_heads * (head_dim + 2) floats, each
+ * region 256-byte aligned.  It does not depend on sequence lengths.
+ * Returns 0 for an invalid shape. */
 PKV_API size_t pkv_decode_workspace_bytes(int32_t batch, int32_t num_heads, int32_t head_dim, pkv_dtype dtype,
-                                          int32_t block_size, int32_t max_seq_len, int32_t partition_tokens);
+                                          int32_t num_work_groups);
 
 /* Decode attention through the block table.
  * For every sequence b < batch and head h < num_heads, with L = seq_lens[b]:
@@ -207,13 +209,16 @@ PKV_API size_t pkv_decode_workspace_bytes(int32_t batch, int32_t num_heads, int3
  *   seq_lens: device int32 [batch].  max_seq_len: host upper bound of every
  *     seq_lens entry (sizes the launch and the workspace).
  *   scale: softmax scale (1/sqrt(head_dim) for plain scaled dot-product).
- *   partition_tokens: split-K partition length (0 = automatic; otherwise a
- *     multiple of block_size and of 8, at least 32).  Sequences longer than
- *     one partition are processed in parallel pieces whose partial softmax
- *     states (max, sum, weighted values) are merged afterwards; partitions
- *     depend only on logical positions, so the result does not depend on
- *     where the blocks sit physically.
- *   workspace: device memory of at least pkv_decode_workspace_bytes(...).
+ *   num_work_groups: 0 = automatic (pkv_decode_work_groups), else the
+ *     number of work-groups.  The tokens of all sequences are laid end to
+ *     end in chunks of 8 and every work-group takes an equal contiguous
+ *     range of chunks, so the work is balanced however ragged the lengths
+ *     are.  A sequence split across ranges is computed in pieces whose
+ *     partial softmax states (max, sum, weighted values) a second kernel on
+ *     the same stream merges.  Cut points depend only on logical positions,
+ *     so the result does not depend on where the blocks sit physically.
+ *   workspace: device memory of at least pkv_decode_workspace_bytes(...)
+ *     (no initialisation needed; calls sharing one must not overlap).
  * L = 0 gives a zero row.  A sequence whose length is negative or exceeds
  * max_seq_len or max_blocks_per_seq * block_size, or whose table holds an id
  * outside [0, num_blocks) in its first ceil(L / block_size) entries, gets
@@ -223,7 +228,7 @@ PKV_API int pkv_attention_decode(void* out, const void* q, const void* k_cache, 
                                  const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* seq_lens,
                                  int32_t max_seq_len, int32_t batch, int32_t num_heads, int32_t head_dim,
                                  int32_t block_size, int32_t num_blocks, float scale, pkv_dtype dtype,
-                                 int32_t partition_tokens, void* workspace, size_t workspace_bytes,
+                                 int32_t num_work_groups, void* workspace, size_t workspace_bytes,
                                  hipStream_t stream);
 
 #ifdef __cplusplus

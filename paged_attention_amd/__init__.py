@@ -5,7 +5,7 @@ here checks tensor shapes and dtypes, passes raw pointers and the current
 HIP stream, and turns status codes into exceptions.  All computation happens
 in the library (HIP kernels and the C++ allocator); there is no Python or CPU
 fallback, and importing this package fails loudly if ``libpkv.so`` has not
-been built (``python -m paged_attention_amd.build``).
+been built (``python paged_attention_amd/build.py``).
 
 Entry points keep the C names:
 
@@ -54,7 +54,7 @@ class InvalidArgument(PkvError, ValueError):
 
 def _load():
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m paged_attention_amd.build`")
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python paged_attention_amd/build.py`")
     lib = ctypes.CDLL(LIB_PATH)
     i32, i64, vp, sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t
     p32, p64 = ctypes.POINTER(i32), ctypes.POINTER(i64)
@@ -78,8 +78,8 @@ def _load():
         "pkv_seq_release": (ctypes.c_int, [vp, p32, i32]),
         "pkv_append": (ctypes.c_int, [vp, vp, i32, vp, vp, vp, i32, i32, i32, i32, ctypes.c_int, vp]),
         "pkv_copy_blocks": (ctypes.c_int, [ctypes.POINTER(vp), ctypes.POINTER(vp), i32, vp, i32, i32, sz, vp]),
-        "pkv_decode_partition_tokens": (i32, [i32, i32, i32, ctypes.c_int, i32, i32]),
-        "pkv_decode_workspace_bytes": (sz, [i32, i32, i32, ctypes.c_int, i32, i32, i32]),
+        "pkv_decode_work_groups": (i32, []),
+        "pkv_decode_workspace_bytes": (sz, [i32, i32, i32, ctypes.c_int, i32]),
         "pkv_attention_decode": (ctypes.c_int, [vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, i32, i32,
                                                 ctypes.c_float, ctypes.c_int, i32, vp, sz, vp]),
     }
@@ -133,9 +133,9 @@ class BlockAllocator:
         self.block_size = block_size
 
     def close(self):
-        if getattr(self, "_h", None):
+        if getattr(self, "_h", None) and _lib is not None:
             _lib.pkv_allocator_destroy(self._h)
-            self._h = None
+        self._h = None
 
     def __del__(self):
         self.close()
@@ -292,22 +292,29 @@ def pkv_copy_blocks(k_caches, v_caches, pairs, stream=None) -> None:
                                 bytes_per_block, _stream(stream)))
 
 
-def pkv_decode_partition_tokens(batch, num_heads, head_dim, dtype, block_size, max_seq_len) -> int:
-    return _check(_lib.pkv_decode_partition_tokens(batch, num_heads, head_dim, DTYPE_CODES[dtype], block_size,
-                                                   max_seq_len))
+def pkv_decode_work_groups() -> int:
+    """Work-groups decode attention launches by default on the current device."""
+    return _check(_lib.pkv_decode_work_groups())
 
 
-def pkv_decode_workspace_bytes(batch, num_heads, head_dim, dtype, block_size, max_seq_len,
-                               partition_tokens=0) -> int:
-    return int(_lib.pkv_decode_workspace_bytes(batch, num_heads, head_dim, DTYPE_CODES[dtype], block_size,
-                                               max_seq_len, partition_tokens))
+def pkv_decode_workspace_bytes(batch, num_heads, head_dim, dtype, work_groups=0) -> int:
+    return int(_lib.pkv_decode_workspace_bytes(batch, num_heads, head_dim, DTYPE_CODES[dtype], work_groups))
 
 
 _DT_NAMES = {PKV_F32: "f32", PKV_F16: "f16", PKV_BF16: "bf16"}
 
 
+def decode_workspace(batch, num_heads, head_dim, dtype, work_groups=0, device="cuda"):
+    """Allocate a workspace for these decode sizes (a uint8 tensor)."""
+    torch = _torch()
+    need = pkv_decode_workspace_bytes(batch, num_heads, head_dim, dtype, work_groups)
+    if need == 0:
+        raise InvalidArgument(PKV_ERR_INVALID, "decode_workspace: unsupported sizes")
+    return torch.empty(need, dtype=torch.uint8, device=device)
+
+
 def pkv_attention_decode(out, q, k_cache, v_cache, block_tables, seq_lens, max_seq_len, scale=None,
-                         partition_tokens=0, workspace=None, stream=None) -> None:
+                         work_groups=0, workspace=None, stream=None) -> None:
     """Decode attention of ``q`` ([B][H][D]) over each sequence's paged K/V; writes ``out``."""
     torch = _torch()
     nb, bs, h, d = k_cache.shape
@@ -321,18 +328,20 @@ def pkv_attention_decode(out, q, k_cache, v_cache, block_tables, seq_lens, max_s
     code = _dtype_code(q)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    need = int(_lib.pkv_decode_workspace_bytes(batch, h, d, code, bs, max_seq_len, partition_tokens))
+    if batch == 0:
+        return
     if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+        workspace = decode_workspace(batch, h, d, _DT_NAMES[code], work_groups, q.device)
     _check(_lib.pkv_attention_decode(
         _dev(out, "out"), _dev(q, "q"), _dev(k_cache, "k_cache", ndim=4), _dev(v_cache, "v_cache", ndim=4),
         _dev(block_tables, "block_tables", torch.int32), block_tables.shape[1],
         _dev(seq_lens, "seq_lens", torch.int32), int(max_seq_len), batch, h, d, bs, nb, float(scale), code,
-        int(partition_tokens), _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+        int(work_groups), _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
         _stream(stream)))
 
 
 __all__ = [
     "BlockAllocator", "PkvError", "OutOfBlocks", "InvalidArgument", "pkv_append", "pkv_copy_blocks",
-    "pkv_attention_decode", "pkv_decode_workspace_bytes", "pkv_decode_partition_tokens", "version", "LIB_PATH",
+    "pkv_attention_decode", "pkv_decode_workspace_bytes", "pkv_decode_work_groups",
+    "decode_workspace", "version", "LIB_PATH",
 ]

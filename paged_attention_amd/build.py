@@ -1,9 +1,10 @@
 """Builds libpkv.so in-tree: HIP kernels for gfx950 plus the host allocator.
 
-``python -m paged_attention_amd.build`` (or ``build()``) compiles every source
+``python paged_attention_amd/build.py`` (or ``build()``) compiles every source
 under ``csrc/`` with hipcc and links ``paged_attention_amd/libpkv.so``.  The
 shared library is what the Python binding loads; nothing is compiled at import
-time.
+time.  This file imports nothing from the package, so it runs even when no
+library (or a stale one) is present.
 """
 
 from __future__ import annotations

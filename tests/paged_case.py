@@ -152,10 +152,10 @@ def oracle_out(c: Case, heads=None) -> np.ndarray:
                                  heads=heads)
 
 
-def run_gpu(c: Case, partition_tokens=0, out=None):
+def run_gpu(c: Case, work_groups=0, out=None):
     out = c.out if out is None else out
     pkv.pkv_attention_decode(out, c.q, c.k_cache, c.v_cache, c.tables, c.lens, c.wl.max_seq_len, scale=c.wl.scale,
-                             partition_tokens=partition_tokens)
+                             work_groups=work_groups)
     torch.cuda.synchronize()
     return out
 

@@ -61,8 +61,8 @@ def test_device_calls_reject_bad_shapes_before_launch():
     st = lib.pkv_attention_decode(null, null, null, null, null, 4, null, 64, 1, 4, 128, 16, 8, 1.0, 7, 0, null, 0,
                                   null)
     assert st == pkv.PKV_ERR_INVALID
-    # Partition length must be a positive multiple of 32.
-    st = lib.pkv_attention_decode(null, null, null, null, null, 4, null, 64, 1, 4, 128, 16, 8, 1.0, 1, 48, null, 0,
+    # The work-group count must be 0 (automatic) or a positive count.
+    st = lib.pkv_attention_decode(null, null, null, null, null, 4, null, 64, 1, 4, 128, 16, 8, 1.0, 1, -3, null, 0,
                                   null)
     assert st == pkv.PKV_ERR_INVALID
     # Null pointers with a non-empty batch.
@@ -80,18 +80,17 @@ def test_device_calls_reject_bad_shapes_before_launch():
     assert lib.pkv_copy_blocks(None, None, 1, null, 0, 8, 4096, null) == pkv.PKV_OK
 
 
-def test_workspace_and_partition_queries():
-    # One partition: no workspace.  Otherwise batch*parts*heads*(D floats) + (m,l) pairs.
-    assert pkv.pkv_decode_workspace_bytes(4, 4, 64, "f32", 16, 64, 64) == 0
-    b, h, d, ml, part = 32, 32, 128, 2048, 64
-    parts = ml // part
-    want_acc = -(-(b * parts * h * d * 4) // 256) * 256
-    want_ml = -(-(b * parts * h * 8) // 256) * 256
-    assert pkv.pkv_decode_workspace_bytes(b, h, d, "f16", 16, ml, part) == want_acc + want_ml
-    auto = pkv.pkv_decode_partition_tokens(b, h, d, "f16", 16, ml)
-    assert auto % 32 == 0 and auto >= 32
-    assert pkv.pkv_decode_workspace_bytes(b, h, d, "f16", 16, ml, 0) == \
-        pkv.pkv_decode_workspace_bytes(b, h, d, "f16", 16, ml, auto)
-    assert pkv.pkv_decode_workspace_bytes(b, h, 96, "f16", 16, ml, 0) == 0
-    with pytest.raises(pkv.PkvError):
-        pkv.pkv_decode_partition_tokens(b, h, 96, "f16", 16, ml)
+def test_workspace_queries():
+    up = lambda x: -(-x // 256) * 256  # noqa: E731
+    b, h, d, wg = 32, 32, 128, 512
+    # plan (2 int32 per sequence) + 2*wg partial pieces of h*(d floats + (m, l))
+    want = up(b * 8) + up(2 * wg * h * d * 4) + up(2 * wg * h * 8)
+    assert pkv.pkv_decode_workspace_bytes(b, h, d, "f16", wg) == want
+    # 160 heads at fp16 x 128: 40 wavefronts -> 3 head slices of <= 16 wavefronts
+    want = up(b * 3 * 8) + up(2 * wg * 160 * d * 4) + up(2 * wg * 160 * 8)
+    assert pkv.pkv_decode_workspace_bytes(b, 160, d, "bf16", wg) == want
+    # The plan holds at most one launch's worth of sequences (8190 per head slice).
+    big = pkv.pkv_decode_workspace_bytes(20000, 4, 64, "f32", 8)
+    assert big == up(8190 * 8) + up(2 * 8 * 4 * 64 * 4) + up(2 * 8 * 4 * 8)
+    assert pkv.pkv_decode_workspace_bytes(b, h, 96, "f16", wg) == 0
+    assert pkv.pkv_decode_workspace_bytes(b, h, d, "f16", -1) == 0

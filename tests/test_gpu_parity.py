@@ -57,21 +57,23 @@ def test_small_cases_all_shapes(dtype, head_dim, block_size):
                           seed=1000 + head_dim + block_size)
     c = pc.build(wl, DEV)
     ref = pc.oracle_out(c)
-    for part in (0, 32, 64, 544):
-        _log(f"small {dtype} D{head_dim} bs{block_size} partition {part}")
-        pc.compare(c, pc.run_gpu(c, partition_tokens=part), ref)
+    for wg in (0, 1, 7, 64, 100000):
+        _log(f"small {dtype} D{head_dim} bs{block_size} work-groups {wg}")
+        pc.compare(c, pc.run_gpu(c, work_groups=wg), ref)
 
 
-def test_split_k_boundaries():
-    # Lengths on and just past partition boundaries; split and unsplit agree.
-    lens = [64, 65, 127, 128, 129, 191, 192, 193, 1]
+def test_split_sequences_agree_with_unsplit():
+    # One work-group sees every sequence whole (nothing to merge); more
+    # work-groups cut sequences at chunk boundaries, down to one chunk each.
+    lens = [64, 65, 127, 128, 129, 191, 192, 193, 1, 8, 9]
     wl = workloads.custom(lens, num_heads=8, head_dim=128, dtype="f16", block_size=16, seed=77)
     c = pc.build(wl, DEV)
     ref = pc.oracle_out(c)
-    one = pc.run_gpu(c, partition_tokens=256).clone()
+    one = pc.run_gpu(c, work_groups=1).clone()
     pc.compare(c, one, ref)
-    for part in (32, 64, 96, 128):
-        split = pc.run_gpu(c, partition_tokens=part)
+    total_chunks = sum(-(-x // 8) for x in lens)
+    for wg in (2, 3, 13, 64, total_chunks, total_chunks + 5, 4096):
+        split = pc.run_gpu(c, work_groups=wg)
         pc.compare(c, split, ref)
         diff = (split.float() - one.float()).abs().max().item()
         assert diff <= 2e-3
@@ -142,11 +144,10 @@ def test_physical_permutation_changes_nothing():
     vc[perm.to(DEV)] = c.v_cache
     tables = perm[torch.from_numpy(c.tables_np).long()].to(torch.int32).to(DEV)
     out = torch.empty_like(c.q)
-    pkv.pkv_attention_decode(out, c.q, kc, vc, tables, c.lens, wl.max_seq_len, scale=wl.scale,
-                             partition_tokens=64)
+    pkv.pkv_attention_decode(out, c.q, kc, vc, tables, c.lens, wl.max_seq_len, scale=wl.scale, work_groups=64)
     ref64 = torch.empty_like(c.q)
     pkv.pkv_attention_decode(ref64, c.q, c.k_cache, c.v_cache, c.tables, c.lens, wl.max_seq_len, scale=wl.scale,
-                             partition_tokens=64)
+                             work_groups=64)
     torch.cuda.synchronize()
     assert torch.equal(out.view(torch.int16), ref64.view(torch.int16))
 
@@ -171,7 +172,7 @@ def test_edge_lengths_and_bad_entries():
     tables[3, 0] = -3
     out = torch.zeros_like(c.q)
     pkv.pkv_attention_decode(out, c.q, c.k_cache, c.v_cache, tables, c.lens, wl.max_seq_len, scale=wl.scale,
-                             partition_tokens=32)
+                             work_groups=5)
     torch.cuda.synchronize()
     assert torch.isnan(out[2]).all() and torch.isnan(out[3]).all()
     ref = pc.oracle_out(c)
@@ -223,6 +224,34 @@ def test_empty_batch_and_tiny_launch():
     empty = torch.empty((0, 1, 64), dtype=torch.float32, device=DEV)
     pkv.pkv_attention_decode(empty, empty, c.k_cache, c.v_cache, c.tables[:0], c.lens[:0], 8)
     torch.cuda.synchronize()
+
+
+def test_workspace_reused_across_calls_and_shapes():
+    # One workspace, never cleared, serves many calls of different shapes.
+    wa = workloads.custom([700, 65, 1, 300], num_heads=40, head_dim=128, dtype="bf16", block_size=32, seed=21)
+    wb = workloads.custom([90, 1000], num_heads=8, head_dim=64, dtype="f16", block_size=8, seed=22)
+    ca, cb = pc.build(wa, DEV), pc.build(wb, DEV)
+    ra, rb = pc.oracle_out(ca), pc.oracle_out(cb)
+    ws = torch.full((64 << 20,), 0x7F, dtype=torch.uint8, device=DEV)  # garbage, not zeros
+    for i in range(4):
+        for c, ref in ((ca, ra), (cb, rb)):
+            out = torch.empty_like(c.q)
+            pkv.pkv_attention_decode(out, c.q, c.k_cache, c.v_cache, c.tables, c.lens, c.wl.max_seq_len,
+                                     scale=c.wl.scale, work_groups=64 + 32 * (i % 2), workspace=ws)
+            torch.cuda.synchronize()
+            pc.compare(c, out, ref)
+
+
+def test_batch_larger_than_one_launch():
+    # More sequences than one launch's prefix arrays hold: the library runs
+    # the batch in slices.
+    rng = np.random.default_rng(31)
+    lens = rng.integers(0, 20, size=9000)
+    wl = workloads.custom(lens, num_heads=4, head_dim=64, dtype="f32", block_size=8, seed=31)
+    c = pc.build(wl, DEV, check_pools=False)
+    ref = pc.oracle_out(c)
+    for wg in (0, 300):
+        pc.compare(c, pc.run_gpu(c, work_groups=wg), ref)
 
 
 def test_scale_is_applied():
