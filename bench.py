@@ -1,26 +1,34 @@
 """Decode-step benchmark for paged-KV attention on one MI355X.
 
-One step = the whole decode path for one batch: host block reservation for
-the new token of every sequence (C++ allocator), staging of slots, block
-tables and lengths to the device, copy-on-write block copies (when any),
-scatter of the new K/V rows (pkv_append) and decode attention over the paged
-cache (pkv_attention_decode).  Inputs are resident in HBM before timing.
+One step = the whole decode path for one batch:
+  1. host block reservation for every sequence's new token (C++ allocator),
+  2. staging of slots, block tables and lengths to the device (pinned memory,
+     asynchronous copies on the compute stream),
+  3. copy-on-write block copies (pkv_copy_blocks) when a reservation produced any,
+  4. scatter of the new K/V rows (pkv_append), and
+  5. decode attention over the paged cache (pkv_attention_decode),
+with 4-5 repeated per layer for multi-layer workloads.  Inputs are resident in
+HBM before timing; sequences grow by one token per step.
 
-Default workload: one layer of a 7B-shaped model (32 heads x 128, fp16,
-block 16, batch 32, lengths uniform on [128, 2048], blocks scattered through
-a pool of 1.3x the blocks needed).  The sequences grow by one token per step.
+Default workload: one layer of a 7B-shaped model (32 heads x 128, fp16, block
+16, batch 32, lengths uniform on [128, 2048], blocks scattered through a pool
+of 1.3x the blocks needed).  ``--workload full7b_step`` runs the 32-layer step
+(batch 256, lognormal lengths, 30 % sharing a 256-token prefix, pool = 85 % of
+free HBM); ``--workload long13b`` the 40-head bf16 4096-token case.
 
 Prints one JSON line.  ``value`` is KV GB/s over the whole timed step (K+V
-bytes attention reads / step time); ``roofline`` reports the decode-attention
-launch alone, timed with HIP events on its stream; ``cpu_baseline`` times the
-oracle on a bounded sample of the same workload on the host cores.
+bytes attention reads / step time).  ``roofline`` reports the decode-attention
+call (decode kernel + merge kernel) timed with HIP events on its stream, and
+the HBM traffic rocprofv3 counted for it when the recorded counters belong to
+the current kernel source.  ``cpu_baseline`` times the oracle on a bounded
+sample of the same workload on the host cores.
 """
 
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
-import math
 import os
 import sys
 import time
@@ -29,59 +37,85 @@ import numpy as np
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
+# Host-to-device staging copies through the runtime's blit kernels on the
+# compute queue: the copy engine path makes every step's kernels wait on a
+# cross-engine signal (measured 20-45 us per step on MI355X).
+os.environ.setdefault("HSA_ENABLE_SDMA", "0")
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, 8 TB/s
 METRIC = "paged-attn decode KV GB/s and % of MI355X HBM peak; tokens-steps/sec"
+KERNEL_SOURCE = os.path.join(ROOT, "paged_attention_amd", "csrc", "kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
 
 
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=100)
+    p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", default="llama7b_layer", choices=["llama7b_layer", "long13b", "full7b_step"])
+    p.add_argument("--block-size", type=int, default=16, help="block size of the long13b workload")
     p.add_argument("--work-groups", type=int, default=0, help="decode work-groups (0 = library choice)")
-    p.add_argument("--cpu-seconds", type=float, default=15.0, help="target length of the oracle timing sample")
+    p.add_argument("--ring", type=int, default=4, help="host staging buffers (how many steps the host may run ahead)")
+    p.add_argument("--cpu-seconds", type=float, default=12.0, help="target length of the oracle timing sample")
     p.add_argument("--no-cpu", action="store_true", help="skip the cpu_baseline leg")
     p.add_argument("--copy-calibration", action="store_true",
-                   help="also run a plain 1 GiB device copy (reference for HBM byte counters)")
-    p.add_argument("--attention-only", type=int, default=0,
-                   help="after the timed steps, launch decode attention N more times back to back")
+                   help="also run a plain 1 GiB device-to-device copy (reference for HBM byte counters)")
     return p.parse_args()
 
 
-def cpu_baseline(wl, lens_now, k_rows_fn, target_s):
-    """Time the oracle on a sample of sequences of the same workload (host cores)."""
+def source_hash() -> str:
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def recorded_traffic(workload: str):
+    """HBM bytes per decode-attention call from committed rocprofv3 counters, if still current."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    entry = rec.get(workload)
+    if not entry or entry.get("kernel_source_sha256_16") != source_hash():
+        return None
+    return entry.get("bytes_per_call")
+
+
+def cpu_baseline(wl, sample_rows, target_s):
+    """Time the oracle on sequences of the same workload until ~target_s of work."""
     from oracle import attention as oatt
 
     try:
         from threadpoolctl import threadpool_info
 
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:  # threadpoolctl missing: the oracle is single threaded numpy
+    except Exception:  # no threadpoolctl: numpy's BLAS threads unknown, report one
         cores = 1
-    h, d, dt = wl.num_heads, wl.head_dim, wl.dtype
+    h, d = wl.num_heads, wl.head_dim
     order = np.random.default_rng(99).permutation(wl.batch)
-    done_bytes, spent, used = 0, 0.0, []
-    for b in order:
-        L = int(lens_now[b])
-        q, keys, vals = k_rows_fn(int(b), L)
+    done_bytes, spent, seqs, tokens = 0, 0.0, 0, 0
+    i = 0
+    while spent < target_s and i < 100 * wl.batch:
+        b = int(order[i % wl.batch])
+        i += 1
+        q, keys, vals = sample_rows(b)
         t0 = time.perf_counter()
-        oatt.contiguous_attention(q[None], [keys], [vals], dt, wl.scale)
+        oatt.contiguous_attention(q[None], [keys], [vals], wl.dtype, wl.scale)
         spent += time.perf_counter() - t0
-        done_bytes += L * 2 * h * d * wl.dtype_bytes
-        used.append(int(b))
-        if spent >= target_s:
-            break
+        done_bytes += keys.shape[0] * 2 * h * d * wl.dtype_bytes
+        seqs += 1
+        tokens += keys.shape[0]
     return {"value": round(done_bytes / spent / 1e9, 4), "unit": "GB/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"numpy float64 oracle over {len(used)} of {wl.batch} sequences of the same workload "
-                      f"({sum(int(lens_now[b]) for b in used)} tokens x {h} heads), {spent:.1f} s"}
+            "sample": f"numpy float64 oracle, {seqs} sequence decodes of this workload ({tokens} tokens x {h} heads, "
+                      f"one layer), {spent:.1f} s of oracle time"}
 
 
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported on this single-GPU build "
-              f"(sharding is described in the design notes)", file=sys.stderr)
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported by this single-GPU build "
+              f"(how the path would shard is described in the design notes)", file=sys.stderr)
         sys.exit(2)
     import torch
 
@@ -90,80 +124,126 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    wl = workloads.llama7b_layer()
-    B, H, D, bs = wl.batch, wl.num_heads, wl.head_dim, wl.block_size
-    dt = torch.float16
-    esz = 2
     total_steps = args.warmup + args.steps
-    hist = wl.seq_lens.astype(np.int64) - 1            # tokens already cached before the first step
-    max_len = int(wl.seq_lens.max()) + total_steps
+    if args.workload == "llama7b_layer":
+        wl = workloads.llama7b_layer()
+    elif args.workload == "long13b":
+        wl = workloads.long13b(args.block_size)
+    else:
+        # 32 layers; the pool takes 85 % of the free device memory.
+        free, _ = torch.cuda.mem_get_info()
+        per_block = 32 * 2 * 16 * 32 * 128 * 2
+        wl = workloads.full7b_step(int(0.85 * free) // per_block)
+    B, H, D, bs, NL = wl.batch, wl.num_heads, wl.head_dim, wl.block_size, wl.num_layers
+    tdt = {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32}[wl.dtype]
+    esz = wl.dtype_bytes
+    lens0 = wl.seq_lens.astype(np.int64)
+    max_len = int(lens0.max()) + total_steps
     maxb = -(-max_len // bs)
-    print(f"[bench] workload: {wl.title}; steps {args.steps} warmup {args.warmup}", file=sys.stderr, flush=True)
+    print(f"[bench] {wl.title}; pool {wl.num_blocks} blocks; steps {args.steps} warmup {args.warmup}",
+          file=sys.stderr, flush=True)
 
-    # --- set-up (not timed): allocator, pools, history prefill ------------
+    # --- set-up (not timed): allocator, pools, history ---------------------
     alloc = pkv.BlockAllocator(wl.num_blocks, bs, wl.free_order)
     tables = np.zeros((B, maxb), dtype=np.int32)
     nblk = np.zeros(B, dtype=np.int32)
-    slots, pairs = alloc.reserve_batch(tables, nblk, np.zeros(B, dtype=np.int32), hist)
-    k_cache = torch.full((wl.num_blocks, bs, H, D), float("nan"), dtype=dt, device=dev)
-    v_cache = torch.full_like(k_cache, float("nan"))
-    gen = torch.Generator(device=dev).manual_seed(2024)
-    n_hist = int(hist.sum())
-    k_hist = torch.randn((n_hist, H, D), generator=gen, device=dev, dtype=torch.float32).to(dt)
-    v_hist = torch.randn((n_hist, H, D), generator=gen, device=dev, dtype=torch.float32).to(dt)
-    pkv.pkv_append(k_hist, v_hist, torch.from_numpy(slots).to(dev), k_cache, v_cache)
-    # per-step inputs, resident in HBM before timing
-    q_all = torch.randn((total_steps, B, H, D), generator=gen, device=dev, dtype=torch.float32).to(dt)
-    k_new = torch.randn((total_steps, B, H, D), generator=gen, device=dev, dtype=torch.float32).to(dt)
-    v_new = torch.randn((total_steps, B, H, D), generator=gen, device=dev, dtype=torch.float32).to(dt)
-    out = torch.empty((B, H, D), dtype=dt, device=dev)
+    done = np.zeros(B, dtype=np.int64)
+    sharers = [int(s) for s in wl.sharers]
+    history = []  # slots of each reservation, in order
+    if sharers and wl.prefix_len:
+        s0 = sharers[0]
+        sl, _ = alloc.reserve_batch(tables[s0:s0 + 1], nblk[s0:s0 + 1], [0], [wl.prefix_len])
+        history.append(sl)
+        done[s0] = wl.prefix_len
+        for s in sharers[1:]:
+            row = alloc.fork(tables[s0, : nblk[s0]])
+            tables[s, : len(row)] = row
+            nblk[s] = len(row)
+            done[s] = wl.prefix_len
+    hist = np.maximum(lens0 - 1 - done, 0)
+    sl, pr = alloc.reserve_batch(tables, nblk, done, hist)
+    assert len(pr) == 0
+    history.append(sl)
+    cur = (done + hist).astype(np.int32)
+    slots_hist = torch.from_numpy(np.concatenate(history)).to(dev)
+    n_hist = slots_hist.numel()
+    k_caches, v_caches = [], []
+    gen = torch.Generator(device=dev)
+    for layer in range(NL):
+        kc = torch.empty((wl.num_blocks, bs, H, D), dtype=tdt, device=dev)
+        vc = torch.empty_like(kc)
+        gen.manual_seed(5000 + layer)
+        for a0 in range(0, n_hist, 1 << 16):   # history rows drawn on the device, in slices
+            a1 = min(n_hist, a0 + (1 << 16))
+            kr = torch.randn((a1 - a0, H, D), generator=gen, device=dev, dtype=torch.float32).to(tdt)
+            vr = torch.randn((a1 - a0, H, D), generator=gen, device=dev, dtype=torch.float32).to(tdt)
+            pkv.pkv_append(kr, vr, slots_hist[a0:a1], kc, vc)
+        k_caches.append(kc)
+        v_caches.append(vc)
+    del slots_hist
+    gen.manual_seed(7)
+    q_all = torch.randn((total_steps, NL, B, H, D), generator=gen, device=dev, dtype=torch.float32).to(tdt)
+    k_new = torch.randn((total_steps, NL, B, H, D), generator=gen, device=dev, dtype=torch.float32).to(tdt)
+    v_new = torch.randn((total_steps, NL, B, H, D), generator=gen, device=dev, dtype=torch.float32).to(tdt)
+    out = torch.empty((B, H, D), dtype=tdt, device=dev)
     wgs = args.work_groups or pkv.pkv_decode_work_groups()
-    workspace = pkv.decode_workspace(B, H, D, "f16", wgs, device=dev)
-    # device metadata (double-buffered) and pinned host staging (ring)
-    ring = 4
-    d_tables = [torch.empty((B, maxb), dtype=torch.int32, device=dev) for _ in range(2)]
-    d_lens = [torch.empty(B, dtype=torch.int32, device=dev) for _ in range(2)]
-    d_slots = [torch.empty(B, dtype=torch.int64, device=dev) for _ in range(2)]
+    workspace = pkv.decode_workspace(B, H, D, wl.dtype, wgs, device=dev)
+    # Step metadata travels in one packed buffer: slots (int64), lengths and
+    # block tables (int32).  Host side: a ring of pinned buffers so the host
+    # can prepare step i+1 while step i's copy is still queued.
+    off_lens = 8 * B
+    off_tab = off_lens + 4 * B
+    nbytes = off_tab + 4 * B * maxb
+    d_meta = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    d_slots = d_meta[:off_lens].view(torch.int64)
+    d_lens = d_meta[off_lens:off_tab].view(torch.int32)
+    d_tables = d_meta[off_tab:].view(torch.int32).view(B, maxb)
     d_pairs = torch.empty((B, 2), dtype=torch.int32, device=dev)
-    h_tables = [torch.empty((B, maxb), dtype=torch.int32, pin_memory=True) for _ in range(ring)]
-    h_lens = [torch.empty(B, dtype=torch.int32, pin_memory=True) for _ in range(ring)]
-    h_slots = [torch.empty(B, dtype=torch.int64, pin_memory=True) for _ in range(ring)]
+    ring = args.ring
+    h_meta = [torch.empty(nbytes, dtype=torch.uint8, pin_memory=True) for _ in range(ring)]
+    h_views = []
+    for hm in h_meta:
+        raw = hm.numpy()
+        h_views.append((raw[:off_lens].view(np.int64), raw[off_lens:off_tab].view(np.int32),
+                        raw[off_tab:].view(np.int32).reshape(B, maxb)))
     h_pairs = [torch.empty((B, 2), dtype=torch.int32, pin_memory=True) for _ in range(ring)]
     h_done = [None] * ring
     stream = torch.cuda.current_stream()
+    # Calls checked once; each step only swaps the per-step row pointers.
+    appends = [pkv.PreparedAppend(k_new[0, l], v_new[0, l], d_slots, k_caches[l], v_caches[l]) for l in range(NL)]
+    decodes = [pkv.PreparedDecode(out, q_all[0, l], k_caches[l], v_caches[l], d_tables, d_lens, max_len,
+                                  scale=wl.scale, work_groups=wgs, workspace=workspace) for l in range(NL)]
     torch.cuda.synchronize()
 
-    cur = hist.astype(np.int32).copy()
     ones = np.ones(B, dtype=np.int32)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(total_steps)]
-    kv_bytes = []
-    table_entries = []
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(NL)]
+          for _ in range(total_steps)]
+    copied = [torch.cuda.Event() for _ in range(ring)]
+    kv_bytes, table_entries, n_pairs = [], [], [0]
 
     def step(i):
-        r, d = i % ring, i % 2
-        if h_done[r] is not None:
-            h_done[r].synchronize()          # host buffer free again (its copy has run)
-        sl, pr = alloc.reserve_batch(tables, nblk, cur, ones)   # a1: host reservation
+        r = i % ring
+        if h_done[r] is not None:                                      # staging slot r free again:
+            while not h_done[r].query():                               # poll; a blocking wait sleeps and
+                pass                                                   # wakes up late
+        slots_v, lens_v, tab_v = h_views[r]
+        npairs = alloc.reserve_batch_into(tables, nblk, cur, ones, slots_v, h_pairs[r].numpy())  # 1. reserve
         cur[:] += 1
-        h_tables[r].numpy()[:] = tables
-        h_lens[r].numpy()[:] = cur
-        h_slots[r].numpy()[:] = sl
-        d_tables[d].copy_(h_tables[r], non_blocking=True)           # a2: stage metadata
-        d_lens[d].copy_(h_lens[r], non_blocking=True)
-        d_slots[d].copy_(h_slots[r], non_blocking=True)
-        if len(pr):                                                 # a3: copy-on-write
-            h_pairs[r].numpy()[: len(pr)] = pr
-            d_pairs[: len(pr)].copy_(h_pairs[r][: len(pr)], non_blocking=True)
-            pkv.pkv_copy_blocks([k_cache], [v_cache], d_pairs[: len(pr)])
-        e = torch.cuda.Event()
-        e.record(stream)
-        h_done[r] = e
-        pkv.pkv_append(k_new[i], v_new[i], d_slots[d], k_cache, v_cache)   # a4: scatter
-        ev[i][0].record(stream)
-        pkv.pkv_attention_decode(out, q_all[i], k_cache, v_cache, d_tables[d], d_lens[d], max_len,   # a5, a6
-                                 scale=wl.scale, work_groups=wgs, workspace=workspace)
-        ev[i][1].record(stream)
-        kv_bytes.append(int(cur.astype(np.int64).sum()) * 2 * H * D * esz)
+        lens_v[:] = cur
+        tab_v[:] = tables
+        d_meta.copy_(h_meta[r], non_blocking=True)                     # 2. stage metadata (one copy)
+        if npairs:                                                     # 3. copy-on-write
+            d_pairs[:npairs].copy_(h_pairs[r][:npairs], non_blocking=True)
+            pkv.pkv_copy_blocks(k_caches, v_caches, d_pairs[:npairs])
+            n_pairs[0] += npairs
+        copied[r].record(stream)
+        h_done[r] = copied[r]
+        for layer in range(NL):
+            appends[layer].launch(k_new[i, layer], v_new[i, layer])    # 4. scatter new rows
+            ev[i][layer][0].record(stream)
+            decodes[layer].launch(q_all[i, layer])                     # 5. decode attention
+            ev[i][layer][1].record(stream)
+        kv_bytes.append(int(cur.astype(np.int64).sum()) * 2 * H * D * esz * NL)
         table_entries.append(int(((cur.astype(np.int64) + bs - 1) // bs).sum()))
 
     for i in range(args.warmup):
@@ -177,29 +257,18 @@ def main():
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
-    lens_end = cur.copy()
-    attn_ms = [ev[i][0].elapsed_time(ev[i][1]) for i in range(args.warmup, total_steps)]
-    attn_avg_s = float(np.mean(attn_ms)) / 1e3
+    attn_s = float(np.mean([ev[i][layer][0].elapsed_time(ev[i][layer][1])
+                            for i in range(args.warmup, total_steps) for layer in range(NL)])) / 1e3
     kv_total = float(sum(kv_bytes))
     value = kv_total / elapsed / 1e9
-    # algorithmic bytes of one decode-attention launch (average over the timed steps):
-    # K+V rows + q in + out + block-table entries + lengths
-    mean_len_sum = float(np.mean(kv_bytes)) / (2 * H * D * esz)
-    algo = float(np.mean(kv_bytes)) + 2 * B * H * D * esz + 4 * float(np.mean(table_entries)) + 4 * B
-    achieved = algo / attn_avg_s / 1e9
+    # Algorithmic bytes of one decode-attention call (mean over timed steps, one
+    # layer): K+V rows read + q in + out + block-table entries + lengths.
+    kv_per_call = float(np.mean(kv_bytes)) / NL
+    algo = kv_per_call + 2 * B * H * D * esz + 4 * float(np.mean(table_entries)) + 4 * B
+    achieved = algo / attn_s / 1e9
+    traffic = recorded_traffic(args.workload)
 
     extra = {}
-    if args.attention_only:
-        # Back-to-back launches of the dominant kernel alone (profiling aid).
-        s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        s0.record(stream)
-        for _ in range(args.attention_only):
-            pkv.pkv_attention_decode(out, q_all[-1], k_cache, v_cache, d_tables[(total_steps - 1) % 2],
-                                     d_lens[(total_steps - 1) % 2], max_len, scale=wl.scale, work_groups=wgs,
-                                     workspace=workspace)
-        s1.record(stream)
-        torch.cuda.synchronize()
-        extra["attention_only_avg_us"] = round(s0.elapsed_time(s1) * 1e3 / args.attention_only, 2)
     if args.copy_calibration:
         a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         bcopy = torch.empty_like(a)
@@ -209,19 +278,21 @@ def main():
 
     cpu = None
     if not args.no_cpu:
-        k_cpu, v_cpu = None, None
+        # The oracle reads the logical rows of layer 0 that the GPU attended to
+        # in the last step, gathered from the pool by position.
+        def rows(b):
+            L = int(cur[b])
+            idx = np.arange(L)
+            blocks = tables[b, idx // bs].astype(np.int64)
+            flat = torch.from_numpy(blocks * bs + idx % bs).to(dev)
+            kk = k_caches[0].view(-1, H, D)[flat].cpu()
+            vv = v_caches[0].view(-1, H, D)[flat].cpu()
+            qq = q_all[total_steps - 1, 0, b].cpu()
+            if tdt == torch.bfloat16:
+                return tuple(x.view(torch.int16).numpy().view(np.uint16) for x in (qq, kk, vv))
+            return qq.numpy(), kk.numpy(), vv.numpy()
 
-        def rows(b, L):
-            # The same logical rows the GPU attends: history rows then this
-            # run's appended rows, all drawn by torch's generator above.
-            start = int(hist[:b].sum())
-            kh = k_hist[start: start + int(hist[b])]
-            vh = v_hist[start: start + int(hist[b])]
-            kk = torch.cat([kh, k_new[:total_steps, b]], 0)[:L].cpu().numpy()
-            vv = torch.cat([vh, v_new[:total_steps, b]], 0)[:L].cpu().numpy()
-            return q_all[total_steps - 1, b].cpu().numpy(), kk, vv
-
-        cpu = cpu_baseline(wl, lens_end, rows, args.cpu_seconds)
+        cpu = cpu_baseline(wl, rows, args.cpu_seconds)
 
     ms_per_step = elapsed / args.steps * 1e3
     rec = {
@@ -235,17 +306,17 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16",
-        "data": "synthetic (seeded; K/V/Q ~ N(0,1) in fp16)",
-        "config": {"workload": wl.title, "batch": B, "heads": H, "head_dim": D, "block_size": bs,
+        "dtype": wl.dtype,
+        "data": "synthetic (seeded; Q/K/V ~ N(0,1) cast to the storage dtype)",
+        "config": {"workload": wl.title, "layers": NL, "batch": B, "heads": H, "head_dim": D, "block_size": bs,
                    "pool_blocks": wl.num_blocks, "work_groups": wgs,
-                   "mean_seq_len": round(mean_len_sum / B, 1)},
+                   "mean_seq_len": round(kv_per_call / (2 * H * D * esz) / B, 1), "cow_pairs": n_pairs[0]},
         "hbm_peak_frac": round(value / HBM_PEAK_GBS, 4),
         "token_steps_per_s": round(B * args.steps / elapsed, 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "pkv_attention_decode", "avg_launch_us": round(attn_avg_s * 1e6, 2),
-                     "algorithmic_bytes_per_launch": int(algo)},
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "kernel": "pkv_attention_decode (decode_kernel + decode_merge_kernel)",
+                     "avg_call_us": round(attn_s * 1e6, 2), "algorithmic_bytes_per_call": int(algo)},
         "cpu_baseline": cpu,
     }
     rec.update(extra)

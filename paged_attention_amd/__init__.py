@@ -57,7 +57,7 @@ def _load():
         raise ImportError(f"{LIB_PATH} is missing: build it with `python paged_attention_amd/build.py`")
     lib = ctypes.CDLL(LIB_PATH)
     i32, i64, vp, sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t
-    p32, p64 = ctypes.POINTER(i32), ctypes.POINTER(i64)
+    p32 = p64 = vp  # host arrays are passed as raw addresses
     sig = {
         "pkv_strerror": (ctypes.c_char_p, [ctypes.c_int]),
         "pkv_last_error": (ctypes.c_char_p, []),
@@ -108,12 +108,13 @@ def version() -> int:
     return _lib.pkv_version()
 
 
-def _i32p(arr: np.ndarray):
-    return arr.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+def _ptr(arr: np.ndarray):
+    # The array interface is far cheaper than numpy's .ctypes attribute.
+    return ctypes.c_void_p(arr.__array_interface__["data"][0])
 
 
-def _i64p(arr: np.ndarray):
-    return arr.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
+_i32p = _ptr
+_i64p = _ptr
 
 
 class BlockAllocator:
@@ -216,6 +217,17 @@ class BlockAllocator:
                                           ctypes.byref(ncow)))
         return slots[: int(new.sum())], pairs[: ncow.value]
 
+    def reserve_batch_into(self, tables: np.ndarray, n_blocks: np.ndarray, cur_lens: np.ndarray, n_new: np.ndarray,
+                           slots_out: np.ndarray, pairs_out: np.ndarray) -> int:
+        """As :meth:`reserve_batch`, writing into caller arrays (e.g. pinned staging
+        memory); every array must already be C-contiguous of the right dtype
+        (int32, slots int64).  Returns the number of copy pairs written."""
+        ncow = ctypes.c_int32(0)
+        _check(_lib.pkv_seq_reserve_batch(self._h, _i32p(tables), tables.shape[1], _i32p(n_blocks), _i32p(cur_lens),
+                                          _i32p(n_new), tables.shape[0], _i64p(slots_out), _i32p(pairs_out),
+                                          pairs_out.shape[0], ctypes.byref(ncow)))
+        return ncow.value
+
     def release_table_row(self, tables: np.ndarray, i: int, n_blocks: int) -> None:
         row = np.ascontiguousarray(tables[i, :n_blocks])
         self.release(row)
@@ -257,8 +269,7 @@ def _stream(stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
-def pkv_append(k_new, v_new, slot_mapping, k_cache, v_cache, stream=None) -> None:
-    """Scatter rows ``k_new[t]``/``v_new[t]`` ([T][H][D]) to flat slot ``slot_mapping[t]``."""
+def _append_args(k_new, v_new, slot_mapping, k_cache, v_cache, stream):
     torch = _torch()
     nb, bs, h, d = k_cache.shape
     if k_new.shape[1:] != (h, d) or v_new.shape != k_new.shape or v_cache.shape != k_cache.shape:
@@ -267,9 +278,14 @@ def pkv_append(k_new, v_new, slot_mapping, k_cache, v_cache, stream=None) -> Non
         raise InvalidArgument(PKV_ERR_INVALID, "append: dtype mismatch")
     if slot_mapping.shape != (k_new.shape[0],):
         raise InvalidArgument(PKV_ERR_INVALID, "append: slot_mapping must be [T]")
-    _check(_lib.pkv_append(_dev(k_new, "k_new"), _dev(v_new, "v_new"), k_new.shape[0],
-                           _dev(slot_mapping, "slot_mapping", torch.int64), _dev(k_cache, "k_cache", ndim=4),
-                           _dev(v_cache, "v_cache", ndim=4), nb, bs, h, d, _dtype_code(k_cache), _stream(stream)))
+    return [_dev(k_new, "k_new"), _dev(v_new, "v_new"), k_new.shape[0], _dev(slot_mapping, "slot_mapping", torch.int64),
+            _dev(k_cache, "k_cache", ndim=4), _dev(v_cache, "v_cache", ndim=4), nb, bs, h, d, _dtype_code(k_cache),
+            _stream(stream)]
+
+
+def pkv_append(k_new, v_new, slot_mapping, k_cache, v_cache, stream=None) -> None:
+    """Scatter rows ``k_new[t]``/``v_new[t]`` ([T][H][D]) to flat slot ``slot_mapping[t]``."""
+    _check(_lib.pkv_append(*_append_args(k_new, v_new, slot_mapping, k_cache, v_cache, stream)))
 
 
 def pkv_copy_blocks(k_caches, v_caches, pairs, stream=None) -> None:
@@ -313,9 +329,8 @@ def decode_workspace(batch, num_heads, head_dim, dtype, work_groups=0, device="c
     return torch.empty(need, dtype=torch.uint8, device=device)
 
 
-def pkv_attention_decode(out, q, k_cache, v_cache, block_tables, seq_lens, max_seq_len, scale=None,
-                         work_groups=0, workspace=None, stream=None) -> None:
-    """Decode attention of ``q`` ([B][H][D]) over each sequence's paged K/V; writes ``out``."""
+def _decode_args(out, q, k_cache, v_cache, block_tables, seq_lens, max_seq_len, scale, work_groups, workspace,
+                 stream):
     torch = _torch()
     nb, bs, h, d = k_cache.shape
     batch = q.shape[0]
@@ -328,20 +343,73 @@ def pkv_attention_decode(out, q, k_cache, v_cache, block_tables, seq_lens, max_s
     code = _dtype_code(q)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    if batch == 0:
-        return
     if workspace is None:
-        workspace = decode_workspace(batch, h, d, _DT_NAMES[code], work_groups, q.device)
-    _check(_lib.pkv_attention_decode(
-        _dev(out, "out"), _dev(q, "q"), _dev(k_cache, "k_cache", ndim=4), _dev(v_cache, "v_cache", ndim=4),
-        _dev(block_tables, "block_tables", torch.int32), block_tables.shape[1],
-        _dev(seq_lens, "seq_lens", torch.int32), int(max_seq_len), batch, h, d, bs, nb, float(scale), code,
-        int(work_groups), _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
-        _stream(stream)))
+        workspace = decode_workspace(max(batch, 1), h, d, _DT_NAMES[code], work_groups, q.device)
+    args = [_dev(out, "out"), _dev(q, "q"), _dev(k_cache, "k_cache", ndim=4), _dev(v_cache, "v_cache", ndim=4),
+            _dev(block_tables, "block_tables", torch.int32), block_tables.shape[1],
+            _dev(seq_lens, "seq_lens", torch.int32), int(max_seq_len), batch, h, d, bs, nb, float(scale), code,
+            int(work_groups), _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+            _stream(stream)]
+    return args, workspace
+
+
+def pkv_attention_decode(out, q, k_cache, v_cache, block_tables, seq_lens, max_seq_len, scale=None,
+                         work_groups=0, workspace=None, stream=None) -> None:
+    """Decode attention of ``q`` ([B][H][D]) over each sequence's paged K/V; writes ``out``."""
+    if q.shape[0] == 0:
+        return
+    args, _ = _decode_args(out, q, k_cache, v_cache, block_tables, seq_lens, max_seq_len, scale, work_groups,
+                           workspace, stream)
+    _check(_lib.pkv_attention_decode(*args))
+
+
+class PreparedDecode:
+    """A pkv_attention_decode call whose arguments are checked once.
+
+    ``launch(q, out)`` only swaps the query/output pointers (tensors of the
+    same shape and dtype as at preparation) and enqueues the kernels; it is
+    meant for decode loops where Python overhead would otherwise dominate.
+    The tensors given at preparation must stay alive and in place.
+    """
+
+    def __init__(self, out, q, k_cache, v_cache, block_tables, seq_lens, max_seq_len, scale=None, work_groups=0,
+                 workspace=None, stream=None):
+        self._args, ws = _decode_args(out, q, k_cache, v_cache, block_tables, seq_lens, max_seq_len, scale,
+                                      work_groups, workspace, stream)
+        self._keep = (k_cache, v_cache, block_tables, seq_lens, ws)
+        self._shape, self._dtype = tuple(q.shape), q.dtype
+
+    def _swap(self, i, t, what):
+        if tuple(t.shape) != self._shape or t.dtype != self._dtype or not t.is_contiguous() or not t.is_cuda:
+            raise InvalidArgument(PKV_ERR_INVALID, f"prepared call: {what} differs from the prepared tensor")
+        self._args[i] = ctypes.c_void_p(t.data_ptr())
+
+    def launch(self, q=None, out=None) -> None:
+        if q is not None:
+            self._swap(1, q, "q")
+        if out is not None:
+            self._swap(0, out, "out")
+        _check(_lib.pkv_attention_decode(*self._args))
+
+
+class PreparedAppend(PreparedDecode):
+    """A pkv_append call checked once; ``launch(k_new, v_new)`` swaps the new rows."""
+
+    def __init__(self, k_new, v_new, slot_mapping, k_cache, v_cache, stream=None):  # noqa: D107
+        self._args = _append_args(k_new, v_new, slot_mapping, k_cache, v_cache, stream)
+        self._keep = (slot_mapping, k_cache, v_cache)
+        self._shape, self._dtype = tuple(k_new.shape), k_new.dtype
+
+    def launch(self, k_new=None, v_new=None) -> None:
+        if k_new is not None:
+            self._swap(0, k_new, "k_new")
+        if v_new is not None:
+            self._swap(1, v_new, "v_new")
+        _check(_lib.pkv_append(*self._args))
 
 
 __all__ = [
     "BlockAllocator", "PkvError", "OutOfBlocks", "InvalidArgument", "pkv_append", "pkv_copy_blocks",
     "pkv_attention_decode", "pkv_decode_workspace_bytes", "pkv_decode_work_groups",
-    "decode_workspace", "version", "LIB_PATH",
+    "decode_workspace", "PreparedDecode", "PreparedAppend", "version", "LIB_PATH",
 ]

@@ -44,32 +44,28 @@ namespace {
 
 int32_t ceil_div(int64_t a, int64_t b) { return static_cast<int32_t>((a + b - 1) / b); }
 
-// Checks that every id of a row is in range and that each block has at least
-// as many references as the row holds it (so a release cannot underflow).
-int check_row(const pkv_allocator* a, const int32_t* row, int32_t n, const char* what) {
+// Checks that every id of a row is in range and referenced.  With
+// `count_duplicates`, also that each block has at least as many references as
+// the row holds it, so releasing the row cannot underflow a count (rows made
+// by the allocator never repeat an id; only release and fork need the check).
+int check_row(const pkv_allocator* a, const int32_t* row, int32_t n, const char* what, bool count_duplicates) {
   if (n < 0) return pkv::fail(PKV_ERR_INVALID, "%s: negative block count %d", what, n);
   if (n > 0 && row == nullptr) return pkv::fail(PKV_ERR_INVALID, "%s: null row", what);
-  bool dup = false;
   for (int32_t j = 0; j < n; ++j) {
     const int32_t b = row[j];
     if (!a->in_range(b)) return pkv::fail(PKV_ERR_BAD_BLOCK, "%s: block %d out of range [0,%d)", what, b, a->num_blocks);
     if (a->ref[b] < 1) return pkv::fail(PKV_ERR_REFCOUNT, "%s: block %d is free", what, b);
   }
-  // Rows produced by the allocator never repeat an id; tolerate it anyway if
-  // the count covers every occurrence.
+  if (!count_duplicates || n < 2) return PKV_OK;
   std::vector<int32_t> sorted(row, row + n);
   std::sort(sorted.begin(), sorted.end());
-  for (int32_t j = 1; j < n; ++j) dup |= sorted[j] == sorted[j - 1];
-  if (dup) {
-    int32_t j = 0;
-    while (j < n) {
-      int32_t k = j;
-      while (k < n && sorted[k] == sorted[j]) ++k;
-      if (a->ref[sorted[j]] < k - j)
-        return pkv::fail(PKV_ERR_REFCOUNT, "%s: block %d held %d times with count %d", what, sorted[j], k - j,
-                         a->ref[sorted[j]]);
-      j = k;
-    }
+  for (int32_t j = 0; j < n;) {
+    int32_t k = j;
+    while (k < n && sorted[k] == sorted[j]) ++k;
+    if (a->ref[sorted[j]] < k - j)
+      return pkv::fail(PKV_ERR_REFCOUNT, "%s: block %d held %d times with count %d", what, sorted[j], k - j,
+                       a->ref[sorted[j]]);
+    j = k;
   }
   return PKV_OK;
 }
@@ -91,7 +87,7 @@ int plan_reserve(const pkv_allocator* a, const int32_t* row, int32_t row_capacit
   if (n_blocks != ceil_div(cur_len, bs))
     return pkv::fail(PKV_ERR_INVALID, "reserve: row holds %d blocks but cur_len %d needs %d", n_blocks, cur_len,
                      ceil_div(cur_len, bs));
-  int st = check_row(a, row, n_blocks, "reserve");
+  int st = check_row(a, row, n_blocks, "reserve", false);
   if (st != PKV_OK) return st;
   const int64_t end = static_cast<int64_t>(cur_len) + n_new;
   if (end > INT32_MAX) return pkv::fail(PKV_ERR_INVALID, "reserve: length overflow");
@@ -221,7 +217,7 @@ PKV_API int pkv_free_list(const pkv_allocator* a, int32_t* out, int32_t capacity
 
 PKV_API int pkv_seq_fork(pkv_allocator* a, const int32_t* src_row, int32_t n_blocks, int32_t* dst_row) {
   if (a == nullptr || (n_blocks > 0 && dst_row == nullptr)) return pkv::fail(PKV_ERR_INVALID, "seq_fork: null argument");
-  int st = check_row(a, src_row, n_blocks, "seq_fork");
+  int st = check_row(a, src_row, n_blocks, "seq_fork", true);
   if (st != PKV_OK) return st;
   for (int32_t j = 0; j < n_blocks; ++j) {
     ++a->ref[src_row[j]];
@@ -290,7 +286,7 @@ PKV_API int pkv_seq_reserve_batch(pkv_allocator* a, int32_t* tables, int32_t row
 
 PKV_API int pkv_seq_release(pkv_allocator* a, const int32_t* row, int32_t n_blocks) {
   if (a == nullptr) return pkv::fail(PKV_ERR_INVALID, "seq_release: null allocator");
-  int st = check_row(a, row, n_blocks, "seq_release");
+  int st = check_row(a, row, n_blocks, "seq_release", true);
   if (st != PKV_OK) return st;
   for (int32_t j = 0; j < n_blocks; ++j)
     if (--a->ref[row[j]] == 0) a->push(row[j]);

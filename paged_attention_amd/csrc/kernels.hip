@@ -458,13 +458,19 @@ __global__ void __launch_bounds__(kMaxWaves * 64) decode_kernel(DecodeArgs a) {
 
 // Merges the pieces of every cut sequence:
 //   M = max_i m_i,  S = sum_i l_i 2^(m_i - M),  out = sum_i acc_i 2^(m_i - M) / S.
-// One wavefront per (sequence, head).  Lanes split into groups of D/4 lanes,
-// each group reading whole piece rows as float4 and taking every
-// (64 / (D/4))-th piece; every load is independent of the others.
+// One wavefront per (sequence, head).  Lane i holds piece i's (m, l); the
+// lanes also split into groups of D/4 lanes that hold whole piece rows as
+// float4, kMergeRows rows per group.  Every load of a batch of pieces is
+// issued before any of them is used, so a batch costs one memory round trip;
+// the weights reach the row holders by lane shuffles.
+constexpr int kMergeRows = 8;
+
 template <int DT, int D>
 __global__ void __launch_bounds__(kMergeWaves * 64) decode_merge_kernel(DecodeArgs a) {
   constexpr int LPR = D / 4;     // lanes per piece row (float4 each)
   constexpr int RPW = 64 / LPR;  // rows per wavefront instruction
+  constexpr int BATCH = RPW * kMergeRows;
+  static_assert(BATCH <= 64, "a batch of pieces must fit one (m, l) per lane");
   const int v = blockIdx.y;
   const int first = a.ws_plan[2 * v];
   const int count = a.ws_plan[2 * v + 1];
@@ -476,28 +482,44 @@ __global__ void __launch_bounds__(kMergeWaves * 64) decode_merge_kernel(DecodeAr
   const int h = slice_lo + __builtin_amdgcn_readfirstlane(blockIdx.x * kMergeWaves + (threadIdx.x >> 6));
   if (h >= slice_hi) return;
   const int lane = threadIdx.x & 63;
-  const float2* ml = a.ws_ml + static_cast<int64_t>(first) * a.num_heads + h;  // stride num_heads
-  float mx = -INFINITY;
-  for (int i = lane; i < count; i += 64) mx = fmaxf(mx, ml[static_cast<int64_t>(i) * a.num_heads].x);
-  mx = wave_max(mx);
-  float sum = 0.f;
-  for (int i = lane; i < count; i += 64) {
-    const float2 m_l = ml[static_cast<int64_t>(i) * a.num_heads];
-    sum = fmaf(m_l.y, __builtin_amdgcn_exp2f(m_l.x - mx), sum);
-  }
-  sum = wave_sum(sum);
   const int grp = lane / LPR;
   const int sub = lane % LPR;
+  const float2* ml = a.ws_ml + static_cast<int64_t>(first) * a.num_heads + h;  // stride num_heads
   const float* accp = a.ws_acc + (static_cast<int64_t>(first) * a.num_heads + h) * D + sub * 4;
+  const int64_t row_stride = static_cast<int64_t>(a.num_heads) * D;
+
+  float mx = -INFINITY;   // running max over batches (wave-uniform)
+  float sum = 0.f;        // running sum, scaled to mx
   float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll 8
-  for (int i = grp; i < count; i += RPW) {
-    const float w = __builtin_amdgcn_exp2f(ml[static_cast<int64_t>(i) * a.num_heads].x - mx);
-    const float4 x = *reinterpret_cast<const float4*>(accp + static_cast<int64_t>(i) * a.num_heads * D);
-    o.x = fmaf(x.x, w, o.x);
-    o.y = fmaf(x.y, w, o.y);
-    o.z = fmaf(x.z, w, o.z);
-    o.w = fmaf(x.w, w, o.w);
+  for (int i0 = 0; i0 < count; i0 += BATCH) {
+    const int n = min(BATCH, count - i0);
+    // issue every load of the batch first
+    const float2 mine = lane < n ? ml[static_cast<int64_t>(i0 + lane) * a.num_heads] : make_float2(-INFINITY, 0.f);
+    float4 rows[kMergeRows];
+#pragma unroll
+    for (int k = 0; k < kMergeRows; ++k) {
+      const int i = grp + k * RPW;
+      rows[k] = i < n ? *reinterpret_cast<const float4*>(accp + static_cast<int64_t>(i0 + i) * row_stride)
+                      : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    const float bmx = wave_max(mine.x);
+    const float nmx = fmaxf(mx, bmx);
+    const float rescale = __builtin_amdgcn_exp2f(mx - nmx);  // 0 on the first batch
+    const float w = lane < n ? __builtin_amdgcn_exp2f(mine.x - nmx) : 0.f;
+    sum = sum * rescale + wave_sum(mine.y * w);
+    o.x *= rescale;
+    o.y *= rescale;
+    o.z *= rescale;
+    o.w *= rescale;
+#pragma unroll
+    for (int k = 0; k < kMergeRows; ++k) {
+      const float wk = __shfl(w, grp + k * RPW, 64);
+      o.x = fmaf(rows[k].x, wk, o.x);
+      o.y = fmaf(rows[k].y, wk, o.y);
+      o.z = fmaf(rows[k].z, wk, o.z);
+      o.w = fmaf(rows[k].w, wk, o.w);
+    }
+    mx = nmx;
   }
 #pragma unroll
   for (int off = LPR; off < 64; off <<= 1) {

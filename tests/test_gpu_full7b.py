@@ -1,0 +1,141 @@
+"""Full 7B decode step at its real size: 32 layers, batch 256, pool = 85 % of
+free HBM, 30 % of sequences sharing a 256-token prefix.
+
+The oracle cannot hold this step (about 68 GB of K/V), so the test checks:
+  * allocator indexing at full size, bit-exact against the oracle allocator;
+  * the scattered pool, bit-exact, for sampled sequences of sampled layers;
+  * decode attention for every head of 16 sampled sequences on layers 0 and
+    31, and of 8 more sequences on every layer, against the oracle computed
+    one sequence at a time.
+K/V rows are drawn on the device by torch's generator (seeded 5000 + layer,
+in reservation order); the oracle re-draws the same rows from the same seed
+and gathers each sequence's logical rows by position, never from the pool.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import paged_attention_amd as pkv
+import workloads
+from oracle import allocator as oalloc
+from oracle import attention as oatt
+
+pytestmark = pytest.mark.gpu
+
+LAYERS, H, D, BS = 32, 32, 128, 16
+
+
+def _draw(layer, n, dev):
+    g = torch.Generator(device=dev).manual_seed(5000 + layer)
+    k = torch.randn((n, H, D), generator=g, device=dev, dtype=torch.float32).half()
+    v = torch.randn((n, H, D), generator=g, device=dev, dtype=torch.float32).half()
+    return k, v
+
+
+@pytest.mark.skipif(not torch.cuda.is_available(), reason="no GPU")
+def test_full7b_step_sampled():
+    dev = torch.device("cuda:0")
+    torch.cuda.empty_cache()
+    free, _ = torch.cuda.mem_get_info()
+    per_block = LAYERS * 2 * BS * H * D * 2
+    # 85 % of free memory for the pools, less room for one layer's drawn rows
+    # (about 2 GB) that the test keeps beside them.
+    num_blocks = int(0.85 * free - 4e9) // per_block
+    wl = workloads.full7b_step(num_blocks)
+    B = wl.batch
+    lens = wl.seq_lens.astype(np.int64)
+    sharers = [int(s) for s in wl.sharers]
+    shared = set(sharers)
+    pre = wl.prefix_len
+    print(f"full 7B step: pool {num_blocks} blocks ({num_blocks * per_block / 1e9:.1f} GB), "
+          f"{len(sharers)} sharers, sum len {int(lens.sum())}", flush=True)
+
+    # --- allocation, product and oracle, same operations --------------------
+    maxb = -(-int(lens.max()) // BS) + 1
+    alloc = pkv.BlockAllocator(num_blocks, BS, wl.free_order)
+    oa = oalloc.OracleAllocator(num_blocks, BS, wl.free_order)
+    tables = np.zeros((B, maxb), dtype=np.int32)
+    nblk = np.zeros(B, dtype=np.int32)
+    orows = [[] for _ in range(B)]
+    s0 = sharers[0]
+    sl_pre, _ = alloc.reserve_batch(tables[s0:s0 + 1], nblk[s0:s0 + 1], [0], [pre])
+    ol_pre, _ = oa.reserve(orows[s0], 0, pre)
+    assert sl_pre.tolist() == ol_pre
+    done = np.zeros(B, dtype=np.int64)
+    done[s0] = pre
+    for s in sharers[1:]:
+        row = alloc.fork(tables[s0, : nblk[s0]])
+        tables[s, : len(row)] = row
+        nblk[s] = len(row)
+        orows[s] = oa.fork(orows[s0], len(orows[s0]))
+        done[s] = pre
+    hist = lens - 1 - done
+    sl_hist, pairs = alloc.reserve_batch(tables, nblk, done, hist)
+    ol_hist, opairs = oa.reserve_batch(orows, done, hist)
+    assert sl_hist.tolist() == ol_hist and len(pairs) == 0 and not opairs   # prefix is whole blocks: no copy
+    sl_dec, pairs = alloc.reserve_batch(tables, nblk, done + hist, np.ones(B, dtype=np.int64))
+    ol_dec, opairs = oa.reserve_batch(orows, done + hist, [1] * B)
+    assert sl_dec.tolist() == ol_dec and len(pairs) == 0
+    for b in range(B):
+        assert tables[b, : nblk[b]].tolist() == orows[b]
+
+    # Logical row ranges in draw order: the prefix (once), then each
+    # sequence's private history, then one decode row per sequence.
+    n_hist = pre + int(hist.sum())
+    priv_start = pre + np.concatenate([[0], np.cumsum(hist)[:-1]])
+
+    def logical_rows(b, k_all, v_all, k_dec, v_dec):
+        idx = list(range(priv_start[b], priv_start[b] + int(hist[b])))
+        if b in shared:
+            idx = list(range(pre)) + idx
+        idx_t = torch.tensor(idx, dtype=torch.int64, device=dev)
+        kk = torch.cat([k_all[idx_t], k_dec[b: b + 1]])
+        vv = torch.cat([v_all[idx_t], v_dec[b: b + 1]])
+        return kk, vv
+
+    # --- build every layer through the product path -------------------------
+    slots_all = torch.from_numpy(np.concatenate([sl_pre, sl_hist])).to(dev)
+    slots_dec = torch.from_numpy(sl_dec).to(dev)
+    d_tables = torch.from_numpy(tables).to(dev)
+    d_lens = torch.from_numpy(lens.astype(np.int32)).to(dev)
+    q = torch.randn((LAYERS, B, H, D), generator=torch.Generator(device=dev).manual_seed(6000), device=dev).half()
+    dec_gen = torch.Generator(device=dev).manual_seed(7000)
+    k_dec = torch.randn((LAYERS, B, H, D), generator=dec_gen, device=dev).half()
+    v_dec = torch.randn((LAYERS, B, H, D), generator=dec_gen, device=dev).half()
+    outs = torch.empty((LAYERS, B, H, D), dtype=torch.float16, device=dev)
+    ws = pkv.decode_workspace(B, H, D, "f16", device=dev)
+    rng = np.random.default_rng(55)
+    check_layers = {0: rng.choice(B, 16, replace=False).tolist(), 31: rng.choice(B, 16, replace=False).tolist()}
+    every_layer = rng.choice(B, 8, replace=False).tolist()
+    pools_checked = 0
+    # Every layer's pool stays resident, as in serving (85 % of free HBM in all).
+    k_caches = [torch.empty((num_blocks, BS, H, D), dtype=torch.float16, device=dev) for _ in range(LAYERS)]
+    v_caches = [torch.empty_like(k_caches[0]) for _ in range(LAYERS)]
+    for layer in range(LAYERS):
+        kc, vc = k_caches[layer], v_caches[layer]
+        k_all, v_all = _draw(layer, n_hist, dev)
+        pkv.pkv_append(k_all, v_all, slots_all, kc, vc)
+        pkv.pkv_append(k_dec[layer], v_dec[layer], slots_dec, kc, vc)
+        pkv.pkv_attention_decode(outs[layer], q[layer], kc, vc, d_tables, d_lens, int(lens.max()), workspace=ws)
+        torch.cuda.synchronize()
+        sample = sorted(set(check_layers.get(layer, [])) | set(every_layer))
+        for b in sample:
+            kk, vv = logical_rows(b, k_all, v_all, k_dec[layer], v_dec[layer])
+            if layer in check_layers and pools_checked < 8:
+                # the pool, read through the table, holds exactly these rows
+                t = torch.arange(int(lens[b]), device=dev)
+                flat = d_tables[b, t // BS].long() * BS + t % BS
+                assert torch.equal(kc.view(-1, H, D)[flat].view(torch.int16), kk.view(torch.int16))
+                assert torch.equal(vc.view(-1, H, D)[flat].view(torch.int16), vv.view(torch.int16))
+                pools_checked += 1
+            ref = oatt.contiguous_attention(q[layer, b: b + 1].cpu().numpy(), [kk.cpu().numpy()],
+                                            [vv.cpu().numpy()], "f16")
+            got = outs[layer, b].float().cpu().numpy().astype(np.float64)
+            err = np.max(np.abs(got - ref[0]))
+            assert err <= 2e-3, (layer, b, err)
+        del k_all, v_all
+        if layer % 8 == 0:
+            print(f"layer {layer} checked ({len(sample)} sequences)", flush=True)
+    del k_caches, v_caches
+    torch.cuda.empty_cache()
