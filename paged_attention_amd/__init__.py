@@ -55,6 +55,12 @@ class InvalidArgument(PkvError, ValueError):
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with `python paged_attention_amd/build.py`")
+    # torch opens its own HIP runtime by path.  Loading it first lets the
+    # library's libamdhip64.so.7 dependency resolve to that same runtime;
+    # otherwise the process holds two runtimes and torch's streams and
+    # device state are unknown to the library's.
+    import torch  # noqa: F401
+
     lib = ctypes.CDLL(LIB_PATH)
     i32, i64, vp, sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t
     p32 = p64 = vp  # host arrays are passed as raw addresses
@@ -325,7 +331,8 @@ def decode_workspace(batch, num_heads, head_dim, dtype, work_groups=0, device="c
     torch = _torch()
     need = pkv_decode_workspace_bytes(batch, num_heads, head_dim, dtype, work_groups)
     if need == 0:
-        raise InvalidArgument(PKV_ERR_INVALID, "decode_workspace: unsupported sizes")
+        detail = _lib.pkv_last_error().decode()
+        raise InvalidArgument(PKV_ERR_INVALID, f"decode_workspace: unsupported sizes ({detail})")
     return torch.empty(need, dtype=torch.uint8, device=device)
 
 

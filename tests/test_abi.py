@@ -94,3 +94,17 @@ def test_workspace_queries():
     assert big == up(8190 * 8) + up(2 * 8 * 4 * 64 * 4) + up(2 * 8 * 4 * 8)
     assert pkv.pkv_decode_workspace_bytes(b, h, 96, "f16", wg) == 0
     assert pkv.pkv_decode_workspace_bytes(b, h, d, "f16", -1) == 0
+
+
+def test_one_hip_runtime_per_process():
+    # Importing the binding first must not load a second HIP runtime beside
+    # the one torch brings: the library has to share torch's streams.
+    code = (
+        "import sys; sys.path.insert(0, %r)\n"
+        "import paged_attention_amd\n"
+        "import torch\n"
+        "paths = {l.split()[-1] for l in open('/proc/self/maps') if 'libamdhip64' in l}\n"
+        "print(len(paths), sorted(paths))\n"
+    ) % ROOT
+    out = subprocess.run(["python", "-c", code], capture_output=True, text=True, check=True).stdout
+    assert out.startswith("1 "), out
