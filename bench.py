@@ -2,8 +2,9 @@
 
 One step = the whole decode path for one batch:
   1. host block reservation for every sequence's new token (C++ allocator),
-  2. staging of slots, block tables and lengths to the device (pinned memory,
-     asynchronous copies on the compute stream),
+  2. hand-over of slots, block tables and lengths: the kernels read them in
+     place from pinned host memory, with no copy on the queue (``--metadata
+     device`` stages them with one asynchronous copy per step instead),
   3. copy-on-write block copies (pkv_copy_blocks) when a reservation produced any,
   4. scatter of the new K/V rows (pkv_append), and
   5. decode attention over the paged cache (pkv_attention_decode),
@@ -57,6 +58,8 @@ def parse():
     p.add_argument("--block-size", type=int, default=16, help="block size of the long13b workload")
     p.add_argument("--work-groups", type=int, default=0, help="decode work-groups (0 = library choice)")
     p.add_argument("--ring", type=int, default=4, help="host staging buffers (how many steps the host may run ahead)")
+    p.add_argument("--metadata", choices=["pinned", "device"], default="pinned",
+                   help="where kernels read step metadata: pinned host memory in place, or a device copy")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target length of the oracle timing sample")
     p.add_argument("--no-cpu", action="store_true", help="skip the cpu_baseline leg")
     p.add_argument("--copy-calibration", action="store_true",
@@ -188,17 +191,18 @@ def main():
     out = torch.empty((B, H, D), dtype=tdt, device=dev)
     wgs = args.work_groups or pkv.pkv_decode_work_groups()
     workspace = pkv.decode_workspace(B, H, D, wl.dtype, wgs, device=dev)
-    # Step metadata travels in one packed buffer: slots (int64), lengths and
-    # block tables (int32).  Host side: a ring of pinned buffers so the host
-    # can prepare step i+1 while step i's copy is still queued.
+    # Step metadata is one packed buffer: slots (int64), lengths and block
+    # tables (int32).  Host side: a ring of pinned buffers, so the host can
+    # prepare step i+1 while step i's kernels still read (or copy) slot i.
     off_lens = 8 * B
     off_tab = off_lens + 4 * B
     nbytes = off_tab + 4 * B * maxb
-    d_meta = torch.empty(nbytes, dtype=torch.uint8, device=dev)
-    d_slots = d_meta[:off_lens].view(torch.int64)
-    d_lens = d_meta[off_lens:off_tab].view(torch.int32)
-    d_tables = d_meta[off_tab:].view(torch.int32).view(B, maxb)
-    d_pairs = torch.empty((B, 2), dtype=torch.int32, device=dev)
+    mode = args.metadata
+
+    def split(buf):
+        return (buf[:off_lens].view(torch.int64), buf[off_lens:off_tab].view(torch.int32),
+                buf[off_tab:].view(torch.int32).view(B, maxb))
+
     ring = args.ring
     h_meta = [torch.empty(nbytes, dtype=torch.uint8, pin_memory=True) for _ in range(ring)]
     h_views = []
@@ -207,23 +211,38 @@ def main():
         h_views.append((raw[:off_lens].view(np.int64), raw[off_lens:off_tab].view(np.int32),
                         raw[off_tab:].view(np.int32).reshape(B, maxb)))
     h_pairs = [torch.empty((B, 2), dtype=torch.int32, pin_memory=True) for _ in range(ring)]
+    d_pairs = torch.empty((B, 2), dtype=torch.int32, device=dev)
     h_done = [None] * ring
     stream = torch.cuda.current_stream()
-    # Calls checked once; each step only swaps the per-step row pointers.
-    appends = [pkv.PreparedAppend(k_new[0, l], v_new[0, l], d_slots, k_caches[l], v_caches[l]) for l in range(NL)]
-    decodes = [pkv.PreparedDecode(out, q_all[0, l], k_caches[l], v_caches[l], d_tables, d_lens, max_len,
-                                  scale=wl.scale, work_groups=wgs, workspace=workspace) for l in range(NL)]
+    # Calls checked once; each step only swaps the per-step row pointers.  In
+    # pinned mode every ring slot has its own set of calls pointing into it.
+    if mode == "device":
+        d_meta = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        metas = [split(d_meta)] * ring
+    else:
+        d_meta = None
+        metas = [split(hm) for hm in h_meta]
+    per_slot = {}
+    for r in range(ring):
+        key = metas[r][0].data_ptr()
+        if key not in per_slot:
+            sl_t, ln_t, tb_t = metas[r]
+            per_slot[key] = (
+                [pkv.PreparedAppend(k_new[0, l], v_new[0, l], sl_t, k_caches[l], v_caches[l]) for l in range(NL)],
+                [pkv.PreparedDecode(out, q_all[0, l], k_caches[l], v_caches[l], tb_t, ln_t, max_len,
+                                    scale=wl.scale, work_groups=wgs, workspace=workspace) for l in range(NL)])
+    calls = [per_slot[metas[r][0].data_ptr()] for r in range(ring)]
     torch.cuda.synchronize()
 
     ones = np.ones(B, dtype=np.int32)
     ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(NL)]
           for _ in range(total_steps)]
-    copied = [torch.cuda.Event() for _ in range(ring)]
+    released = [torch.cuda.Event() for _ in range(ring)]
     kv_bytes, table_entries, n_pairs = [], [], [0]
 
     def step(i):
         r = i % ring
-        if h_done[r] is not None:                                      # staging slot r free again:
+        if h_done[r] is not None:                                      # ring slot r free again:
             while not h_done[r].query():                               # poll; a blocking wait sleeps and
                 pass                                                   # wakes up late
         slots_v, lens_v, tab_v = h_views[r]
@@ -231,18 +250,23 @@ def main():
         cur[:] += 1
         lens_v[:] = cur
         tab_v[:] = tables
-        d_meta.copy_(h_meta[r], non_blocking=True)                     # 2. stage metadata (one copy)
+        if d_meta is not None:
+            d_meta.copy_(h_meta[r], non_blocking=True)                 # 2. stage metadata (one copy)
         if npairs:                                                     # 3. copy-on-write
             d_pairs[:npairs].copy_(h_pairs[r][:npairs], non_blocking=True)
             pkv.pkv_copy_blocks(k_caches, v_caches, d_pairs[:npairs])
             n_pairs[0] += npairs
-        copied[r].record(stream)
-        h_done[r] = copied[r]
+        if d_meta is not None:                                         # slot r is free once copied
+            released[r].record(stream)
+        appends, decodes = calls[r]
         for layer in range(NL):
             appends[layer].launch(k_new[i, layer], v_new[i, layer])    # 4. scatter new rows
             ev[i][layer][0].record(stream)
             decodes[layer].launch(q_all[i, layer])                     # 5. decode attention
             ev[i][layer][1].record(stream)
+        if d_meta is None:                                             # read in place until here
+            released[r].record(stream)
+        h_done[r] = released[r]
         kv_bytes.append(int(cur.astype(np.int64).sum()) * 2 * H * D * esz * NL)
         table_entries.append(int(((cur.astype(np.int64) + bs - 1) // bs).sum()))
 
@@ -309,7 +333,7 @@ def main():
         "dtype": wl.dtype,
         "data": "synthetic (seeded; Q/K/V ~ N(0,1) cast to the storage dtype)",
         "config": {"workload": wl.title, "layers": NL, "batch": B, "heads": H, "head_dim": D, "block_size": bs,
-                   "pool_blocks": wl.num_blocks, "work_groups": wgs,
+                   "pool_blocks": wl.num_blocks, "work_groups": wgs, "metadata": mode,
                    "mean_seq_len": round(kv_per_call / (2 * H * D * esz) / B, 1), "cow_pairs": n_pairs[0]},
         "hbm_peak_frac": round(value / HBM_PEAK_GBS, 4),
         "token_steps_per_s": round(B * args.steps / elapsed, 1),

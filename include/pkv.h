@@ -20,10 +20,15 @@
  *     pkv_last_error() returns a human-readable detail of the calling
  *     thread's most recent failure.  Out-parameters are written only on
  *     success, and a failed allocator call leaves the allocator unchanged.
- *   - Device pointers are caller-owned device memory.  The library keeps no
- *     pointer after a call returns and never allocates, frees or
- *     synchronises: device operations are enqueued on `stream` and return.
- *     The caller keeps every buffer alive until the stream has finished.
+ *   - Device pointers are caller-owned memory the GPU can access.  Pools, K/V
+ *     rows, queries, outputs and workspaces are device memory.  The small
+ *     per-step metadata (slot mappings, block tables, lengths, copy pairs)
+ *     may also be pinned host memory (hipHostMalloc), which the kernels read
+ *     in place: a few host-memory reads per work-group instead of a
+ *     host-to-device copy on the queue.  The library keeps no pointer after
+ *     a call returns and never allocates, frees or synchronises: device
+ *     operations are enqueued on `stream` and return.  The caller keeps every
+ *     buffer alive and unchanged until the stream has finished with it.
  *   - Pool layout (both K and V, per layer): [num_blocks][block_size]
  *     [num_heads][head_dim], contiguous, element type `dtype`.  Token
  *     position `pos` of a sequence lives in block table[pos / block_size] at
@@ -158,7 +163,7 @@ PKV_API int pkv_seq_release(pkv_allocator* a, const int32_t* row, int32_t n_bloc
 
 /* Scatter new K/V rows into the pools.
  * k_new, v_new: device [num_tokens][num_heads][head_dim] of `dtype`;
- * slot_mapping: device int64 [num_tokens]; token t goes to flat slot
+ * slot_mapping: int64 [num_tokens] (device or pinned host); token t goes to flat slot
  * slot_mapping[t] of k_cache / v_cache (device pools, layout above).  A
  * negative slot is skipped (padding); a slot >= num_blocks * block_size is
  * also skipped, never written.  A bit copy: the new step's K/V join the cache
@@ -170,7 +175,7 @@ PKV_API int pkv_append(const void* k_new, const void* v_new, int32_t num_tokens,
 
 /* Copy whole blocks for copy-on-write (hnwysp.cn/news/103996 §3.3).
  * k_caches, v_caches: HOST arrays of `num_layers` device pool pointers.
- * pairs: device int32 [n_pairs][2] = (source, destination) block ids.
+ * pairs: int32 [n_pairs][2] (device or pinned host) = (source, destination) block ids.
  * Every layer's K and V block `dst` becomes a bit copy of block `src`
  * (bytes_per_block = block_size * num_heads * head_dim * dtype bytes, a
  * multiple of 16).  Pairs are copied concurrently: destinations must be
@@ -205,8 +210,8 @@ PKV_API size_t pkv_decode_workspace_bytes(int32_t batch, int32_t num_heads, int3
  *   out, q: device [batch][num_heads][head_dim] of `dtype`; out rounded to
  *     nearest-even from float32 accumulation.
  *   k_cache, v_cache: device pools of num_blocks blocks (layout above).
- *   block_tables: device int32 [batch][max_blocks_per_seq].
- *   seq_lens: device int32 [batch].  max_seq_len: host upper bound of every
+ *   block_tables: int32 [batch][max_blocks_per_seq] (device or pinned host).
+ *   seq_lens: int32 [batch] (device or pinned host).  max_seq_len: host upper bound of every
  *     seq_lens entry (sizes the launch and the workspace).
  *   scale: softmax scale (1/sqrt(head_dim) for plain scaled dot-product).
  *   num_work_groups: 0 = automatic (pkv_decode_work_groups), else the

@@ -257,9 +257,12 @@ def _dtype_code(t) -> int:
     return codes[t.dtype]
 
 
-def _dev(t, name, dtype=None, ndim=None):
-    if not t.is_cuda:
-        raise InvalidArgument(PKV_ERR_INVALID, f"{name} must be a device tensor")
+def _dev(t, name, dtype=None, ndim=None, pinned_ok=False):
+    # Small per-step metadata may live in pinned host memory, which the GPU
+    # reads directly; everything else must be device memory.
+    if not (t.is_cuda or (pinned_ok and t.is_pinned())):
+        kind = "a device tensor or pinned host tensor" if pinned_ok else "a device tensor"
+        raise InvalidArgument(PKV_ERR_INVALID, f"{name} must be {kind}")
     if not t.is_contiguous():
         raise InvalidArgument(PKV_ERR_INVALID, f"{name} must be contiguous")
     if dtype is not None and t.dtype != dtype:
@@ -284,7 +287,8 @@ def _append_args(k_new, v_new, slot_mapping, k_cache, v_cache, stream):
         raise InvalidArgument(PKV_ERR_INVALID, "append: dtype mismatch")
     if slot_mapping.shape != (k_new.shape[0],):
         raise InvalidArgument(PKV_ERR_INVALID, "append: slot_mapping must be [T]")
-    return [_dev(k_new, "k_new"), _dev(v_new, "v_new"), k_new.shape[0], _dev(slot_mapping, "slot_mapping", torch.int64),
+    return [_dev(k_new, "k_new"), _dev(v_new, "v_new"), k_new.shape[0],
+            _dev(slot_mapping, "slot_mapping", torch.int64, pinned_ok=True),
             _dev(k_cache, "k_cache", ndim=4), _dev(v_cache, "v_cache", ndim=4), nb, bs, h, d, _dtype_code(k_cache),
             _stream(stream)]
 
@@ -310,7 +314,7 @@ def pkv_copy_blocks(k_caches, v_caches, pairs, stream=None) -> None:
     karr = (ctypes.c_void_p * nl)(*[t.data_ptr() for t in k_caches])
     varr = (ctypes.c_void_p * nl)(*[t.data_ptr() for t in v_caches])
     bytes_per_block = bs * h * d * k_caches[0].element_size()
-    _check(_lib.pkv_copy_blocks(karr, varr, nl, _dev(pairs, "pairs", torch.int32), pairs.shape[0], nb,
+    _check(_lib.pkv_copy_blocks(karr, varr, nl, _dev(pairs, "pairs", torch.int32, pinned_ok=True), pairs.shape[0], nb,
                                 bytes_per_block, _stream(stream)))
 
 
@@ -353,8 +357,9 @@ def _decode_args(out, q, k_cache, v_cache, block_tables, seq_lens, max_seq_len, 
     if workspace is None:
         workspace = decode_workspace(max(batch, 1), h, d, _DT_NAMES[code], work_groups, q.device)
     args = [_dev(out, "out"), _dev(q, "q"), _dev(k_cache, "k_cache", ndim=4), _dev(v_cache, "v_cache", ndim=4),
-            _dev(block_tables, "block_tables", torch.int32), block_tables.shape[1],
-            _dev(seq_lens, "seq_lens", torch.int32), int(max_seq_len), batch, h, d, bs, nb, float(scale), code,
+            _dev(block_tables, "block_tables", torch.int32, pinned_ok=True), block_tables.shape[1],
+            _dev(seq_lens, "seq_lens", torch.int32, pinned_ok=True), int(max_seq_len), batch, h, d, bs, nb,
+            float(scale), code,
             int(work_groups), _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
             _stream(stream)]
     return args, workspace
@@ -376,7 +381,8 @@ class PreparedDecode:
     ``launch(q, out)`` only swaps the query/output pointers (tensors of the
     same shape and dtype as at preparation) and enqueues the kernels; it is
     meant for decode loops where Python overhead would otherwise dominate.
-    The tensors given at preparation must stay alive and in place.
+    ``set_metadata`` repoints the tables and lengths (same shapes).  The
+    tensors given at preparation must stay alive and in place.
     """
 
     def __init__(self, out, q, k_cache, v_cache, block_tables, seq_lens, max_seq_len, scale=None, work_groups=0,
@@ -390,6 +396,15 @@ class PreparedDecode:
         if tuple(t.shape) != self._shape or t.dtype != self._dtype or not t.is_contiguous() or not t.is_cuda:
             raise InvalidArgument(PKV_ERR_INVALID, f"prepared call: {what} differs from the prepared tensor")
         self._args[i] = ctypes.c_void_p(t.data_ptr())
+
+    def set_metadata(self, block_tables, seq_lens) -> None:
+        """Point the call at other tables/lengths of the prepared shapes (device or pinned host)."""
+        torch = _torch()
+        if tuple(block_tables.shape) != (self._shape[0], self._args[5]) or tuple(seq_lens.shape) != (self._shape[0],):
+            raise InvalidArgument(PKV_ERR_INVALID, "prepared decode: metadata shapes differ")
+        self._args[4] = _dev(block_tables, "block_tables", torch.int32, pinned_ok=True)
+        self._args[6] = _dev(seq_lens, "seq_lens", torch.int32, pinned_ok=True)
+        self._meta = (block_tables, seq_lens)   # kept alive while the call points at them
 
     def launch(self, q=None, out=None) -> None:
         if q is not None:
@@ -406,6 +421,14 @@ class PreparedAppend(PreparedDecode):
         self._args = _append_args(k_new, v_new, slot_mapping, k_cache, v_cache, stream)
         self._keep = (slot_mapping, k_cache, v_cache)
         self._shape, self._dtype = tuple(k_new.shape), k_new.dtype
+
+    def set_slots(self, slot_mapping) -> None:
+        """Point the call at another slot array of the prepared length (device or pinned host)."""
+        torch = _torch()
+        if tuple(slot_mapping.shape) != (self._shape[0],):
+            raise InvalidArgument(PKV_ERR_INVALID, "prepared append: slot_mapping shape differs")
+        self._args[3] = _dev(slot_mapping, "slot_mapping", torch.int64, pinned_ok=True)
+        self._meta = (slot_mapping,)
 
     def launch(self, k_new=None, v_new=None) -> None:
         if k_new is not None:

@@ -263,3 +263,53 @@ def test_scale_is_applied():
         torch.cuda.synchronize()
         ref = oatt.decode_attention(c.vals["q"], c.ok_pool, c.ov_pool, c.tables_np, wl.seq_lens, "f32", scale)
         pc.compare(c, out, ref)
+
+
+def test_metadata_in_pinned_host_memory():
+    # Tables, lengths, slots and copy pairs read in place from pinned host
+    # memory give the same bytes as the same calls with device metadata.
+    wl = workloads.custom([700, 65, 1, 0, 300, 33], num_heads=8, head_dim=128, dtype="f16", block_size=16, seed=41)
+    c = pc.build(wl, DEV)
+    ref = pc.oracle_out(c)
+    h_tables = c.tables.cpu().pin_memory()
+    h_lens = c.lens.cpu().pin_memory()
+    dev_out = pc.run_gpu(c).clone()
+    out = torch.empty_like(c.q)
+    for wg in (0, 48):
+        pkv.pkv_attention_decode(out, c.q, c.k_cache, c.v_cache, h_tables, h_lens, wl.max_seq_len,
+                                 scale=wl.scale, work_groups=wg)
+        torch.cuda.synchronize()
+        pc.compare(c, out, ref)
+        if wg == 0:
+            assert torch.equal(out.view(torch.int16), dev_out.view(torch.int16))
+    # Prepared call repointed between device and pinned metadata.
+    prep = pkv.PreparedDecode(out, c.q, c.k_cache, c.v_cache, c.tables, c.lens, wl.max_seq_len, scale=wl.scale)
+    for tb, ln in ((h_tables, h_lens), (c.tables, c.lens), (h_tables, h_lens)):
+        out.fill_(float("nan"))
+        prep.set_metadata(tb, ln)
+        prep.launch()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), dev_out.view(torch.int16))
+    with pytest.raises(pkv.InvalidArgument):
+        pkv.pkv_attention_decode(out, c.q, c.k_cache, c.v_cache, c.tables.cpu(), c.lens, wl.max_seq_len)
+
+    # Scatter and block copies with pinned slots / pairs, bit-exact.
+    nb, bs, h, d = 10, 8, 2, 64
+    rng = np.random.default_rng(42)
+    okp = np.full((nb, bs, h, d), workloads.nan_storage("bf16"), dtype=workloads.storage_np_dtype("bf16"))
+    ovp = okp.copy()
+    kc = torch.full((nb, bs, h, d), float("nan"), dtype=torch.bfloat16, device=DEV)
+    vc = torch.full_like(kc, float("nan"))
+    slots = rng.permutation(nb * bs)[:37].astype(np.int64)
+    kn = workloads.to_storage(rng.standard_normal((37, h, d), dtype=np.float32), "bf16")
+    vn = workloads.to_storage(rng.standard_normal((37, h, d), dtype=np.float32), "bf16")
+    prep_a = pkv.PreparedAppend(pc.to_device(kn, "bf16", DEV), pc.to_device(vn, "bf16", DEV),
+                                torch.from_numpy(slots).pin_memory(), kc, vc)
+    prep_a.launch()
+    pairs = [(1, 7), (4, 2), (9, 0)]
+    pkv.pkv_copy_blocks([kc], [vc], torch.tensor(pairs, dtype=torch.int32).pin_memory())
+    torch.cuda.synchronize()
+    opool.append(okp, ovp, kn, vn, slots.tolist())
+    opool.copy_blocks([okp], [ovp], pairs)
+    assert np.array_equal(pc.to_bits(kc), pc.storage_bits(okp))
+    assert np.array_equal(pc.to_bits(vc), pc.storage_bits(ovp))
