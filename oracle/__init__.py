@@ -27,11 +27,13 @@ Modules:
   (fork, reserve with copy-on-write, release).
 * :mod:`oracle.pool` — K/V scatter into blocks and whole-block copies.
 * :mod:`oracle.attention` — decode attention by its plain definition.
+* :mod:`oracle.quant` — 8-bit (int8 / FP8 E4M3) K/V rows: per-row absmax
+  quantisation on write, exact dequantisation and attention on read.
 
 Parity status: every function is pinned by ``tests/test_oracle_*.py`` against
 closed forms printed on the pages, hand-derived traces, library routines
-(``torch.nn.functional.scaled_dot_product_attention`` in float64) and
-invariants; none is "parity unpinned".
+(``torch.nn.functional.scaled_dot_product_attention`` in float64, torch's
+``float8_e4m3fn`` type) and invariants; none is "parity unpinned".
 """
 
-from . import allocator, attention, pool, sizes  # noqa: F401
+from . import allocator, attention, pool, quant, sizes  # noqa: F401
