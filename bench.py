@@ -17,6 +17,10 @@ of 1.3x the blocks needed).  ``--workload full7b_step`` runs the 32-layer step
 (batch 256, lognormal lengths, 30 % sharing a 256-token prefix, pool = 85 % of
 free HBM); ``--workload long13b`` the 40-head bf16 4096-token case.
 
+``--kv-dtype i8|fp8`` stores K/V as 8-bit codes plus one float32 scale per
+(token, head) (pkv_append_quant / pkv_attention_decode_quant); queries and
+outputs stay in the workload's dtype.
+
 Prints one JSON line.  ``value`` is KV GB/s over the whole timed step (K+V
 bytes attention reads / step time).  ``roofline`` reports the decode-attention
 call (decode kernel + merge kernel) timed with HIP events on its stream, and
@@ -45,7 +49,8 @@ os.environ.setdefault("HSA_ENABLE_SDMA", "0")
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, 8 TB/s
 METRIC = "paged-attn decode KV GB/s and % of MI355X HBM peak; tokens-steps/sec"
-KERNEL_SOURCE = os.path.join(ROOT, "paged_attention_amd", "csrc", "kernels.hip")
+KERNEL_SOURCES = [os.path.join(ROOT, "paged_attention_amd", "csrc", f)
+                  for f in ("decode_common.h", "kernels.hip", "kernels_q8.hip")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
 
 
@@ -60,6 +65,8 @@ def parse():
     p.add_argument("--ring", type=int, default=4, help="host staging buffers (how many steps the host may run ahead)")
     p.add_argument("--metadata", choices=["pinned", "device"], default="pinned",
                    help="where kernels read step metadata: pinned host memory in place, or a device copy")
+    p.add_argument("--kv-dtype", choices=["auto", "i8", "fp8"], default="auto",
+                   help="K/V cache storage: the workload's dtype (auto) or an 8-bit format")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target length of the oracle timing sample")
     p.add_argument("--no-cpu", action="store_true", help="skip the cpu_baseline leg")
     p.add_argument("--copy-calibration", action="store_true",
@@ -68,8 +75,11 @@ def parse():
 
 
 def source_hash() -> str:
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in KERNEL_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def recorded_traffic(workload: str):
@@ -85,9 +95,10 @@ def recorded_traffic(workload: str):
     return entry.get("bytes_per_call")
 
 
-def cpu_baseline(wl, sample_rows, target_s):
+def cpu_baseline(wl, sample_rows, target_s, kv):
     """Time the oracle on sequences of the same workload until ~target_s of work."""
     from oracle import attention as oatt
+    from oracle import quant as oquant
 
     try:
         from threadpoolctl import threadpool_info
@@ -102,13 +113,23 @@ def cpu_baseline(wl, sample_rows, target_s):
     while spent < target_s and i < 100 * wl.batch:
         b = int(order[i % wl.batch])
         i += 1
-        q, keys, vals = sample_rows(b)
+        rows = sample_rows(b)
+        L = rows[1].shape[0]
         t0 = time.perf_counter()
-        oatt.contiguous_attention(q[None], [keys], [vals], wl.dtype, wl.scale)
+        if kv == "dense":
+            q, keys, vals = rows
+            oatt.contiguous_attention(q[None], [keys], [vals], wl.dtype, wl.scale)
+            done_bytes += L * 2 * h * d * wl.dtype_bytes
+        else:
+            # The sequence's rows as a pool of one-token blocks, read through
+            # an identity table.
+            q, kc, ks, vc, vs = rows
+            oquant.decode_attention(q[None], kc[:, None], vc[:, None], ks[:, :, None], vs[:, :, None],
+                                    np.arange(L, dtype=np.int64)[None], [L], wl.dtype, kv, wl.scale)
+            done_bytes += L * 2 * h * (d + 4)
         spent += time.perf_counter() - t0
-        done_bytes += keys.shape[0] * 2 * h * d * wl.dtype_bytes
         seqs += 1
-        tokens += keys.shape[0]
+        tokens += L
     return {"value": round(done_bytes / spent / 1e9, 4), "unit": "GB/s", "cores": int(cores), "kind": "oracle",
             "sample": f"numpy float64 oracle, {seqs} sequence decodes of this workload ({tokens} tokens x {h} heads, "
                       f"one layer), {spent:.1f} s of oracle time"}
@@ -140,6 +161,9 @@ def main():
     B, H, D, bs, NL = wl.batch, wl.num_heads, wl.head_dim, wl.block_size, wl.num_layers
     tdt = {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32}[wl.dtype]
     esz = wl.dtype_bytes
+    kv = "dense" if args.kv_dtype == "auto" else args.kv_dtype
+    # K/V bytes one token adds to one layer's cache (codes and scales for 8-bit)
+    tok_bytes = 2 * H * D * esz if kv == "dense" else 2 * H * (D + 4)
     lens0 = wl.seq_lens.astype(np.int64)
     max_len = int(lens0.max()) + total_steps
     maxb = -(-max_len // bs)
@@ -170,17 +194,23 @@ def main():
     cur = (done + hist).astype(np.int32)
     slots_hist = torch.from_numpy(np.concatenate(history)).to(dev)
     n_hist = slots_hist.numel()
-    k_caches, v_caches = [], []
+    k_caches, v_caches, k_scales, v_scales = [], [], [], []
     gen = torch.Generator(device=dev)
     for layer in range(NL):
-        kc = torch.empty((wl.num_blocks, bs, H, D), dtype=tdt, device=dev)
+        kc = torch.empty((wl.num_blocks, bs, H, D), dtype=tdt if kv == "dense" else torch.uint8, device=dev)
         vc = torch.empty_like(kc)
+        if kv != "dense":
+            k_scales.append(torch.empty((wl.num_blocks, H, bs), dtype=torch.float32, device=dev))
+            v_scales.append(torch.empty_like(k_scales[-1]))
         gen.manual_seed(5000 + layer)
         for a0 in range(0, n_hist, 1 << 16):   # history rows drawn on the device, in slices
             a1 = min(n_hist, a0 + (1 << 16))
             kr = torch.randn((a1 - a0, H, D), generator=gen, device=dev, dtype=torch.float32).to(tdt)
             vr = torch.randn((a1 - a0, H, D), generator=gen, device=dev, dtype=torch.float32).to(tdt)
-            pkv.pkv_append(kr, vr, slots_hist[a0:a1], kc, vc)
+            if kv == "dense":
+                pkv.pkv_append(kr, vr, slots_hist[a0:a1], kc, vc)
+            else:
+                pkv.pkv_append_quant(kr, vr, slots_hist[a0:a1], kc, vc, k_scales[-1], v_scales[-1], kv)
         k_caches.append(kc)
         v_caches.append(vc)
     del slots_hist
@@ -189,8 +219,8 @@ def main():
     k_new = torch.randn((total_steps, NL, B, H, D), generator=gen, device=dev, dtype=torch.float32).to(tdt)
     v_new = torch.randn((total_steps, NL, B, H, D), generator=gen, device=dev, dtype=torch.float32).to(tdt)
     out = torch.empty((B, H, D), dtype=tdt, device=dev)
-    wgs = args.work_groups or pkv.pkv_decode_work_groups()
-    workspace = pkv.decode_workspace(B, H, D, wl.dtype, wgs, device=dev)
+    wgs = args.work_groups or pkv.pkv_decode_work_groups(wl.dtype if kv == "dense" else kv)
+    workspace = pkv.decode_workspace(B, H, D, wl.dtype if kv == "dense" else kv, wgs, device=dev)
     # Step metadata is one packed buffer: slots (int64), lengths and block
     # tables (int32).  Host side: a ring of pinned buffers, so the host can
     # prepare step i+1 while step i's kernels still read (or copy) slot i.
@@ -227,10 +257,19 @@ def main():
         key = metas[r][0].data_ptr()
         if key not in per_slot:
             sl_t, ln_t, tb_t = metas[r]
-            per_slot[key] = (
-                [pkv.PreparedAppend(k_new[0, l], v_new[0, l], sl_t, k_caches[l], v_caches[l]) for l in range(NL)],
-                [pkv.PreparedDecode(out, q_all[0, l], k_caches[l], v_caches[l], tb_t, ln_t, max_len,
-                                    scale=wl.scale, work_groups=wgs, workspace=workspace) for l in range(NL)])
+            if kv == "dense":
+                per_slot[key] = (
+                    [pkv.PreparedAppend(k_new[0, l], v_new[0, l], sl_t, k_caches[l], v_caches[l])
+                     for l in range(NL)],
+                    [pkv.PreparedDecode(out, q_all[0, l], k_caches[l], v_caches[l], tb_t, ln_t, max_len,
+                                        scale=wl.scale, work_groups=wgs, workspace=workspace) for l in range(NL)])
+            else:
+                per_slot[key] = (
+                    [pkv.PreparedAppendQuant(k_new[0, l], v_new[0, l], sl_t, k_caches[l], v_caches[l],
+                                             k_scales[l], v_scales[l], kv) for l in range(NL)],
+                    [pkv.PreparedDecodeQuant(out, q_all[0, l], k_caches[l], v_caches[l], k_scales[l], v_scales[l],
+                                             tb_t, ln_t, max_len, kv, scale=wl.scale, work_groups=wgs,
+                                             workspace=workspace) for l in range(NL)])
     calls = [per_slot[metas[r][0].data_ptr()] for r in range(ring)]
     torch.cuda.synchronize()
 
@@ -255,6 +294,8 @@ def main():
         if npairs:                                                     # 3. copy-on-write
             d_pairs[:npairs].copy_(h_pairs[r][:npairs], non_blocking=True)
             pkv.pkv_copy_blocks(k_caches, v_caches, d_pairs[:npairs])
+            if kv != "dense":
+                pkv.pkv_copy_blocks(k_scales, v_scales, d_pairs[:npairs])
             n_pairs[0] += npairs
         if d_meta is not None:                                         # slot r is free once copied
             released[r].record(stream)
@@ -267,7 +308,7 @@ def main():
         if d_meta is None:                                             # read in place until here
             released[r].record(stream)
         h_done[r] = released[r]
-        kv_bytes.append(int(cur.astype(np.int64).sum()) * 2 * H * D * esz * NL)
+        kv_bytes.append(int(cur.astype(np.int64).sum()) * tok_bytes * NL)
         table_entries.append(int(((cur.astype(np.int64) + bs - 1) // bs).sum()))
 
     for i in range(args.warmup):
@@ -286,11 +327,12 @@ def main():
     kv_total = float(sum(kv_bytes))
     value = kv_total / elapsed / 1e9
     # Algorithmic bytes of one decode-attention call (mean over timed steps, one
-    # layer): K+V rows read + q in + out + block-table entries + lengths.
+    # layer): K+V rows read (8-bit: codes and scales) + q in + out +
+    # block-table entries + lengths.
     kv_per_call = float(np.mean(kv_bytes)) / NL
     algo = kv_per_call + 2 * B * H * D * esz + 4 * float(np.mean(table_entries)) + 4 * B
     achieved = algo / attn_s / 1e9
-    traffic = recorded_traffic(args.workload)
+    traffic = recorded_traffic(args.workload if kv == "dense" else f"{args.workload}/{kv}")
 
     extra = {}
     if args.copy_calibration:
@@ -309,14 +351,22 @@ def main():
             idx = np.arange(L)
             blocks = tables[b, idx // bs].astype(np.int64)
             flat = torch.from_numpy(blocks * bs + idx % bs).to(dev)
-            kk = k_caches[0].view(-1, H, D)[flat].cpu()
-            vv = v_caches[0].view(-1, H, D)[flat].cpu()
             qq = q_all[total_steps - 1, 0, b].cpu()
             if tdt == torch.bfloat16:
-                return tuple(x.view(torch.int16).numpy().view(np.uint16) for x in (qq, kk, vv))
-            return qq.numpy(), kk.numpy(), vv.numpy()
+                qq = qq.view(torch.int16).numpy().view(np.uint16)
+            else:
+                qq = qq.numpy()
+            if kv != "dense":
+                fb, fp = flat // bs, flat % bs
+                return (qq, k_caches[0].view(-1, H, D)[flat].cpu().numpy(), k_scales[0][fb, :, fp].cpu().numpy(),
+                        v_caches[0].view(-1, H, D)[flat].cpu().numpy(), v_scales[0][fb, :, fp].cpu().numpy())
+            kk = k_caches[0].view(-1, H, D)[flat].cpu()
+            vv = v_caches[0].view(-1, H, D)[flat].cpu()
+            if tdt == torch.bfloat16:
+                return (qq,) + tuple(x.view(torch.int16).numpy().view(np.uint16) for x in (kk, vv))
+            return qq, kk.numpy(), vv.numpy()
 
-        cpu = cpu_baseline(wl, rows, args.cpu_seconds)
+        cpu = cpu_baseline(wl, rows, args.cpu_seconds, kv)
 
     ms_per_step = elapsed / args.steps * 1e3
     rec = {
@@ -330,11 +380,12 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": wl.dtype,
+        "dtype": wl.dtype if kv == "dense" else {"i8": "i8", "fp8": "fp8_e4m3"}[kv],
         "data": "synthetic (seeded; Q/K/V ~ N(0,1) cast to the storage dtype)",
-        "config": {"workload": wl.title, "layers": NL, "batch": B, "heads": H, "head_dim": D, "block_size": bs,
+        "config": {"workload": wl.title + ("" if kv == "dense" else f"; K/V cache {kv} + f32 scale per (token, head)"),
+                   "kv_cache": wl.dtype if kv == "dense" else kv, "q_dtype": wl.dtype, "layers": NL, "batch": B, "heads": H, "head_dim": D, "block_size": bs,
                    "pool_blocks": wl.num_blocks, "work_groups": wgs, "metadata": mode,
-                   "mean_seq_len": round(kv_per_call / (2 * H * D * esz) / B, 1), "cow_pairs": n_pairs[0]},
+                   "mean_seq_len": round(kv_per_call / tok_bytes / B, 1), "cow_pairs": n_pairs[0]},
         "hbm_peak_frac": round(value / HBM_PEAK_GBS, 4),
         "token_steps_per_s": round(B * args.steps / elapsed, 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",

@@ -67,7 +67,10 @@ enum {
   PKV_ERR_HIP = -5        /* a HIP runtime call failed (launch error) */
 };
 
-typedef enum { PKV_F32 = 0, PKV_F16 = 1, PKV_BF16 = 2 } pkv_dtype;
+/* Element types.  F32/F16/BF16 are the types of queries, outputs, new K/V
+ * rows and 16/32-bit caches; I8 and FP8_E4M3 are 8-bit cache formats only
+ * (symmetric int8 codes in [-127, 127]; OCP FP8 E4M3, bias 7, largest 448). */
+typedef enum { PKV_F32 = 0, PKV_F16 = 1, PKV_BF16 = 2, PKV_I8 = 3, PKV_FP8_E4M3 = 4 } pkv_dtype;
 
 /* Short description of a status code (static storage). */
 PKV_API const char* pkv_strerror(int status);
@@ -185,13 +188,17 @@ PKV_API int pkv_copy_blocks(void* const* k_caches, void* const* v_caches, int32_
                             const int32_t* pairs, int32_t n_pairs, int32_t num_blocks, size_t bytes_per_block,
                             hipStream_t stream);
 
-/* Work-groups pkv_attention_decode launches when called with
- * num_work_groups = 0: one per compute unit of the current device (256 on
- * MI355X).  PKV_ERR_HIP if no device is current. */
-PKV_API int32_t pkv_decode_work_groups(void);
+/* Work-groups a decode call launches when called with num_work_groups = 0,
+ * for caches of `cache_dtype`: one per compute unit of the current device
+ * for F32/F16/BF16 caches (256 on MI355X), two per compute unit for I8 and
+ * FP8_E4M3 caches.  PKV_ERR_HIP if no device is current, PKV_ERR_INVALID for
+ * an unknown type. */
+PKV_API int32_t pkv_decode_work_groups(pkv_dtype cache_dtype);
 
-/* Device workspace pkv_attention_decode needs for `num_work_groups` (0 = the
- * automatic count): a per-sequence plan (2 int32 per sequence and head
+/* Device workspace a decode call needs for `num_work_groups` (0 = the
+ * automatic count for that cache type).  `dtype` is the cache element type:
+ * F32/F16/BF16 for pkv_attention_decode, I8/FP8_E4M3 for
+ * pkv_attention_decode_quant.  It holds a per-sequence plan (2 int32 per sequence and head
  * slice, at most 8190 per launch) and float32 partial softmax states for
  * 2 * num_work_groups pieces of num_heads * (head_dim + 2) floats, each
  * region 256-byte aligned.  It does not depend on sequence lengths.
@@ -235,6 +242,60 @@ PKV_API int pkv_attention_decode(void* out, const void* q, const void* k_cache, 
                                  int32_t block_size, int32_t num_blocks, float scale, pkv_dtype dtype,
                                  int32_t num_work_groups, void* workspace, size_t workspace_bytes,
                                  hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * 8-bit caches (int8 or OCP FP8 E4M3)
+ *
+ * Storing K/V in 8 bits halves the bytes per token against fp16 and changes
+ * nothing of the paging: block tables, slots, the allocator and
+ * pkv_copy_blocks are the same (hnwysp.cn/news/103996 §5.4;
+ * icman.com.cn/news/78786 §1.3; m.lqnn.cn/news/240480 §6.2).
+ *
+ * Code pools: [num_blocks][block_size][num_heads][head_dim] bytes, the
+ * layout above with one-byte elements.  Scale pools: float32
+ * [num_blocks][num_heads][block_size], one scale per (token, head) row, for K
+ * and for V.  A row x of head_dim values is stored as
+ *   scale = max_i |x_i| / QMAX          (QMAX = 127 for I8, 448 for FP8_E4M3)
+ *   I8:       code_i = clamp(rint(x_i / scale), -127, 127)
+ *   FP8_E4M3: code_i = the E4M3 value nearest clamp(x_i / scale, -448, 448),
+ *             ties to the even code (bias 7, subnormals, no infinities)
+ * with float32 arithmetic (IEEE division); a row of zeros stores scale 0 and
+ * zero codes.  It reads back as code_i * scale.  New rows must be finite.
+ * Copy-on-write copies a block of the code pools and of the scale pools:
+ * call pkv_copy_blocks once with the code pools (bytes_per_block =
+ * block_size * num_heads * head_dim) and once with the scale pools
+ * (num_heads * block_size * 4).
+ * ------------------------------------------------------------------------- */
+
+/* Quantise and scatter new K/V rows.
+ * k_new, v_new: device [num_tokens][num_heads][head_dim] of src_dtype
+ * (F32, F16 or BF16); slot_mapping: int64 [num_tokens] (device or pinned
+ * host).  Token t's codes go to flat slot slot_mapping[t] of k_cache /
+ * v_cache and its per-head scales to k_scales / v_scales at
+ * [slot / block_size][h][slot % block_size].  Negative slots and slots >=
+ * num_blocks * block_size are skipped.  cache_dtype: I8 or FP8_E4M3.
+ * Rows and pools must be 16-byte aligned. */
+PKV_API int pkv_append_quant(const void* k_new, const void* v_new, int32_t num_tokens,
+                             const int64_t* slot_mapping, void* k_cache, void* v_cache, float* k_scales,
+                             float* v_scales, int32_t num_blocks, int32_t block_size, int32_t num_heads,
+                             int32_t head_dim, pkv_dtype src_dtype, pkv_dtype cache_dtype, hipStream_t stream);
+
+/* Decode attention over an 8-bit paged cache: pkv_attention_decode's result
+ * with every K/V element read as code * scale of its row, dequantised inside
+ * the kernel.  q and out are device [batch][num_heads][head_dim] of q_dtype
+ * (F32, F16 or BF16); k_scales / v_scales the scale pools above;
+ * cache_dtype I8 or FP8_E4M3; every other argument, the workspace
+ * (pkv_decode_workspace_bytes with dtype = cache_dtype) and the handling of
+ * bad lengths and block ids are those of pkv_attention_decode.  q, out,
+ * pools and scale pools must be 16-byte aligned. */
+PKV_API int pkv_attention_decode_quant(void* out, const void* q, const void* k_cache, const void* v_cache,
+                                       const float* k_scales, const float* v_scales,
+                                       const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                       const int32_t* seq_lens, int32_t max_seq_len, int32_t batch,
+                                       int32_t num_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                       float scale, pkv_dtype q_dtype, pkv_dtype cache_dtype,
+                                       int32_t num_work_groups, void* workspace, size_t workspace_bytes,
+                                       hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -11,7 +11,9 @@ Entry points keep the C names:
 
 * :class:`BlockAllocator` — ``pkv_allocator_*``, ``pkv_block_*``, ``pkv_seq_*``
 * :func:`pkv_append`, :func:`pkv_copy_blocks`, :func:`pkv_attention_decode`,
-  :func:`pkv_decode_workspace_bytes`, :func:`pkv_decode_partition_tokens`
+  :func:`pkv_decode_workspace_bytes`, :func:`pkv_decode_work_groups`
+* 8-bit caches: :func:`pkv_append_quant`, :func:`pkv_attention_decode_quant`
+  (code pools of one-byte elements plus float32 scale pools ``[NB][H][bs]``)
 """
 
 from __future__ import annotations
@@ -32,8 +34,9 @@ PKV_ERR_BAD_BLOCK = -3
 PKV_ERR_REFCOUNT = -4
 PKV_ERR_HIP = -5
 
-PKV_F32, PKV_F16, PKV_BF16 = 0, 1, 2
-DTYPE_CODES = {"f32": PKV_F32, "f16": PKV_F16, "bf16": PKV_BF16}
+PKV_F32, PKV_F16, PKV_BF16, PKV_I8, PKV_FP8_E4M3 = 0, 1, 2, 3, 4
+DTYPE_CODES = {"f32": PKV_F32, "f16": PKV_F16, "bf16": PKV_BF16, "i8": PKV_I8, "fp8": PKV_FP8_E4M3}
+CACHE_FORMATS = ("i8", "fp8")   # 8-bit cache formats: int8 codes, OCP FP8 E4M3 codes
 
 
 class PkvError(RuntimeError):
@@ -84,10 +87,15 @@ def _load():
         "pkv_seq_release": (ctypes.c_int, [vp, p32, i32]),
         "pkv_append": (ctypes.c_int, [vp, vp, i32, vp, vp, vp, i32, i32, i32, i32, ctypes.c_int, vp]),
         "pkv_copy_blocks": (ctypes.c_int, [ctypes.POINTER(vp), ctypes.POINTER(vp), i32, vp, i32, i32, sz, vp]),
-        "pkv_decode_work_groups": (i32, []),
+        "pkv_decode_work_groups": (i32, [ctypes.c_int]),
         "pkv_decode_workspace_bytes": (sz, [i32, i32, i32, ctypes.c_int, i32]),
         "pkv_attention_decode": (ctypes.c_int, [vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, i32, i32,
                                                 ctypes.c_float, ctypes.c_int, i32, vp, sz, vp]),
+        "pkv_append_quant": (ctypes.c_int, [vp, vp, i32, vp, vp, vp, vp, vp, i32, i32, i32, i32, ctypes.c_int,
+                                            ctypes.c_int, vp]),
+        "pkv_attention_decode_quant": (ctypes.c_int, [vp, vp, vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, i32,
+                                                      i32, ctypes.c_float, ctypes.c_int, ctypes.c_int, i32, vp, sz,
+                                                      vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -299,35 +307,44 @@ def pkv_append(k_new, v_new, slot_mapping, k_cache, v_cache, stream=None) -> Non
 
 
 def pkv_copy_blocks(k_caches, v_caches, pairs, stream=None) -> None:
-    """Copy blocks ``pairs[i, 0] -> pairs[i, 1]`` in every layer's K and V pool."""
+    """Copy blocks ``pairs[i, 0] -> pairs[i, 1]`` in every layer's K and V pool.
+
+    A pool is any tensor whose first dimension is the block id: K/V pools
+    ``[NB][bs][H][D]`` and also the ``[NB][H][bs]`` scale pools of 8-bit caches
+    (copy those with a second call).
+    """
     torch = _torch()
     if len(k_caches) != len(v_caches) or not k_caches:
         raise InvalidArgument(PKV_ERR_INVALID, "copy_blocks: need matching non-empty layer lists")
-    nb, bs, h, d = k_caches[0].shape
+    nb = k_caches[0].shape[0]
     for t in list(k_caches) + list(v_caches):
         if t.shape != k_caches[0].shape or t.dtype != k_caches[0].dtype:
             raise InvalidArgument(PKV_ERR_INVALID, "copy_blocks: layer pools differ in shape or dtype")
-        _dev(t, "pool", ndim=4)
+        if t.dim() < 2:
+            raise InvalidArgument(PKV_ERR_INVALID, "copy_blocks: a pool is [num_blocks][...]")
+        _dev(t, "pool")
     if pairs.dim() != 2 or pairs.shape[1] != 2:
         raise InvalidArgument(PKV_ERR_INVALID, "copy_blocks: pairs must be [n][2]")
     nl = len(k_caches)
     karr = (ctypes.c_void_p * nl)(*[t.data_ptr() for t in k_caches])
     varr = (ctypes.c_void_p * nl)(*[t.data_ptr() for t in v_caches])
-    bytes_per_block = bs * h * d * k_caches[0].element_size()
+    bytes_per_block = k_caches[0][0].numel() * k_caches[0].element_size()
     _check(_lib.pkv_copy_blocks(karr, varr, nl, _dev(pairs, "pairs", torch.int32, pinned_ok=True), pairs.shape[0], nb,
                                 bytes_per_block, _stream(stream)))
 
 
-def pkv_decode_work_groups() -> int:
-    """Work-groups decode attention launches by default on the current device."""
-    return _check(_lib.pkv_decode_work_groups())
+def pkv_decode_work_groups(cache_dtype: str = "f16") -> int:
+    """Work-groups decode attention launches by default on the current device for this cache type."""
+    if cache_dtype not in DTYPE_CODES:
+        raise InvalidArgument(PKV_ERR_INVALID, f"unknown dtype {cache_dtype!r}")
+    return _check(_lib.pkv_decode_work_groups(DTYPE_CODES[cache_dtype]))
 
 
 def pkv_decode_workspace_bytes(batch, num_heads, head_dim, dtype, work_groups=0) -> int:
     return int(_lib.pkv_decode_workspace_bytes(batch, num_heads, head_dim, DTYPE_CODES[dtype], work_groups))
 
 
-_DT_NAMES = {PKV_F32: "f32", PKV_F16: "f16", PKV_BF16: "bf16"}
+_DT_NAMES = {PKV_F32: "f32", PKV_F16: "f16", PKV_BF16: "bf16", PKV_I8: "i8", PKV_FP8_E4M3: "fp8"}
 
 
 def decode_workspace(batch, num_heads, head_dim, dtype, work_groups=0, device="cuda"):
@@ -391,6 +408,7 @@ class PreparedDecode:
                                       work_groups, workspace, stream)
         self._keep = (k_cache, v_cache, block_tables, seq_lens, ws)
         self._shape, self._dtype = tuple(q.shape), q.dtype
+        self._fn = _lib.pkv_attention_decode
 
     def _swap(self, i, t, what):
         if tuple(t.shape) != self._shape or t.dtype != self._dtype or not t.is_contiguous() or not t.is_cuda:
@@ -411,7 +429,7 @@ class PreparedDecode:
             self._swap(1, q, "q")
         if out is not None:
             self._swap(0, out, "out")
-        _check(_lib.pkv_attention_decode(*self._args))
+        _check(self._fn(*self._args))
 
 
 class PreparedAppend(PreparedDecode):
@@ -438,8 +456,125 @@ class PreparedAppend(PreparedDecode):
         _check(_lib.pkv_append(*self._args))
 
 
+
+# ---------------------------------------------------------------------------
+# 8-bit caches
+# ---------------------------------------------------------------------------
+
+def _fmt_code(cache_dtype: str) -> int:
+    if cache_dtype not in CACHE_FORMATS:
+        raise InvalidArgument(PKV_ERR_INVALID, f"cache_dtype must be one of {CACHE_FORMATS}, got {cache_dtype!r}")
+    return DTYPE_CODES[cache_dtype]
+
+
+def _q8_pools(k_cache, v_cache, k_scales, v_scales, what):
+    torch = _torch()
+    if k_cache.dim() != 4 or v_cache.shape != k_cache.shape:
+        raise InvalidArgument(PKV_ERR_INVALID, f"{what}: code pools must be [NB][bs][H][D] and alike")
+    if k_cache.element_size() != 1 or v_cache.element_size() != 1:
+        raise InvalidArgument(PKV_ERR_INVALID, f"{what}: code pools hold one-byte elements")
+    nb, bs, h, d = k_cache.shape
+    if k_scales.shape != (nb, h, bs) or v_scales.shape != (nb, h, bs):
+        raise InvalidArgument(PKV_ERR_INVALID, f"{what}: scale pools must be [NB][H][bs] = {(nb, h, bs)}")
+    return [_dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _dev(k_scales, "k_scales", torch.float32),
+            _dev(v_scales, "v_scales", torch.float32)], (nb, bs, h, d)
+
+
+def _append_quant_args(k_new, v_new, slot_mapping, k_cache, v_cache, k_scales, v_scales, cache_dtype, stream):
+    torch = _torch()
+    pools, (nb, bs, h, d) = _q8_pools(k_cache, v_cache, k_scales, v_scales, "append_quant")
+    if k_new.shape[1:] != (h, d) or v_new.shape != k_new.shape or v_new.dtype != k_new.dtype:
+        raise InvalidArgument(PKV_ERR_INVALID, "append_quant: new rows must be [T][H][D], K and V alike")
+    if slot_mapping.shape != (k_new.shape[0],):
+        raise InvalidArgument(PKV_ERR_INVALID, "append_quant: slot_mapping must be [T]")
+    return [_dev(k_new, "k_new"), _dev(v_new, "v_new"), k_new.shape[0],
+            _dev(slot_mapping, "slot_mapping", torch.int64, pinned_ok=True), *pools, nb, bs, h, d,
+            _dtype_code(k_new), _fmt_code(cache_dtype), _stream(stream)]
+
+
+def pkv_append_quant(k_new, v_new, slot_mapping, k_cache, v_cache, k_scales, v_scales, cache_dtype,
+                     stream=None) -> None:
+    """Quantise rows ``k_new[t]``/``v_new[t]`` ([T][H][D], f32/f16/bf16) into 8-bit codes
+    and per-(token, head) scales at flat slot ``slot_mapping[t]``."""
+    _check(_lib.pkv_append_quant(*_append_quant_args(k_new, v_new, slot_mapping, k_cache, v_cache, k_scales,
+                                                     v_scales, cache_dtype, stream)))
+
+
+def _decode_quant_args(out, q, k_cache, v_cache, k_scales, v_scales, block_tables, seq_lens, max_seq_len,
+                       cache_dtype, scale, work_groups, workspace, stream):
+    torch = _torch()
+    pools, (nb, bs, h, d) = _q8_pools(k_cache, v_cache, k_scales, v_scales, "attention_decode_quant")
+    batch = q.shape[0]
+    if q.shape != (batch, h, d) or out.shape != q.shape or out.dtype != q.dtype:
+        raise InvalidArgument(PKV_ERR_INVALID, "attention_decode_quant: q and out must be [B][H][D], one dtype")
+    if block_tables.dim() != 2 or block_tables.shape[0] != batch or seq_lens.shape != (batch,):
+        raise InvalidArgument(PKV_ERR_INVALID, "attention_decode_quant: tables must be [B][max_blocks], lens [B]")
+    code = _fmt_code(cache_dtype)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if workspace is None:
+        workspace = decode_workspace(max(batch, 1), h, d, cache_dtype, work_groups, q.device)
+    args = [_dev(out, "out"), _dev(q, "q"), *pools,
+            _dev(block_tables, "block_tables", torch.int32, pinned_ok=True), block_tables.shape[1],
+            _dev(seq_lens, "seq_lens", torch.int32, pinned_ok=True), int(max_seq_len), batch, h, d, bs, nb,
+            float(scale), _dtype_code(q), code, int(work_groups), _dev(workspace, "workspace"),
+            workspace.numel() * workspace.element_size(), _stream(stream)]
+    return args, workspace
+
+
+def pkv_attention_decode_quant(out, q, k_cache, v_cache, k_scales, v_scales, block_tables, seq_lens, max_seq_len,
+                               cache_dtype, scale=None, work_groups=0, workspace=None, stream=None) -> None:
+    """Decode attention of ``q`` over an 8-bit paged cache (dequantised in the kernel); writes ``out``."""
+    if q.shape[0] == 0:
+        return
+    args, _ = _decode_quant_args(out, q, k_cache, v_cache, k_scales, v_scales, block_tables, seq_lens,
+                                 max_seq_len, cache_dtype, scale, work_groups, workspace, stream)
+    _check(_lib.pkv_attention_decode_quant(*args))
+
+
+class PreparedDecodeQuant(PreparedDecode):
+    """A pkv_attention_decode_quant call checked once; ``launch(q, out)`` swaps q/out."""
+
+    def __init__(self, out, q, k_cache, v_cache, k_scales, v_scales, block_tables, seq_lens, max_seq_len,
+                 cache_dtype, scale=None, work_groups=0, workspace=None, stream=None):  # noqa: D107
+        self._args, ws = _decode_quant_args(out, q, k_cache, v_cache, k_scales, v_scales, block_tables, seq_lens,
+                                            max_seq_len, cache_dtype, scale, work_groups, workspace, stream)
+        self._keep = (k_cache, v_cache, k_scales, v_scales, block_tables, seq_lens, ws)
+        self._shape, self._dtype = tuple(q.shape), q.dtype
+        self._fn = _lib.pkv_attention_decode_quant
+
+    def set_metadata(self, block_tables, seq_lens) -> None:
+        torch = _torch()
+        if tuple(block_tables.shape) != (self._shape[0], self._args[7]) or tuple(seq_lens.shape) != (self._shape[0],):
+            raise InvalidArgument(PKV_ERR_INVALID, "prepared decode: metadata shapes differ")
+        self._args[6] = _dev(block_tables, "block_tables", torch.int32, pinned_ok=True)
+        self._args[8] = _dev(seq_lens, "seq_lens", torch.int32, pinned_ok=True)
+        self._meta = (block_tables, seq_lens)
+
+
+class PreparedAppendQuant(PreparedDecode):
+    """A pkv_append_quant call checked once; ``launch(k_new, v_new)`` swaps the new rows."""
+
+    def __init__(self, k_new, v_new, slot_mapping, k_cache, v_cache, k_scales, v_scales, cache_dtype,
+                 stream=None):  # noqa: D107
+        self._args = _append_quant_args(k_new, v_new, slot_mapping, k_cache, v_cache, k_scales, v_scales,
+                                        cache_dtype, stream)
+        self._keep = (slot_mapping, k_cache, v_cache, k_scales, v_scales)
+        self._shape, self._dtype = tuple(k_new.shape), k_new.dtype
+        self._fn = _lib.pkv_append_quant
+
+    def launch(self, k_new=None, v_new=None) -> None:
+        if k_new is not None:
+            self._swap(0, k_new, "k_new")
+        if v_new is not None:
+            self._swap(1, v_new, "v_new")
+        _check(self._fn(*self._args))
+
+
 __all__ = [
     "BlockAllocator", "PkvError", "OutOfBlocks", "InvalidArgument", "pkv_append", "pkv_copy_blocks",
     "pkv_attention_decode", "pkv_decode_workspace_bytes", "pkv_decode_work_groups",
     "decode_workspace", "PreparedDecode", "PreparedAppend", "version", "LIB_PATH",
+    "pkv_append_quant", "pkv_attention_decode_quant", "PreparedDecodeQuant", "PreparedAppendQuant",
+    "CACHE_FORMATS",
 ]

@@ -1,0 +1,701 @@
+// Device code shared by the 16/32-bit and the 8-bit K/V paths of libpkv
+// (gfx950, CDNA4): element helpers, lane reductions, the stream-K decode
+// attention kernel (generic over how a chunk of K/V rows is loaded and
+// scored), the merge kernel for sequences split across work-groups, and the
+// host-side launch geometry.
+//
+// Pool layout (K and V alike): [num_blocks][block_size][num_heads][head_dim].
+// One token's row for all heads is contiguous, so the rows a wavefront needs
+// for a group of adjacent heads at one token form one contiguous 1 KiB run.
+//
+// Decode attention is a memory-bound matrix-vector product: per (token, head)
+// it reads 2 * head_dim * element bytes and does about 4 * head_dim flops,
+// far below the FP32 vector ridge point, so it runs on the vector ALUs, not
+// MFMA.  Work split:
+//   - each wavefront takes HPW adjacent heads, and each head's row is spread
+//     over LPH lanes holding 16 bytes each (one global_load_dwordx4 per lane
+//     per token fetches K, one fetches V);
+//   - q.k is reduced across the LPH lanes with DPP row permutes;
+//   - the softmax runs online over chunks of 8 tokens (running max m, sum l,
+//     weighted value accumulator) in base 2 with log2(e) folded into the
+//     scale;
+//   - work-groups take equal ranges of all sequences' chunks (stream-K); a
+//     sequence cut by range boundaries leaves one (m, l, acc) piece per range
+//     in the workspace and the merge kernel combines them.
+// Block-table entries are wavefront-uniform; every id is range-checked before
+// it forms an address.
+//
+// Everything here has internal linkage: each source that includes this file
+// gets its own copy of the templates it instantiates.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "status.h"
+
+namespace {
+
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef __bf16 bf162v __attribute__((ext_vector_type(2)));
+
+struct alignas(16) Vec16 {
+  uint32_t w[4];
+};
+
+constexpr int kChunk = 8;        // tokens per online-softmax step
+constexpr int kMaxWaves = 16;    // wavefronts per work-group at most (any format)
+
+__host__ __device__ constexpr int dtype_bytes(int dt) {
+  return dt == PKV_F32 ? 4 : (dt == PKV_F16 || dt == PKV_BF16) ? 2 : 1;
+}
+
+__host__ __device__ constexpr bool is_8bit(int dt) { return dt == PKV_I8 || dt == PKV_FP8_E4M3; }
+
+// ---- element helpers -------------------------------------------------------
+
+template <int DT>
+__device__ __forceinline__ float dot16(const Vec16& q, const Vec16& k, float acc) {
+  if constexpr (DT == PKV_F32) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc = fmaf(__uint_as_float(q.w[i]), __uint_as_float(k.w[i]), acc);
+  } else if constexpr (DT == PKV_F16) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2v, q.w[i]), __builtin_bit_cast(half2v, k.w[i]), acc, false);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf162v, q.w[i]), __builtin_bit_cast(bf162v, k.w[i]),
+                                            acc, false);
+  }
+  return acc;
+}
+
+template <int DT>
+__device__ __forceinline__ void unpack16(const Vec16& v, float* out) {
+  if constexpr (DT == PKV_F32) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) out[i] = __uint_as_float(v.w[i]);
+  } else if constexpr (DT == PKV_F16) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      half2v h = __builtin_bit_cast(half2v, v.w[i]);
+      out[2 * i] = static_cast<float>(h.x);
+      out[2 * i + 1] = static_cast<float>(h.y);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      out[2 * i] = __uint_as_float(v.w[i] << 16);
+      out[2 * i + 1] = __uint_as_float(v.w[i] & 0xffff0000u);
+    }
+  }
+}
+
+// float -> bfloat16 bits, round to nearest even (quiet NaN kept quiet).
+__device__ __forceinline__ uint32_t bf16_rne(float x) {
+  uint32_t u = __float_as_uint(x);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t f16_bits(float x) {
+  _Float16 h = static_cast<_Float16>(x);  // v_cvt_f16_f32: round to nearest even
+  return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, h));
+}
+
+// Packs N floats (N = 16 / dtype bytes) into 16 bytes of storage.
+template <int DT>
+__device__ __forceinline__ Vec16 pack16(const float* in) {
+  Vec16 r;
+  if constexpr (DT == PKV_F32) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r.w[i] = __float_as_uint(in[i]);
+  } else if constexpr (DT == PKV_F16) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r.w[i] = f16_bits(in[2 * i]) | (f16_bits(in[2 * i + 1]) << 16);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r.w[i] = bf16_rne(in[2 * i]) | (bf16_rne(in[2 * i + 1]) << 16);
+  }
+  return r;
+}
+
+// Stores N floats as N elements of DT at p (16-byte aligned; N * bytes a
+// multiple of 16).
+template <int DT, int N>
+__device__ __forceinline__ void store_row(uint8_t* p, const float* in) {
+  constexpr int per = 16 / dtype_bytes(DT);
+  static_assert(N % per == 0, "whole 16-byte stores only");
+#pragma unroll
+  for (int k = 0; k < N / per; ++k) reinterpret_cast<Vec16*>(p)[k] = pack16<DT>(in + k * per);
+}
+
+// DPP lane permutes inside a row of 16 lanes.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+
+constexpr int kDppXor1 = 0xB1;         // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;         // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;  // lane i <- lane 7-i within 8
+constexpr int kDppMirror = 0x140;      // lane i <- lane 15-i within 16
+
+// Sum over each aligned group of N lanes (N = 4, 8, 16 or 32); every lane of
+// the group receives the total.
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+  x += dpp<kDppXor1>(x);
+  x += dpp<kDppXor2>(x);
+  if constexpr (N >= 8) x += dpp<kDppHalfMirror>(x);
+  if constexpr (N >= 16) x += dpp<kDppMirror>(x);
+  if constexpr (N >= 32) x += __shfl_xor(x, 16, 64);
+  return x;
+}
+
+// Maximum over each aligned group of N lanes (N = 4, 8 or 16).
+template <int N>
+__device__ __forceinline__ float group_max(float x) {
+  x = fmaxf(x, dpp<kDppXor1>(x));
+  x = fmaxf(x, dpp<kDppXor2>(x));
+  if constexpr (N >= 8) x = fmaxf(x, dpp<kDppHalfMirror>(x));
+  if constexpr (N >= 16) x = fmaxf(x, dpp<kDppMirror>(x));
+  static_assert(N <= 16, "groups within one DPP row");
+  return x;
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) x = fmaxf(x, __shfl_xor(x, off, 64));
+  return x;
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
+  return x;
+}
+
+// ---- decode attention ------------------------------------------------------
+//
+// Stream-K schedule.  Every (sequence, head slice) is cut into chunks of
+// kChunk logical tokens (the last chunk of a sequence may be short); the
+// chunks of all sequences are laid end to end and the G work-groups of the
+// launch take equal contiguous ranges of them.  Each work-group therefore
+// reads the same number of K/V bytes (to within one chunk) and pays its
+// start-up latency once, however ragged the lengths are.  A range that holds
+// a whole sequence writes the output directly; a sequence cut by range
+// boundaries leaves one partial softmax state (m, l, acc) per piece, and a
+// small merge kernel combines the pieces.  Cut points depend only on logical
+// positions, so the result does not depend on where blocks sit physically.
+
+constexpr int kMaxVirtual = 8190;   // sequences x head slices per launch (two LDS prefix arrays <= 64 KiB)
+constexpr int kTableWindow = 64;    // block ids held in registers at a time (one per lane)
+constexpr int kMergeWaves = 4;      // heads per merge work-group
+
+struct DecodeArgs {
+  void* out;
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* k_scales;  // 8-bit caches: [num_blocks][H][block_size] per-row scales (else unused)
+  const float* v_scales;
+  const int32_t* tables;
+  const int32_t* lens;
+  float* ws_acc;      // [partial slot][H][D]
+  float2* ws_ml;      // [partial slot][H]: running max (log2 units), running sum
+  int32_t* ws_plan;   // [virtual sequence][2]: first partial slot, number of pieces (0 = written directly)
+  int32_t max_blocks;
+  int32_t max_seq_len;
+  int32_t batch;
+  int32_t num_heads;
+  int32_t num_blocks;
+  int32_t groups_y;         // head slices (work-groups per sequence piece)
+  int32_t waves_per_group;  // head groups (wavefronts) per work-group
+  int32_t heads_per_wave;
+  int32_t block_size;
+  float scale_log2;         // softmax scale * log2(e)
+};
+
+// Exclusive prefix sums of f(0..n-1) into out[0..n] (out[n] = total), over
+// the whole work-group; every thread must call it.  Thread t sums a
+// contiguous run, runs are scanned across lanes and then across wavefronts.
+template <typename F>
+__device__ void block_exclusive_scan(F f, int n, int32_t* out, int32_t* s_waves) {
+  const int nt = blockDim.x;
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int run = (n + nt - 1) / nt;
+  const int i0 = min(n, t * run);
+  const int i1 = min(n, i0 + run);
+  int32_t local = 0;
+  for (int i = i0; i < i1; ++i) local += f(i);
+  int32_t x = local;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int32_t y = __shfl_up(x, off, 64);
+    if (lane >= off) x += y;
+  }
+  if (lane == 63) s_waves[t >> 6] = x;
+  __syncthreads();
+  if (t == 0) {
+    int32_t acc = 0;
+    for (int w = 0; w < nt / 64; ++w) {
+      const int32_t v = s_waves[w];
+      s_waves[w] = acc;
+      acc += v;
+    }
+    s_waves[kMaxWaves] = acc;
+  }
+  __syncthreads();
+  int32_t pre = x - local + s_waves[t >> 6];
+  for (int i = i0; i < i1; ++i) {
+    out[i] = pre;
+    pre += f(i);
+  }
+  if (t == 0) out[n] = s_waves[kMaxWaves];
+  __syncthreads();
+}
+
+// Index of the work-group whose chunk range [c*G/W...) holds chunk c.
+__device__ __forceinline__ int range_owner(int64_t c, int64_t nwg, int64_t total) {
+  return static_cast<int>(((c + 1) * nwg - 1) / total);
+}
+
+template <int BS>
+__device__ __forceinline__ bool length_ok(int L, const DecodeArgs& a) {
+  return L >= 0 && L <= a.max_seq_len && static_cast<int64_t>(L) <= static_cast<int64_t>(a.max_blocks) * BS;
+}
+
+// The decode kernel.  KV (a format policy) supplies:
+//   QT, KB, EPL, kMaxWaves       q/out dtype, cache bytes per element, cache
+//                                elements per lane (16 / KB), launch bound;
+//   QReg load_q(const uint8_t*)  this lane's EPL query elements;
+//   chunk<D, BS, LPH>(...)       load kChunk rows of K/V from block `blk`
+//                                starting at in-block position pos0 and fold
+//                                them into the online softmax state.
+template <class KV, int D, int BS>
+__global__ void __launch_bounds__(KV::kMaxWaves * 64) decode_kernel(DecodeArgs a) {
+  constexpr int EPL = KV::EPL;
+  constexpr int LPH = D / EPL;   // lanes holding one head's row
+  constexpr int HPW = 64 / LPH;  // heads per wavefront
+  constexpr int KB = KV::KB;
+  constexpr int QB = dtype_bytes(KV::QT);
+  static_assert(BS % kChunk == 0, "a chunk of tokens must sit inside one block");
+  static_assert(KV::kMaxWaves <= kMaxWaves, "wave count bound");
+  using Elem = uint8_t;          // addresses are formed in bytes
+
+  extern __shared__ int32_t s_dyn[];
+  __shared__ int32_t s_waves[kMaxWaves + 1];
+  const int nv = a.batch * a.groups_y;
+  int32_t* s_pref = s_dyn;           // [nv + 1]: first chunk of each virtual sequence
+  int32_t* s_part = s_dyn + nv + 1;  // [nv + 1]: first partial slot of each virtual sequence
+  const int g = blockIdx.x;
+
+  // 1. chunk counts of every (head slice, sequence); bad lengths count zero.
+  block_exclusive_scan(
+      [&](int v) {
+        const int L = a.lens[v % a.batch];
+        return length_ok<BS>(L, a) ? (L + kChunk - 1) / kChunk : 0;
+      },
+      nv, s_pref, s_waves);
+  const int64_t total = s_pref[nv];
+  // Ranges are dealt over min(grid, chunks) work-groups so none is empty.
+  const int64_t nwg = total < gridDim.x ? total : static_cast<int64_t>(gridDim.x);
+  // 2. pieces of every sequence the ranges cut; slots for their partials.
+  auto pieces = [&](int v) -> int32_t {
+    const int64_t c0 = s_pref[v], c1 = s_pref[v + 1];
+    if (c1 == c0) return 0;
+    const int k = range_owner(c1 - 1, nwg, total) - range_owner(c0, nwg, total) + 1;
+    return k > 1 ? k : 0;
+  };
+  block_exclusive_scan(pieces, nv, s_part, s_waves);
+  if (g == 0) {
+    for (int v = threadIdx.x; v < nv; v += blockDim.x) {
+      a.ws_plan[2 * v] = s_part[v];
+      a.ws_plan[2 * v + 1] = s_part[v + 1] - s_part[v];
+    }
+  }
+
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int r = lane / LPH;
+  const int c = lane % LPH;
+  const int64_t row_bytes = static_cast<int64_t>(a.num_heads) * D * KB;    // one token's cache row
+  const int64_t q_row_bytes = static_cast<int64_t>(a.num_heads) * D * QB;  // one sequence's q / out row
+
+  // 3. sequences with no chunks (length 0, or a length the table cannot
+  // hold) are written here: zero rows, or NaN rows for an invalid length.
+  for (int v = g; v < nv; v += gridDim.x) {
+    if (s_pref[v + 1] != s_pref[v]) continue;
+    const int b = v % a.batch, y = v / a.batch;
+    const int h = (y * a.waves_per_group + wave) * HPW + r;
+    if ((y * a.waves_per_group + wave) * HPW >= a.num_heads || h >= a.num_heads) continue;
+    const float fill = a.lens[b] == 0 ? 0.f : __builtin_nanf("");
+    float f[EPL];
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) f[e] = fill;
+    store_row<KV::QT, EPL>(static_cast<Elem*>(a.out) + b * q_row_bytes + (h * D + c * EPL) * QB, f);
+  }
+  if (total == 0) return;
+
+  // 4. this work-group's chunks [first, last)
+  if (g >= nwg) return;
+  const int64_t first = g * total / nwg;
+  const int64_t last = (g + 1) * total / nwg;
+  if (first >= last) return;
+  int v;
+  {  // virtual sequence holding chunk `first`: s_pref[v] <= first < s_pref[v + 1]
+    int lo = 0, hi = nv;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (s_pref[mid] <= first) lo = mid; else hi = mid;
+    }
+    v = lo;
+    while (s_pref[v + 1] == s_pref[v]) ++v;
+  }
+
+  for (int64_t cur = first; cur < last;) {
+    const int64_t seq0 = s_pref[v], seq1 = s_pref[v + 1];
+    const int64_t seg_end = last < seq1 ? last : seq1;
+    const int b = v % a.batch, y = v / a.batch;
+    const int hg = y * a.waves_per_group + wave;
+    const int h = hg * HPW + r;
+    const bool whole = cur == seq0 && seg_end == seq1;
+    if (hg * HPW < a.num_heads) {
+      const bool head_ok = h < a.num_heads;
+      const int hl = head_ok ? h : a.num_heads - 1;  // clamped head for loads
+      const int e0 = hl * D + c * EPL;                // this lane's first element of the row
+      const Elem* kp = static_cast<const Elem*>(a.k) + e0 * KB;
+      const Elem* vp = static_cast<const Elem*>(a.v) + e0 * KB;
+      const int L = a.lens[b];
+      const int t_begin = static_cast<int>(cur - seq0) * kChunk;
+      const int t_end = min(L, static_cast<int>(seg_end - seq0) * kChunk);
+      const int32_t* trow = a.tables + static_cast<int64_t>(b) * a.max_blocks;
+      const typename KV::QReg qv = KV::load_q(static_cast<const Elem*>(a.q) + b * q_row_bytes + e0 * QB);
+
+      float m = -INFINITY, l = 0.f;
+      float acc[EPL];
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
+      bool bad_block = false;
+      int win = -kTableWindow;  // first block index held in `tbl`
+      int32_t tbl = 0;
+      for (int t0 = t_begin; t0 < t_end; t0 += kChunk) {
+        const int j = t0 / BS;
+        if (j - win >= kTableWindow) {  // next window of block ids, one per lane, each checked once
+          win = j;
+          const int nb = min(kTableWindow, (t_end - 1) / BS + 1 - win);
+          tbl = lane < nb ? trow[win + lane] : 0;
+          const bool bad = lane < nb && static_cast<uint32_t>(tbl) >= static_cast<uint32_t>(a.num_blocks);
+          bad_block |= __any(bad);
+          if (bad) tbl = 0;
+        }
+        const int32_t blk = __builtin_amdgcn_readlane(tbl, j - win);
+        // rows past the segment repeat its last row (masked)
+        KV::template chunk<D, BS, LPH>(qv, a, kp, vp, blk, t0 % BS, hl, row_bytes, t_end - 1 - t0, t_end - t0, m, l,
+                                       acc);
+      }
+      if (bad_block) l = __builtin_nanf("");
+      if (head_ok) {
+        if (whole) {
+          const float inv = 1.f / l;
+          float o[EPL];
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) o[e] = acc[e] * inv;
+          store_row<KV::QT, EPL>(static_cast<Elem*>(a.out) + b * q_row_bytes + e0 * QB, o);
+        } else {
+          const int piece = g - range_owner(seq0, nwg, total);
+          const int64_t slot = static_cast<int64_t>(s_part[v] + piece) * a.num_heads + h;
+          float* dst = a.ws_acc + slot * D + c * EPL;
+#pragma unroll
+          for (int e = 0; e < EPL; e += 4)
+            *reinterpret_cast<float4*>(dst + e) = make_float4(acc[e], acc[e + 1], acc[e + 2], acc[e + 3]);
+          if (c == 0) a.ws_ml[slot] = make_float2(m, l);
+        }
+      }
+    }
+    cur = seg_end;
+    if (cur < last) {
+      ++v;
+      while (s_pref[v + 1] == s_pref[v]) ++v;
+    }
+  }
+}
+
+// Merges the pieces of every cut sequence:
+//   M = max_i m_i,  S = sum_i l_i 2^(m_i - M),  out = sum_i acc_i 2^(m_i - M) / S.
+// One wavefront per (sequence, head).  Lane i holds piece i's (m, l); the
+// lanes also split into groups of D/4 lanes that hold whole piece rows as
+// float4, kMergeRows rows per group.  Every load of a batch of pieces is
+// issued before any of them is used, so a batch costs one memory round trip;
+// the weights reach the row holders by lane shuffles.
+constexpr int kMergeRows = 8;
+
+template <int DT, int D>
+__global__ void __launch_bounds__(kMergeWaves * 64) decode_merge_kernel(DecodeArgs a) {
+  constexpr int LPR = D / 4;     // lanes per piece row (float4 each)
+  constexpr int RPW = 64 / LPR;  // rows per wavefront instruction
+  constexpr int BATCH = RPW * kMergeRows;
+  static_assert(BATCH <= 64, "a batch of pieces must fit one (m, l) per lane");
+  const int v = blockIdx.y;
+  const int first = a.ws_plan[2 * v];
+  const int count = a.ws_plan[2 * v + 1];
+  if (count == 0) return;
+  const int b = v % a.batch, y = v / a.batch;
+  const int slice_lo = y * a.waves_per_group * a.heads_per_wave;
+  const int slice_hi = min(a.num_heads, slice_lo + a.waves_per_group * a.heads_per_wave);
+  const int h = slice_lo + __builtin_amdgcn_readfirstlane(blockIdx.x * kMergeWaves + (threadIdx.x >> 6));
+  if (h >= slice_hi) return;
+  const int lane = threadIdx.x & 63;
+  const int grp = lane / LPR;
+  const int sub = lane % LPR;
+  const float2* ml = a.ws_ml + static_cast<int64_t>(first) * a.num_heads + h;  // stride num_heads
+  const float* accp = a.ws_acc + (static_cast<int64_t>(first) * a.num_heads + h) * D + sub * 4;
+  const int64_t row_stride = static_cast<int64_t>(a.num_heads) * D;
+
+  float mx = -INFINITY;   // running max over batches (wave-uniform)
+  float sum = 0.f;        // running sum, scaled to mx
+  float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int i0 = 0; i0 < count; i0 += BATCH) {
+    const int n = min(BATCH, count - i0);
+    // issue every load of the batch first
+    const float2 mine = lane < n ? ml[static_cast<int64_t>(i0 + lane) * a.num_heads] : make_float2(-INFINITY, 0.f);
+    float4 rows[kMergeRows];
+#pragma unroll
+    for (int k = 0; k < kMergeRows; ++k) {
+      const int i = grp + k * RPW;
+      rows[k] = i < n ? *reinterpret_cast<const float4*>(accp + static_cast<int64_t>(i0 + i) * row_stride)
+                      : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    const float bmx = wave_max(mine.x);
+    const float nmx = fmaxf(mx, bmx);
+    const float rescale = __builtin_amdgcn_exp2f(mx - nmx);  // 0 on the first batch
+    const float w = lane < n ? __builtin_amdgcn_exp2f(mine.x - nmx) : 0.f;
+    sum = sum * rescale + wave_sum(mine.y * w);
+    o.x *= rescale;
+    o.y *= rescale;
+    o.z *= rescale;
+    o.w *= rescale;
+#pragma unroll
+    for (int k = 0; k < kMergeRows; ++k) {
+      const float wk = __shfl(w, grp + k * RPW, 64);
+      o.x = fmaf(rows[k].x, wk, o.x);
+      o.y = fmaf(rows[k].y, wk, o.y);
+      o.z = fmaf(rows[k].z, wk, o.z);
+      o.w = fmaf(rows[k].w, wk, o.w);
+    }
+    mx = nmx;
+  }
+#pragma unroll
+  for (int off = LPR; off < 64; off <<= 1) {
+    o.x += __shfl_xor(o.x, off, 64);
+    o.y += __shfl_xor(o.y, off, 64);
+    o.z += __shfl_xor(o.z, off, 64);
+    o.w += __shfl_xor(o.w, off, 64);
+  }
+  if (grp != 0) return;
+  const float inv = 1.f / sum;
+  const int64_t out_idx = (static_cast<int64_t>(b) * a.num_heads + h) * D + sub * 4;
+  if constexpr (DT == PKV_F32) {
+    *reinterpret_cast<float4*>(static_cast<float*>(a.out) + out_idx) =
+        make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv);
+  } else {
+    uint32_t lo, hi;
+    if constexpr (DT == PKV_F16) {
+      lo = f16_bits(o.x * inv) | (f16_bits(o.y * inv) << 16);
+      hi = f16_bits(o.z * inv) | (f16_bits(o.w * inv) << 16);
+    } else {
+      lo = bf16_rne(o.x * inv) | (bf16_rne(o.y * inv) << 16);
+      hi = bf16_rne(o.z * inv) | (bf16_rne(o.w * inv) << 16);
+    }
+    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + out_idx) = make_uint2(lo, hi);
+  }
+}
+
+// ---- host helpers ----------------------------------------------------------
+
+inline int32_t ceil_div(int64_t a, int64_t b) { return static_cast<int32_t>((a + b - 1) / b); }
+
+inline bool supported_geometry(int32_t head_dim, int32_t block_size) {
+  return (head_dim == 64 || head_dim == 128) && (block_size == 8 || block_size == 16 || block_size == 32);
+}
+
+inline bool is_16_32(pkv_dtype dt) { return dt == PKV_F32 || dt == PKV_F16 || dt == PKV_BF16; }
+
+// Wavefronts a work-group may hold for a cache format: the 8-bit kernels keep
+// more registers per lane (16 elements per 16-byte load), so they launch at
+// most 8 wavefronts per work-group.
+inline int max_waves_for(pkv_dtype cache_dtype) { return is_8bit(cache_dtype) ? 8 : kMaxWaves; }
+
+inline int heads_per_wave(int32_t head_dim, pkv_dtype cache_dtype) {
+  const int epl = 16 / dtype_bytes(cache_dtype);
+  return 64 / (head_dim / epl);
+}
+
+// Work-groups per compute unit of the automatic choice.  Measured on MI355X
+// (7B-shaped layer): for 16-bit caches, 256 work-groups of 8 wavefronts read
+// at 5.7 TB/s; 512 at 5.4 TB/s, 1024 at 5.1 TB/s — fewer, longer streams keep
+// more DRAM pages open per request.  8-bit caches carry twice the elements
+// per byte and run 4 wavefronts per work-group for 32 heads, so they take two
+// work-groups per compute unit to keep the same wavefronts resident.
+inline int work_groups_per_cu(pkv_dtype cache_dtype) { return is_8bit(cache_dtype) ? 2 : 1; }
+
+// Work-groups of the automatic choice on the current device.
+inline int32_t auto_work_groups(pkv_dtype cache_dtype) {
+  static int32_t cus_cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return pkv::fail(PKV_ERR_HIP, "no current HIP device");
+  int cus = dev < 64 ? cus_cached[dev] : 0;
+  if (cus <= 0) {
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+      return pkv::fail(PKV_ERR_HIP, "cannot query the compute-unit count");
+    if (dev < 64) cus_cached[dev] = cus;
+  }
+  return cus * work_groups_per_cu(cache_dtype);
+}
+
+inline int check_launch(const char* what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return pkv::fail(PKV_ERR_HIP, "%s: launch failed: %s", what, hipGetErrorString(e));
+  return PKV_OK;
+}
+
+// Work-group shape: head groups (one wavefront each) are split into
+// groups_y slices of at most max_waves wavefronts.
+struct Shape {
+  int groups;    // head groups = ceil(H / heads per wavefront)
+  int groups_y;  // head slices
+  int wpg;       // wavefronts per work-group
+  int hpw;       // heads per wavefront
+};
+
+inline Shape decode_shape(int32_t num_heads, int32_t head_dim, pkv_dtype cache_dtype) {
+  Shape sh;
+  sh.hpw = heads_per_wave(head_dim, cache_dtype);
+  sh.groups = ceil_div(num_heads, sh.hpw);
+  sh.groups_y = ceil_div(sh.groups, max_waves_for(cache_dtype));
+  sh.wpg = ceil_div(sh.groups, sh.groups_y);
+  return sh;
+}
+
+// Workspace: [plan: virtual sequences x 2 int32][acc: 2G slots x H x D f32][(m, l): 2G slots x H]
+// (a cut at each of the G-1 range boundaries adds at most one piece and one
+// cut sequence, so the pieces of all cut sequences number at most 2(G-1)).
+struct Layout {
+  size_t plan, acc, ml, total;
+};
+
+inline Layout workspace_layout(int32_t batch, int32_t num_heads, int32_t head_dim, pkv_dtype cache_dtype,
+                               int32_t wg) {
+  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+  const Shape sh = decode_shape(num_heads, head_dim, cache_dtype);
+  const int64_t per_launch = kMaxVirtual / sh.groups_y;
+  const size_t nv = static_cast<size_t>(batch < per_launch ? batch : per_launch) * sh.groups_y;
+  const size_t slots = 2 * static_cast<size_t>(wg) * num_heads;
+  Layout w{};
+  w.plan = 0;
+  w.acc = up(nv * 2 * sizeof(int32_t));
+  w.ml = w.acc + up(slots * head_dim * sizeof(float));
+  w.total = w.ml + up(slots * sizeof(float2));
+  return w;
+}
+
+template <class KV, int D, int BS>
+void launch_decode(const DecodeArgs& a, int wg, hipStream_t stream) {
+  const size_t lds = 2 * (static_cast<size_t>(a.batch) * a.groups_y + 1) * sizeof(int32_t);
+  hipLaunchKernelGGL((decode_kernel<KV, D, BS>), dim3(wg), dim3(a.waves_per_group * 64), lds, stream, a);
+  const int slice_heads = a.waves_per_group * a.heads_per_wave;
+  dim3 mgrid(ceil_div(slice_heads, kMergeWaves), a.batch * a.groups_y);
+  hipLaunchKernelGGL((decode_merge_kernel<KV::QT, D>), mgrid, dim3(kMergeWaves * 64), 0, stream, a);
+}
+
+template <class KV, int D>
+void launch_decode_bs(const DecodeArgs& a, int wg, int32_t bs, hipStream_t stream) {
+  switch (bs) {
+    case 8: launch_decode<KV, D, 8>(a, wg, stream); break;
+    case 16: launch_decode<KV, D, 16>(a, wg, stream); break;
+    default: launch_decode<KV, D, 32>(a, wg, stream); break;
+  }
+}
+
+template <class KV>
+void launch_decode_d(const DecodeArgs& a, int wg, int32_t bs, int32_t d, hipStream_t stream) {
+  if (d == 64)
+    launch_decode_bs<KV, 64>(a, wg, bs, stream);
+  else
+    launch_decode_bs<KV, 128>(a, wg, bs, stream);
+}
+
+// Checks of the scalar arguments of a decode call (made before anything else
+// so that an empty batch still reports them).
+inline int check_decode_scalars(float scale, int32_t num_work_groups) {
+  if (!(std::isfinite(scale))) return pkv::fail(PKV_ERR_INVALID, "attention_decode: scale must be finite");
+  if (num_work_groups < 0 || num_work_groups > (1 << 20))
+    return pkv::fail(PKV_ERR_INVALID, "attention_decode: num_work_groups %d out of range", num_work_groups);
+  return PKV_OK;
+}
+
+// Host-side checks and set-up shared by both decode entry points; fills
+// everything in `a` except the per-slice pointers and batch.  Returns the
+// work-group count (> 0) or a negative status.
+inline int prepare_decode(DecodeArgs& a, const void* q, const void* k_cache, const void* v_cache,
+                          const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                          int32_t max_seq_len, int32_t batch, int32_t num_heads, int32_t head_dim, int32_t block_size,
+                          int32_t num_blocks, float scale, pkv_dtype cache_dtype, int32_t num_work_groups,
+                          void* workspace, size_t workspace_bytes, const void* out) {
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !seq_lens)
+    return pkv::fail(PKV_ERR_INVALID, "attention_decode: null pointer");
+  const int32_t wg = num_work_groups > 0 ? num_work_groups : auto_work_groups(cache_dtype);
+  if (wg <= 0) return wg;
+  const Layout ws = workspace_layout(batch, num_heads, head_dim, cache_dtype, wg);
+  if (workspace == nullptr || workspace_bytes < ws.total)
+    return pkv::fail(PKV_ERR_INVALID, "attention_decode: workspace of %zu bytes needed, %zu given", ws.total,
+                     workspace_bytes);
+  const Shape sh = decode_shape(num_heads, head_dim, cache_dtype);
+  char* base = static_cast<char*>(workspace);
+  a.k = k_cache;
+  a.v = v_cache;
+  a.k_scales = nullptr;
+  a.v_scales = nullptr;
+  a.ws_plan = reinterpret_cast<int32_t*>(base + ws.plan);
+  a.ws_acc = reinterpret_cast<float*>(base + ws.acc);
+  a.ws_ml = reinterpret_cast<float2*>(base + ws.ml);
+  a.max_blocks = max_blocks_per_seq;
+  a.max_seq_len = max_seq_len;
+  a.num_heads = num_heads;
+  a.num_blocks = num_blocks;
+  a.groups_y = sh.groups_y;
+  a.waves_per_group = sh.wpg;
+  a.heads_per_wave = sh.hpw;
+  a.block_size = block_size;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  return wg;
+}
+
+// Runs `launch(a)` over slices of the batch small enough for the on-chip
+// prefix arrays; the slices run one after another on the stream and share the
+// workspace.
+template <class Launch>
+int run_sliced(DecodeArgs a, void* out, const void* q, const int32_t* block_tables, int32_t max_blocks_per_seq,
+               const int32_t* seq_lens, int32_t batch, int64_t q_row_bytes, Launch launch) {
+  const int32_t per_launch = kMaxVirtual / a.groups_y;
+  for (int32_t b0 = 0; b0 < batch; b0 += per_launch) {
+    a.batch = batch - b0 < per_launch ? batch - b0 : per_launch;
+    a.out = static_cast<char*>(out) + b0 * q_row_bytes;
+    a.q = static_cast<const char*>(q) + b0 * q_row_bytes;
+    a.tables = block_tables + static_cast<int64_t>(b0) * max_blocks_per_seq;
+    a.lens = seq_lens + b0;
+    launch(a);
+    const int st = check_launch("attention_decode");
+    if (st != PKV_OK) return st;
+  }
+  return PKV_OK;
+}
+
+}  // namespace

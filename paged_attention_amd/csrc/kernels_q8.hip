@@ -1,0 +1,317 @@
+// 8-bit K/V cache (int8 or OCP FP8 E4M3): quantising scatter and decode
+// attention that dequantises inside the kernel, plus their C entry points.
+//
+// An 8-bit cache halves the bytes per token against fp16, and it changes
+// nothing else of the paging: block tables, slots and block copies are the
+// same (hnwysp.cn/news/103996 §5.4; icman.com.cn/news/78786 §1.3;
+// m.lqnn.cn/news/240480 §6.2).
+//
+// Format.  Every (token, head) row of head_dim values is stored as head_dim
+// code bytes plus one float32 scale:
+//   scale = max |x| / QMAX            (QMAX = 127 for int8, 448 for FP8 E4M3)
+//   r     = x / scale                 (IEEE float32 division)
+//   int8: code = clamp(rint(r), -127, 127)
+//   fp8:  code = E4M3 value nearest to clamp(r, -448, 448), ties to even
+// and a row of zeros stores scale 0 and zero codes.  Reading gives
+// code * scale.  Codes sit in the usual pool layout
+// [num_blocks][block_size][H][D] (one byte each); scales sit in
+// [num_blocks][H][block_size] so that a head's scales for the 8 tokens of a
+// chunk are 32 contiguous bytes.
+//
+// Decode reuses the stream-K kernel of decode_common.h with a policy whose
+// lanes hold 16 codes (one 16-byte load per lane per token for K and for V),
+// turn them into floats (v_cvt_pk_f32_fp8 for E4M3, signed byte extraction
+// for int8), fold the K scale into the score and the V scale into the
+// softmax weight.
+#include "decode_common.h"
+
+namespace {
+
+typedef float float2v __attribute__((ext_vector_type(2)));
+
+// ---- quantising scatter ----------------------------------------------------
+
+constexpr int kQuantElems = 8;   // row elements per thread
+
+template <int KT>
+__device__ __forceinline__ float qmax() {
+  return KT == PKV_I8 ? 127.f : 448.f;
+}
+
+// E4M3 code of r (finite, |r| <= 448), nearest value with ties to the even
+// code, from the float32 bit pattern: normal values keep 3 mantissa bits
+// (rounding may carry into the exponent), values below 2^-6 land on the
+// subnormal grid of 2^-9.
+__device__ __forceinline__ uint32_t e4m3_code(float r) {
+  const uint32_t sign = (__float_as_uint(r) >> 24) & 0x80u;
+  const float a = fabsf(r);
+  uint32_t mag;
+  if (a < 0.015625f) {
+    mag = static_cast<uint32_t>(rintf(a * 512.f));     // 0..8; 8 is the smallest normal
+  } else {
+    uint32_t b = __float_as_uint(a);
+    b += 0x7ffffu + ((b >> 20) & 1u);                  // round the mantissa to 3 bits, ties to even
+    mag = (b >> 20) - (120u << 3);                     // rebias the exponent: 127 -> 7
+  }
+  return sign | mag;
+}
+
+template <int KT>
+__device__ __forceinline__ uint32_t quant_code(float r) {
+  if constexpr (KT == PKV_I8) {
+    const int c = min(127, max(-127, static_cast<int>(rintf(r))));
+    return static_cast<uint32_t>(c) & 0xffu;
+  } else {
+    return e4m3_code(fminf(fmaxf(r, -448.f), 448.f));
+  }
+}
+
+// One thread per 8 elements of one (token, head) row of K (blockIdx.y = 0)
+// or V (1); the D / 8 threads of a row are adjacent lanes and find the row's
+// largest magnitude with DPP.  A row whose slot is negative or out of range
+// is skipped as a whole, so the lanes of a row are active together.
+template <int ST, int KT, int D>
+__global__ void __launch_bounds__(256) append_q8_kernel(const uint8_t* __restrict__ k_new,
+                                                        const uint8_t* __restrict__ v_new,
+                                                        const int64_t* __restrict__ slots,
+                                                        uint8_t* __restrict__ k_cache, uint8_t* __restrict__ v_cache,
+                                                        float* __restrict__ k_scales, float* __restrict__ v_scales,
+                                                        int32_t num_tokens, int32_t num_heads, int32_t block_size,
+                                                        int64_t total_slots) {
+  constexpr int R = D / kQuantElems;   // threads per row
+  constexpr int SB = dtype_bytes(ST);
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int64_t row = i / R;
+  const int part = static_cast<int>(i % R);
+  if (row >= static_cast<int64_t>(num_tokens) * num_heads) return;
+  const int64_t t = row / num_heads;
+  const int h = static_cast<int>(row % num_heads);
+  const int64_t s = slots[t];
+  if (s < 0 || s >= total_slots) return;
+  const bool is_v = blockIdx.y == 1;
+  const uint8_t* src = (is_v ? v_new : k_new) + (row * D + part * kQuantElems) * SB;
+  float x[kQuantElems];
+#pragma unroll
+  for (int k = 0; k < kQuantElems * SB / 16; ++k)
+    unpack16<ST>(reinterpret_cast<const Vec16*>(src)[k], x + k * (16 / SB));
+  float amax = 0.f;
+#pragma unroll
+  for (int e = 0; e < kQuantElems; ++e) amax = fmaxf(amax, fabsf(x[e]));
+  amax = group_max<R>(amax);
+  const float scale = amax / qmax<KT>();
+  uint32_t w0 = 0, w1 = 0;
+  if (scale > 0.f) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      w0 |= quant_code<KT>(x[e] / scale) << (8 * e);
+      w1 |= quant_code<KT>(x[e + 4] / scale) << (8 * e);
+    }
+  }
+  uint8_t* dst = (is_v ? v_cache : k_cache) + (s * num_heads + h) * D + part * kQuantElems;
+  *reinterpret_cast<uint2*>(dst) = make_uint2(w0, w1);
+  if (part == 0) {
+    float* sc = is_v ? v_scales : k_scales;
+    sc[((s / block_size) * num_heads + h) * block_size + s % block_size] = scale;
+  }
+}
+
+// ---- decode attention (8-bit caches) ---------------------------------------
+
+// Format policy of 8-bit caches: a lane holds 16 codes of a row; q (fp32,
+// fp16 or bf16) is widened to 16 floats once per sequence.
+template <int Q, int K>
+struct Q8KV {
+  static constexpr int QT = Q;
+  static constexpr int KB = 1;
+  static constexpr int EPL = 16;
+  static constexpr int kMaxWaves = 8;
+  struct QReg {
+    float f[16];
+  };
+
+  __device__ static QReg load_q(const uint8_t* p) {
+    constexpr int per = 16 / dtype_bytes(Q);
+    QReg r;
+#pragma unroll
+    for (int k = 0; k < 16 / per; ++k) unpack16<Q>(reinterpret_cast<const Vec16*>(p)[k], r.f + k * per);
+    return r;
+  }
+
+  // The 16 code values of one 16-byte load, in byte order (unscaled).
+  __device__ static void codes16(const Vec16& w, float* o) {
+    if constexpr (K == PKV_FP8_E4M3) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float2v lo = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w.w[i]), false);
+        const float2v hi = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w.w[i]), true);
+        o[4 * i] = lo.x;
+        o[4 * i + 1] = lo.y;
+        o[4 * i + 2] = hi.x;
+        o[4 * i + 3] = hi.y;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) o[4 * i + j] = static_cast<float>(static_cast<int8_t>(w.w[i] >> (8 * j)));
+    }
+  }
+
+  template <int D, int BS, int LPH>
+  __device__ static void chunk(const QReg& q, const DecodeArgs& a, const uint8_t* kp, const uint8_t* vp, int32_t blk,
+                               int pos0, int head, int64_t row_bytes, int lastu, int valid, float& m, float& l,
+                               float* acc) {
+    const int64_t base = (static_cast<int64_t>(blk) * BS + pos0) * row_bytes;
+    Vec16 kr[kChunk], vr[kChunk];
+#pragma unroll
+    for (int u = 0; u < kChunk; ++u) {
+      const int64_t ro = base + static_cast<int64_t>(u < lastu ? u : lastu) * row_bytes;
+      kr[u] = *reinterpret_cast<const Vec16*>(kp + ro);
+      vr[u] = *reinterpret_cast<const Vec16*>(vp + ro);
+    }
+    // Scales of the chunk's 8 positions (positions past the segment are
+    // read but never used: their weights are selected to zero).
+    const int64_t so = (static_cast<int64_t>(blk) * a.num_heads + head) * BS + pos0;
+    const float4 k0 = *reinterpret_cast<const float4*>(a.k_scales + so);
+    const float4 k1 = *reinterpret_cast<const float4*>(a.k_scales + so + 4);
+    const float4 v0 = *reinterpret_cast<const float4*>(a.v_scales + so);
+    const float4 v1 = *reinterpret_cast<const float4*>(a.v_scales + so + 4);
+    const float ks[kChunk] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
+    const float vs[kChunk] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+
+    float s[kChunk];
+    float mc = m;
+#pragma unroll
+    for (int u = 0; u < kChunk; ++u) {
+      float c[16];
+      codes16(kr[u], c);
+      float d = 0.f;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) d = fmaf(q.f[e], c[e], d);
+      s[u] = group_sum<LPH>(d) * (ks[u] * a.scale_log2);
+      if (u < valid) mc = fmaxf(mc, s[u]);
+    }
+    const float alpha = __builtin_amdgcn_exp2f(m - mc);
+    l *= alpha;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[e] *= alpha;
+#pragma unroll
+    for (int u = 0; u < kChunk; ++u) {
+      const float pu = u < valid ? __builtin_amdgcn_exp2f(s[u] - mc) : 0.f;
+      const float pv = u < valid ? pu * vs[u] : 0.f;
+      l += pu;
+      float c[16];
+      codes16(vr[u], c);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[e] = fmaf(pv, c[e], acc[e]);
+    }
+    m = mc;
+  }
+};
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+template <int ST, int KT>
+void launch_append_q8(int32_t head_dim, dim3 grid, hipStream_t stream, const void* k_new, const void* v_new,
+                      const int64_t* slots, void* kc, void* vc, float* ks, float* vs, int32_t num_tokens,
+                      int32_t num_heads, int32_t block_size, int64_t total_slots) {
+  auto run = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, grid, dim3(256), 0, stream, static_cast<const uint8_t*>(k_new),
+                       static_cast<const uint8_t*>(v_new), slots, static_cast<uint8_t*>(kc),
+                       static_cast<uint8_t*>(vc), ks, vs, num_tokens, num_heads, block_size, total_slots);
+  };
+  if (head_dim == 64)
+    run(append_q8_kernel<ST, KT, 64>);
+  else
+    run(append_q8_kernel<ST, KT, 128>);
+}
+
+template <int KT>
+void launch_decode_q8(const DecodeArgs& a, int wg, int32_t bs, int32_t d, pkv_dtype q_dtype, hipStream_t stream) {
+  switch (q_dtype) {
+    case PKV_F32: launch_decode_d<Q8KV<PKV_F32, KT>>(a, wg, bs, d, stream); break;
+    case PKV_F16: launch_decode_d<Q8KV<PKV_F16, KT>>(a, wg, bs, d, stream); break;
+    default: launch_decode_d<Q8KV<PKV_BF16, KT>>(a, wg, bs, d, stream); break;
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+PKV_API int pkv_append_quant(const void* k_new, const void* v_new, int32_t num_tokens, const int64_t* slot_mapping,
+                             void* k_cache, void* v_cache, float* k_scales, float* v_scales, int32_t num_blocks,
+                             int32_t block_size, int32_t num_heads, int32_t head_dim, pkv_dtype src_dtype,
+                             pkv_dtype cache_dtype, hipStream_t stream) {
+  if (num_tokens < 0 || num_blocks <= 0 || num_heads <= 0 || !supported_geometry(head_dim, block_size) ||
+      !is_16_32(src_dtype) || !is_8bit(cache_dtype))
+    return pkv::fail(PKV_ERR_INVALID, "append_quant: unsupported sizes (tokens %d, blocks %d, heads %d, head_dim %d, "
+                                      "block %d, src dtype %d, cache dtype %d)", num_tokens, num_blocks, num_heads,
+                     head_dim, block_size, static_cast<int>(src_dtype), static_cast<int>(cache_dtype));
+  if (num_tokens == 0) return PKV_OK;
+  if (!k_new || !v_new || !slot_mapping || !k_cache || !v_cache || !k_scales || !v_scales)
+    return pkv::fail(PKV_ERR_INVALID, "append_quant: null pointer");
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) || !aligned16(v_cache))
+    return pkv::fail(PKV_ERR_INVALID, "append_quant: rows and pools must be 16-byte aligned");
+  const int64_t threads = static_cast<int64_t>(num_tokens) * num_heads * (head_dim / kQuantElems);
+  const int64_t blocks = (threads + 255) / 256;
+  if (blocks > 0x7fffffff) return pkv::fail(PKV_ERR_INVALID, "append_quant: too many tokens");
+  const dim3 grid(static_cast<uint32_t>(blocks), 2);
+  const int64_t total = static_cast<int64_t>(num_blocks) * block_size;
+#define PKV_APPEND_Q8(ST, KT)                                                                                  \
+  launch_append_q8<ST, KT>(head_dim, grid, stream, k_new, v_new, slot_mapping, k_cache, v_cache, k_scales,  \
+                           v_scales, num_tokens, num_heads, block_size, total)
+  if (cache_dtype == PKV_I8) {
+    switch (src_dtype) {
+      case PKV_F32: PKV_APPEND_Q8(PKV_F32, PKV_I8); break;
+      case PKV_F16: PKV_APPEND_Q8(PKV_F16, PKV_I8); break;
+      default: PKV_APPEND_Q8(PKV_BF16, PKV_I8); break;
+    }
+  } else {
+    switch (src_dtype) {
+      case PKV_F32: PKV_APPEND_Q8(PKV_F32, PKV_FP8_E4M3); break;
+      case PKV_F16: PKV_APPEND_Q8(PKV_F16, PKV_FP8_E4M3); break;
+      default: PKV_APPEND_Q8(PKV_BF16, PKV_FP8_E4M3); break;
+    }
+  }
+#undef PKV_APPEND_Q8
+  return check_launch("append_quant");
+}
+
+PKV_API int pkv_attention_decode_quant(void* out, const void* q, const void* k_cache, const void* v_cache,
+                                       const float* k_scales, const float* v_scales, const int32_t* block_tables,
+                                       int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t max_seq_len,
+                                       int32_t batch, int32_t num_heads, int32_t head_dim, int32_t block_size,
+                                       int32_t num_blocks, float scale, pkv_dtype q_dtype, pkv_dtype cache_dtype,
+                                       int32_t num_work_groups, void* workspace, size_t workspace_bytes,
+                                       hipStream_t stream) {
+  if (batch < 0 || num_heads <= 0 || num_blocks <= 0 || max_blocks_per_seq <= 0 || max_seq_len < 0 ||
+      !supported_geometry(head_dim, block_size) || !is_16_32(q_dtype) || !is_8bit(cache_dtype))
+    return pkv::fail(PKV_ERR_INVALID, "attention_decode_quant: unsupported sizes (batch %d, heads %d, head_dim %d, "
+                                      "block %d, blocks %d, max_blocks %d, max_len %d, q dtype %d, cache dtype %d)",
+                     batch, num_heads, head_dim, block_size, num_blocks, max_blocks_per_seq, max_seq_len,
+                     static_cast<int>(q_dtype), static_cast<int>(cache_dtype));
+  const int st = check_decode_scalars(scale, num_work_groups);
+  if (st != PKV_OK) return st;
+  if (batch == 0) return PKV_OK;
+  if (!k_scales || !v_scales) return pkv::fail(PKV_ERR_INVALID, "attention_decode_quant: null scale pool");
+  if (!aligned16(q) || !aligned16(out) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(k_scales) ||
+      !aligned16(v_scales))
+    return pkv::fail(PKV_ERR_INVALID, "attention_decode_quant: q, out, pools and scales must be 16-byte aligned");
+  DecodeArgs a;
+  const int wg = prepare_decode(a, q, k_cache, v_cache, block_tables, max_blocks_per_seq, seq_lens, max_seq_len,
+                                batch, num_heads, head_dim, block_size, num_blocks, scale, cache_dtype,
+                                num_work_groups, workspace, workspace_bytes, out);
+  if (wg <= 0) return wg;
+  a.k_scales = k_scales;
+  a.v_scales = v_scales;
+  const int64_t row = static_cast<int64_t>(num_heads) * head_dim * dtype_bytes(q_dtype);
+  return run_sliced(a, out, q, block_tables, max_blocks_per_seq, seq_lens, batch, row, [&](const DecodeArgs& s) {
+    if (cache_dtype == PKV_I8)
+      launch_decode_q8<PKV_I8>(s, wg, block_size, head_dim, q_dtype, stream);
+    else
+      launch_decode_q8<PKV_FP8_E4M3>(s, wg, block_size, head_dim, q_dtype, stream);
+  });
+}
+
+}  // extern "C"

@@ -1,8 +1,9 @@
 """Builds one workload on both sides for the GPU parity tests.
 
 Product side: the libpkv block allocator on the host, device pools written by
-``pkv_append`` / ``pkv_copy_blocks``.  Oracle side: the oracle allocator and
-numpy pools written by ``oracle.pool``.  Inputs come from ``workloads`` only;
+``pkv_append`` / ``pkv_copy_blocks`` (8-bit caches: ``pkv_append_quant`` and
+block copies of the code and scale pools).  Oracle side: the oracle allocator
+and numpy pools written by ``oracle.pool`` / ``oracle.quant``.  Inputs come from ``workloads`` only;
 nothing the HIP path produces is fed to the oracle.
 
 Sequence of operations (the same on both sides):
@@ -24,6 +25,7 @@ import workloads
 from oracle import allocator as oalloc
 from oracle import attention as oatt
 from oracle import pool as opool
+from oracle import quant as oquant
 
 TORCH_DTYPE = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
 
@@ -53,7 +55,10 @@ class Case:
     pass
 
 
-def build(wl: workloads.Workload, device="cuda", extra_blocks: int = 1, check_pools: bool = True) -> Case:
+def build(wl: workloads.Workload, device="cuda", extra_blocks: int = 1, check_pools: bool = True,
+          kv: str = "dense") -> Case:
+    """``kv``: "dense" (cache in the workload's dtype) or an 8-bit format ("i8", "fp8")
+    whose codes and scales are quantised from the same rows."""
     bs, h, d, dt = wl.block_size, wl.num_heads, wl.head_dim, wl.dtype
     vals = wl.draw_values()
     B = wl.batch
@@ -75,22 +80,44 @@ def build(wl: workloads.Workload, device="cuda", extra_blocks: int = 1, check_po
     nblk = np.zeros(B, dtype=np.int32)
     orows = [[] for _ in range(B)]
 
-    sd = workloads.storage_np_dtype(dt)
-    okp = np.full((wl.num_blocks, bs, h, d), workloads.nan_storage(dt), dtype=sd)
-    ovp = okp.copy()
-    tdt = TORCH_DTYPE[dt]
-    kc = torch.full((wl.num_blocks, bs, h, d), float("nan"), dtype=tdt, device=device)
-    vc = torch.full_like(kc, float("nan"))
+    quant = kv != "dense"
+    if quant:
+        # Unwritten slots hold codes that are not valid data (E4M3 NaN, int8
+        # -128) and NaN scales: any read of one shows in the output.
+        poison = 0x7F if kv == "fp8" else 0x80
+        okp = np.full((wl.num_blocks, bs, h, d), poison, dtype=np.uint8)
+        ovp = okp.copy()
+        oks = np.full((wl.num_blocks, h, bs), np.nan, dtype=np.float32)
+        ovs = oks.copy()
+        kc = torch.full((wl.num_blocks, bs, h, d), poison, dtype=torch.uint8, device=device)
+        vc = torch.full_like(kc, poison)
+        ks = torch.full((wl.num_blocks, h, bs), float("nan"), dtype=torch.float32, device=device)
+        vs = torch.full_like(ks, float("nan"))
+    else:
+        sd = workloads.storage_np_dtype(dt)
+        okp = np.full((wl.num_blocks, bs, h, d), workloads.nan_storage(dt), dtype=sd)
+        ovp = okp.copy()
+        tdt = TORCH_DTYPE[dt]
+        kc = torch.full((wl.num_blocks, bs, h, d), float("nan"), dtype=tdt, device=device)
+        vc = torch.full_like(kc, float("nan"))
 
     def write(slots, krows, vrows, pairs):
         if pairs:
             pt = torch.tensor(np.asarray(pairs, dtype=np.int32).reshape(-1, 2), device=device)
             pkv.pkv_copy_blocks([kc], [vc], pt)
             opool.copy_blocks([okp], [ovp], pairs)
+            if quant:
+                pkv.pkv_copy_blocks([ks], [vs], pt)
+                opool.copy_blocks([oks], [ovs], pairs)
         if len(slots):
             st = torch.tensor(np.asarray(slots, dtype=np.int64), device=device)
-            pkv.pkv_append(to_device(krows, dt, device), to_device(vrows, dt, device), st, kc, vc)
-            opool.append(okp, ovp, krows, vrows, slots)
+            if quant:
+                pkv.pkv_append_quant(to_device(krows, dt, device), to_device(vrows, dt, device), st, kc, vc, ks, vs,
+                                     kv)
+                oquant.append(okp, ovp, oks, ovs, krows, vrows, slots, dt, kv)
+            else:
+                pkv.pkv_append(to_device(krows, dt, device), to_device(vrows, dt, device), st, kc, vc)
+                opool.append(okp, ovp, krows, vrows, slots)
 
     # 1. shared prefix
     done = np.zeros(B, dtype=np.int64)  # tokens already written per sequence
@@ -134,6 +161,9 @@ def build(wl: workloads.Workload, device="cuda", extra_blocks: int = 1, check_po
     c.wl, c.vals, c.palloc, c.oalloc = wl, vals, palloc, oa
     c.tables_np, c.nblk, c.orows = tables, nblk, orows
     c.k_cache, c.v_cache, c.ok_pool, c.ov_pool = kc, vc, okp, ovp
+    c.kv = kv
+    if quant:
+        c.k_scales, c.v_scales, c.ok_scales, c.ov_scales = ks, vs, oks, ovs
     c.cow_pairs = [tuple(p) for p in opairs] + [tuple(p) for p in dpairs]
     c.device = device
     c.tables = torch.tensor(tables, device=device)
@@ -141,19 +171,33 @@ def build(wl: workloads.Workload, device="cuda", extra_blocks: int = 1, check_po
     c.q = to_device(vals["q"], dt, device)
     c.out = torch.empty_like(c.q)
     if check_pools:
-        assert np.array_equal(to_bits(kc), storage_bits(okp)), "K pool differs from the oracle"
-        assert np.array_equal(to_bits(vc), storage_bits(ovp)), "V pool differs from the oracle"
+        if quant:
+            assert np.array_equal(kc.cpu().numpy(), okp), "K codes differ from the oracle"
+            assert np.array_equal(vc.cpu().numpy(), ovp), "V codes differ from the oracle"
+            assert np.array_equal(to_bits(ks), storage_bits(oks)), "K scales differ from the oracle"
+            assert np.array_equal(to_bits(vs), storage_bits(ovs)), "V scales differ from the oracle"
+        else:
+            assert np.array_equal(to_bits(kc), storage_bits(okp)), "K pool differs from the oracle"
+            assert np.array_equal(to_bits(vc), storage_bits(ovp)), "V pool differs from the oracle"
     return c
 
 
 def oracle_out(c: Case, heads=None) -> np.ndarray:
     wl = c.wl
+    if c.kv != "dense":
+        return oquant.decode_attention(c.vals["q"], c.ok_pool, c.ov_pool, c.ok_scales, c.ov_scales, c.tables_np,
+                                       wl.seq_lens, wl.dtype, c.kv, wl.scale, heads=heads)
     return oatt.decode_attention(c.vals["q"], c.ok_pool, c.ov_pool, c.tables_np, wl.seq_lens, wl.dtype, wl.scale,
                                  heads=heads)
 
 
 def run_gpu(c: Case, work_groups=0, out=None):
     out = c.out if out is None else out
+    if c.kv != "dense":
+        pkv.pkv_attention_decode_quant(out, c.q, c.k_cache, c.v_cache, c.k_scales, c.v_scales, c.tables, c.lens,
+                                       c.wl.max_seq_len, c.kv, scale=c.wl.scale, work_groups=work_groups)
+        torch.cuda.synchronize()
+        return out
     pkv.pkv_attention_decode(out, c.q, c.k_cache, c.v_cache, c.tables, c.lens, c.wl.max_seq_len, scale=c.wl.scale,
                              work_groups=work_groups)
     torch.cuda.synchronize()

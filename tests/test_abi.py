@@ -80,6 +80,35 @@ def test_device_calls_reject_bad_shapes_before_launch():
     assert lib.pkv_copy_blocks(None, None, 1, null, 0, 8, 4096, null) == pkv.PKV_OK
 
 
+def test_quant_calls_reject_bad_arguments_before_launch():
+    lib = pkv._lib
+    null = ctypes.c_void_p(0)
+    odd = ctypes.c_void_p(0x1008)   # never dereferenced: rejected as misaligned first
+    f16, i8, fp8 = pkv.PKV_F16, pkv.PKV_I8, pkv.PKV_FP8_E4M3
+
+    def decode(batch=1, hd=128, bs=16, qdt=f16, cdt=fp8, wg=0, ptr=null, scales=null):
+        return lib.pkv_attention_decode_quant(ptr, ptr, ptr, ptr, scales, scales, ptr, 4, ptr, 64, batch, 4, hd, bs,
+                                              8, 1.0, qdt, cdt, wg, null, 0, null)
+
+    assert decode(hd=96) == pkv.PKV_ERR_INVALID
+    assert decode(cdt=f16) == pkv.PKV_ERR_INVALID           # not an 8-bit cache
+    assert decode(qdt=i8) == pkv.PKV_ERR_INVALID            # queries are never 8-bit
+    assert decode(wg=-1) == pkv.PKV_ERR_INVALID
+    assert decode() == pkv.PKV_ERR_INVALID                  # null scale pools
+    assert decode(ptr=odd, scales=odd) == pkv.PKV_ERR_INVALID
+    assert decode(batch=0) == pkv.PKV_OK
+
+    def append(T=3, hd=128, sdt=f16, cdt=i8, ptr=null):
+        return lib.pkv_append_quant(ptr, ptr, T, ptr, ptr, ptr, ptr, ptr, 8, 16, 4, hd, sdt, cdt, null)
+
+    assert append(T=0) == pkv.PKV_OK
+    assert append() == pkv.PKV_ERR_INVALID                  # null pointers
+    assert append(ptr=odd) == pkv.PKV_ERR_INVALID           # misaligned
+    assert append(cdt=pkv.PKV_BF16) == pkv.PKV_ERR_INVALID
+    assert append(sdt=fp8) == pkv.PKV_ERR_INVALID
+    assert append(hd=80) == pkv.PKV_ERR_INVALID
+
+
 def test_workspace_queries():
     up = lambda x: -(-x // 256) * 256  # noqa: E731
     b, h, d, wg = 32, 32, 128, 512
@@ -93,6 +122,14 @@ def test_workspace_queries():
     big = pkv.pkv_decode_workspace_bytes(20000, 4, 64, "f32", 8)
     assert big == up(8190 * 8) + up(2 * 8 * 4 * 64 * 4) + up(2 * 8 * 4 * 8)
     assert pkv.pkv_decode_workspace_bytes(b, h, 96, "f16", wg) == 0
+    # 8-bit caches: 16 elements per lane -> 8 heads per wavefront at 128, at
+    # most 8 wavefronts per work-group.
+    assert pkv.pkv_decode_workspace_bytes(b, h, d, "fp8", wg) == (
+        up(b * 8) + up(2 * wg * h * d * 4) + up(2 * wg * h * 8))
+    assert pkv.pkv_decode_workspace_bytes(b, 160, d, "i8", wg) == (
+        up(b * 3 * 8) + up(2 * wg * 160 * d * 4) + up(2 * wg * 160 * 8))
+    assert pkv.pkv_decode_workspace_bytes(b, 256, 64, "i8", wg) == (
+        up(b * 2 * 8) + up(2 * wg * 256 * 64 * 4) + up(2 * wg * 256 * 8))
     assert pkv.pkv_decode_workspace_bytes(b, h, d, "f16", -1) == 0
 
 
