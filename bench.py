@@ -6,8 +6,9 @@ One step = the whole decode path for one batch:
      place from pinned host memory, with no copy on the queue (``--metadata
      device`` stages them with one asynchronous copy per step instead),
   3. copy-on-write block copies (pkv_copy_blocks) when a reservation produced any,
-  4. scatter of the new K/V rows (pkv_append), and
-  5. decode attention over the paged cache (pkv_attention_decode),
+  4. scatter of the new K/V rows (pkv_append) and
+  5. decode attention over the paged cache (pkv_attention_decode); with
+     ``--fused`` both in one launch per layer (pkv_append_attention_decode),
 with 4-5 repeated per layer for multi-layer workloads.  Inputs are resident in
 HBM before timing; sequences grow by one token per step.
 
@@ -67,6 +68,8 @@ def parse():
                    help="where kernels read step metadata: pinned host memory in place, or a device copy")
     p.add_argument("--kv-dtype", choices=["auto", "i8", "fp8"], default="auto",
                    help="K/V cache storage: the workload's dtype (auto) or an 8-bit format")
+    p.add_argument("--fused", action="store_true",
+                   help="scatter and attend in one launch per layer (pkv_append_attention_decode)")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target length of the oracle timing sample")
     p.add_argument("--no-cpu", action="store_true", help="skip the cpu_baseline leg")
     p.add_argument("--copy-calibration", action="store_true",
@@ -253,11 +256,22 @@ def main():
         d_meta = None
         metas = [split(hm) for hm in h_meta]
     per_slot = {}
+    fused = args.fused
     for r in range(ring):
         key = metas[r][0].data_ptr()
         if key not in per_slot:
             sl_t, ln_t, tb_t = metas[r]
-            if kv == "dense":
+            if fused:
+                qk = {} if kv == "dense" else {"k_scales": None, "v_scales": None, "cache_dtype": kv}
+                calls_l = []
+                for l in range(NL):
+                    if kv != "dense":
+                        qk["k_scales"], qk["v_scales"] = k_scales[l], v_scales[l]
+                    calls_l.append(pkv.PreparedAppendDecode(out, q_all[0, l], k_new[0, l], v_new[0, l], k_caches[l],
+                                                            v_caches[l], tb_t, ln_t, max_len, scale=wl.scale,
+                                                            work_groups=wgs, workspace=workspace, **qk))
+                per_slot[key] = (None, calls_l)
+            elif kv == "dense":
                 per_slot[key] = (
                     [pkv.PreparedAppend(k_new[0, l], v_new[0, l], sl_t, k_caches[l], v_caches[l])
                      for l in range(NL)],
@@ -301,9 +315,13 @@ def main():
             released[r].record(stream)
         appends, decodes = calls[r]
         for layer in range(NL):
-            appends[layer].launch(k_new[i, layer], v_new[i, layer])    # 4. scatter new rows
-            ev[i][layer][0].record(stream)
-            decodes[layer].launch(q_all[i, layer])                     # 5. decode attention
+            if fused:                                                  # 4 + 5 in one launch
+                ev[i][layer][0].record(stream)
+                decodes[layer].launch(q_all[i, layer], k_new[i, layer], v_new[i, layer])
+            else:
+                appends[layer].launch(k_new[i, layer], v_new[i, layer])    # 4. scatter new rows
+                ev[i][layer][0].record(stream)
+                decodes[layer].launch(q_all[i, layer])                     # 5. decode attention
             ev[i][layer][1].record(stream)
         if d_meta is None:                                             # read in place until here
             released[r].record(stream)
@@ -331,8 +349,10 @@ def main():
     # block-table entries + lengths.
     kv_per_call = float(np.mean(kv_bytes)) / NL
     algo = kv_per_call + 2 * B * H * D * esz + 4 * float(np.mean(table_entries)) + 4 * B
+    if fused:   # the launch also reads the new rows and writes them (8-bit: codes and scales) into the pools
+        algo += 2 * B * H * D * esz + B * tok_bytes
     achieved = algo / attn_s / 1e9
-    traffic = recorded_traffic(args.workload if kv == "dense" else f"{args.workload}/{kv}")
+    traffic = recorded_traffic(args.workload + ("" if kv == "dense" else f"/{kv}") + ("/fused" if fused else ""))
 
     extra = {}
     if args.copy_calibration:
@@ -385,12 +405,14 @@ def main():
         "config": {"workload": wl.title + ("" if kv == "dense" else f"; K/V cache {kv} + f32 scale per (token, head)"),
                    "kv_cache": wl.dtype if kv == "dense" else kv, "q_dtype": wl.dtype, "layers": NL, "batch": B, "heads": H, "head_dim": D, "block_size": bs,
                    "pool_blocks": wl.num_blocks, "work_groups": wgs, "metadata": mode,
+                   "launches_per_layer": 1 if fused else 2,
                    "mean_seq_len": round(kv_per_call / tok_bytes / B, 1), "cow_pairs": n_pairs[0]},
         "hbm_peak_frac": round(value / HBM_PEAK_GBS, 4),
         "token_steps_per_s": round(B * args.steps / elapsed, 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "kernel": "pkv_attention_decode (decode_kernel + decode_merge_kernel)",
+                     "kernel": ("pkv_append_attention_decode" if fused else "pkv_attention_decode")
+                     + ("_quant" if kv != "dense" else "") + " (decode_kernel + decode_merge_kernel)",
                      "avg_call_us": round(attn_s * 1e6, 2), "algorithmic_bytes_per_call": int(algo)},
         "cpu_baseline": cpu,
     }

@@ -243,6 +243,26 @@ PKV_API int pkv_attention_decode(void* out, const void* q, const void* k_cache, 
                                  int32_t num_work_groups, void* workspace, size_t workspace_bytes,
                                  hipStream_t stream);
 
+/* Scatter and decode attention in one launch: for every sequence b with
+ * L = seq_lens[b] >= 1, the new rows k_new[b], v_new[b] (device
+ * [batch][num_heads][head_dim] of `dtype`) are stored at logical position
+ * L - 1, i.e. at block block_tables[b][(L - 1) / block_size], slot
+ * (L - 1) % block_size, and attention then runs over positions 0 .. L - 1
+ * exactly as pkv_attention_decode.  The result, in `out` and in the pools,
+ * equals pkv_append with slot_mapping[b] = that slot followed by
+ * pkv_attention_decode; one launch (one kernel boundary) less per layer.
+ * The slot is taken from the table, so the caller's reservation must already
+ * have put the block there (and copied it if it was shared).  A sequence
+ * whose length is invalid, or whose block for L - 1 is outside
+ * [0, num_blocks), writes nothing and gets NaN rows.  Every other argument
+ * is that of pkv_attention_decode. */
+PKV_API int pkv_append_attention_decode(void* out, const void* q, const void* k_new, const void* v_new,
+                                        void* k_cache, void* v_cache, const int32_t* block_tables,
+                                        int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t max_seq_len,
+                                        int32_t batch, int32_t num_heads, int32_t head_dim, int32_t block_size,
+                                        int32_t num_blocks, float scale, pkv_dtype dtype, int32_t num_work_groups,
+                                        void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* ---------------------------------------------------------------------------
  * 8-bit caches (int8 or OCP FP8 E4M3)
  *
@@ -296,6 +316,20 @@ PKV_API int pkv_attention_decode_quant(void* out, const void* q, const void* k_c
                                        float scale, pkv_dtype q_dtype, pkv_dtype cache_dtype,
                                        int32_t num_work_groups, void* workspace, size_t workspace_bytes,
                                        hipStream_t stream);
+
+/* pkv_append_attention_decode for an 8-bit cache: each sequence's new rows
+ * (k_new, v_new: device [batch][num_heads][head_dim] of q_dtype, 16-byte
+ * aligned) are quantised exactly as pkv_append_quant does, stored with their
+ * scales at position L - 1, and attention runs over positions 0 .. L - 1 as
+ * pkv_attention_decode_quant. */
+PKV_API int pkv_append_attention_decode_quant(void* out, const void* q, const void* k_new, const void* v_new,
+                                              void* k_cache, void* v_cache, float* k_scales, float* v_scales,
+                                              const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                              const int32_t* seq_lens, int32_t max_seq_len, int32_t batch,
+                                              int32_t num_heads, int32_t head_dim, int32_t block_size,
+                                              int32_t num_blocks, float scale, pkv_dtype q_dtype,
+                                              pkv_dtype cache_dtype, int32_t num_work_groups, void* workspace,
+                                              size_t workspace_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

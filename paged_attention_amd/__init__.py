@@ -96,6 +96,11 @@ def _load():
         "pkv_attention_decode_quant": (ctypes.c_int, [vp, vp, vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, i32,
                                                       i32, ctypes.c_float, ctypes.c_int, ctypes.c_int, i32, vp, sz,
                                                       vp]),
+        "pkv_append_attention_decode": (ctypes.c_int, [vp, vp, vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, i32,
+                                                       i32, ctypes.c_float, ctypes.c_int, i32, vp, sz, vp]),
+        "pkv_append_attention_decode_quant": (ctypes.c_int, [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, i32, i32,
+                                                             i32, i32, i32, i32, ctypes.c_float, ctypes.c_int,
+                                                             ctypes.c_int, i32, vp, sz, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -409,6 +414,7 @@ class PreparedDecode:
         self._keep = (k_cache, v_cache, block_tables, seq_lens, ws)
         self._shape, self._dtype = tuple(q.shape), q.dtype
         self._fn = _lib.pkv_attention_decode
+        self._ti = 4   # argument index of block_tables (max_blocks and seq_lens follow)
 
     def _swap(self, i, t, what):
         if tuple(t.shape) != self._shape or t.dtype != self._dtype or not t.is_contiguous() or not t.is_cuda:
@@ -418,10 +424,12 @@ class PreparedDecode:
     def set_metadata(self, block_tables, seq_lens) -> None:
         """Point the call at other tables/lengths of the prepared shapes (device or pinned host)."""
         torch = _torch()
-        if tuple(block_tables.shape) != (self._shape[0], self._args[5]) or tuple(seq_lens.shape) != (self._shape[0],):
+        ti = self._ti
+        if tuple(block_tables.shape) != (self._shape[0], self._args[ti + 1]) or \
+                tuple(seq_lens.shape) != (self._shape[0],):
             raise InvalidArgument(PKV_ERR_INVALID, "prepared decode: metadata shapes differ")
-        self._args[4] = _dev(block_tables, "block_tables", torch.int32, pinned_ok=True)
-        self._args[6] = _dev(seq_lens, "seq_lens", torch.int32, pinned_ok=True)
+        self._args[ti] = _dev(block_tables, "block_tables", torch.int32, pinned_ok=True)
+        self._args[ti + 2] = _dev(seq_lens, "seq_lens", torch.int32, pinned_ok=True)
         self._meta = (block_tables, seq_lens)   # kept alive while the call points at them
 
     def launch(self, q=None, out=None) -> None:
@@ -542,14 +550,7 @@ class PreparedDecodeQuant(PreparedDecode):
         self._keep = (k_cache, v_cache, k_scales, v_scales, block_tables, seq_lens, ws)
         self._shape, self._dtype = tuple(q.shape), q.dtype
         self._fn = _lib.pkv_attention_decode_quant
-
-    def set_metadata(self, block_tables, seq_lens) -> None:
-        torch = _torch()
-        if tuple(block_tables.shape) != (self._shape[0], self._args[7]) or tuple(seq_lens.shape) != (self._shape[0],):
-            raise InvalidArgument(PKV_ERR_INVALID, "prepared decode: metadata shapes differ")
-        self._args[6] = _dev(block_tables, "block_tables", torch.int32, pinned_ok=True)
-        self._args[8] = _dev(seq_lens, "seq_lens", torch.int32, pinned_ok=True)
-        self._meta = (block_tables, seq_lens)
+        self._ti = 6
 
 
 class PreparedAppendQuant(PreparedDecode):
@@ -571,10 +572,82 @@ class PreparedAppendQuant(PreparedDecode):
         _check(self._fn(*self._args))
 
 
+
+# ---------------------------------------------------------------------------
+# scatter + decode in one launch
+# ---------------------------------------------------------------------------
+
+def _check_new_rows(k_new, v_new, q):
+    if tuple(k_new.shape) != tuple(q.shape) or v_new.shape != k_new.shape or k_new.dtype != q.dtype or \
+            v_new.dtype != q.dtype:
+        raise InvalidArgument(PKV_ERR_INVALID, "append_attention_decode: k_new/v_new must match q ([B][H][D])")
+    return [_dev(k_new, "k_new"), _dev(v_new, "v_new")]
+
+
+def pkv_append_attention_decode(out, q, k_new, v_new, k_cache, v_cache, block_tables, seq_lens, max_seq_len,
+                                scale=None, work_groups=0, workspace=None, stream=None) -> None:
+    """Store each sequence's new K/V row at its position ``seq_lens[b] - 1`` (through the
+    table) and run decode attention over all positions, in one launch."""
+    if q.shape[0] == 0:
+        return
+    args, _ = _decode_args(out, q, k_cache, v_cache, block_tables, seq_lens, max_seq_len, scale, work_groups,
+                           workspace, stream)
+    _check(_lib.pkv_append_attention_decode(*(args[:2] + _check_new_rows(k_new, v_new, q) + args[2:])))
+
+
+def pkv_append_attention_decode_quant(out, q, k_new, v_new, k_cache, v_cache, k_scales, v_scales, block_tables,
+                                      seq_lens, max_seq_len, cache_dtype, scale=None, work_groups=0, workspace=None,
+                                      stream=None) -> None:
+    """pkv_append_attention_decode for an 8-bit cache (the new rows are quantised on the way in)."""
+    if q.shape[0] == 0:
+        return
+    args, _ = _decode_quant_args(out, q, k_cache, v_cache, k_scales, v_scales, block_tables, seq_lens, max_seq_len,
+                                 cache_dtype, scale, work_groups, workspace, stream)
+    _check(_lib.pkv_append_attention_decode_quant(*(args[:2] + _check_new_rows(k_new, v_new, q) + args[2:])))
+
+
+class PreparedAppendDecode(PreparedDecode):
+    """A pkv_append_attention_decode[_quant] call checked once.
+
+    ``launch(q, k_new, v_new, out)`` swaps the per-step row pointers (same
+    shapes and dtype as at preparation); ``set_metadata`` repoints the tables
+    and lengths.  Pass ``k_scales``, ``v_scales`` and ``cache_dtype`` for an
+    8-bit cache.
+    """
+
+    def __init__(self, out, q, k_new, v_new, k_cache, v_cache, block_tables, seq_lens, max_seq_len, scale=None,
+                 work_groups=0, workspace=None, stream=None, k_scales=None, v_scales=None,
+                 cache_dtype=None):  # noqa: D107
+        if cache_dtype is None:
+            args, ws = _decode_args(out, q, k_cache, v_cache, block_tables, seq_lens, max_seq_len, scale,
+                                    work_groups, workspace, stream)
+            self._fn = _lib.pkv_append_attention_decode
+            self._ti = 6
+        else:
+            args, ws = _decode_quant_args(out, q, k_cache, v_cache, k_scales, v_scales, block_tables, seq_lens,
+                                          max_seq_len, cache_dtype, scale, work_groups, workspace, stream)
+            self._fn = _lib.pkv_append_attention_decode_quant
+            self._ti = 8
+        self._args = args[:2] + _check_new_rows(k_new, v_new, q) + args[2:]
+        self._keep = (k_cache, v_cache, k_scales, v_scales, block_tables, seq_lens, ws)
+        self._shape, self._dtype = tuple(q.shape), q.dtype
+
+    def launch(self, q=None, k_new=None, v_new=None, out=None) -> None:
+        if q is not None:
+            self._swap(1, q, "q")
+        if k_new is not None:
+            self._swap(2, k_new, "k_new")
+        if v_new is not None:
+            self._swap(3, v_new, "v_new")
+        if out is not None:
+            self._swap(0, out, "out")
+        _check(self._fn(*self._args))
+
+
 __all__ = [
     "BlockAllocator", "PkvError", "OutOfBlocks", "InvalidArgument", "pkv_append", "pkv_copy_blocks",
     "pkv_attention_decode", "pkv_decode_workspace_bytes", "pkv_decode_work_groups",
     "decode_workspace", "PreparedDecode", "PreparedAppend", "version", "LIB_PATH",
     "pkv_append_quant", "pkv_attention_decode_quant", "PreparedDecodeQuant", "PreparedAppendQuant",
-    "CACHE_FORMATS",
+    "CACHE_FORMATS", "pkv_append_attention_decode", "pkv_append_attention_decode_quant", "PreparedAppendDecode",
 ]

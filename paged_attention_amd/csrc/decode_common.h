@@ -201,10 +201,12 @@ constexpr int kMergeWaves = 4;      // heads per merge work-group
 struct DecodeArgs {
   void* out;
   const void* q;
-  const void* k;
-  const void* v;
-  const float* k_scales;  // 8-bit caches: [num_blocks][H][block_size] per-row scales (else unused)
-  const float* v_scales;
+  void* k;                // pools (written only by the appending variant)
+  void* v;
+  float* k_scales;        // 8-bit caches: [num_blocks][H][block_size] per-row scales (else unused)
+  float* v_scales;
+  const void* k_new;      // appending variant: [batch][H][D] new rows in q's dtype (else unused)
+  const void* v_new;
   const int32_t* tables;
   const int32_t* lens;
   float* ws_acc;      // [partial slot][H][D]
@@ -278,8 +280,15 @@ __device__ __forceinline__ bool length_ok(int L, const DecodeArgs& a) {
 //   QReg load_q(const uint8_t*)  this lane's EPL query elements;
 //   chunk<D, BS, LPH>(...)       load kChunk rows of K/V from block `blk`
 //                                starting at in-block position pos0 and fold
-//                                them into the online softmax state.
-template <class KV, int D, int BS>
+//                                them into the online softmax state;
+//   store_new<D, BS, LPH>(...)   (APPEND) store this lane's part of the
+//                                sequence's new K/V row at a pool position.
+// With APPEND the launch first stores each sequence's new row (k_new[b],
+// v_new[b]) at its position L - 1, then attends over all L positions.  The
+// work-group whose range holds a sequence's last chunk is the only one that
+// reads position L - 1, and it stores the row itself, lane by lane, before
+// reading it back with the same lanes: no other work-group is involved.
+template <class KV, int D, int BS, bool APPEND>
 __global__ void __launch_bounds__(KV::kMaxWaves * 64) decode_kernel(DecodeArgs a) {
   constexpr int EPL = KV::EPL;
   constexpr int LPH = D / EPL;   // lanes holding one head's row
@@ -378,6 +387,14 @@ __global__ void __launch_bounds__(KV::kMaxWaves * 64) decode_kernel(DecodeArgs a
       const int t_end = min(L, static_cast<int>(seg_end - seq0) * kChunk);
       const int32_t* trow = a.tables + static_cast<int64_t>(b) * a.max_blocks;
       const typename KV::QReg qv = KV::load_q(static_cast<const Elem*>(a.q) + b * q_row_bytes + e0 * QB);
+      if constexpr (APPEND) {
+        if (head_ok && seg_end == seq1 && L >= 1) {
+          const int pos = L - 1;
+          const int32_t id = trow[pos / BS];
+          if (static_cast<uint32_t>(id) < static_cast<uint32_t>(a.num_blocks))
+            KV::template store_new<D, BS, LPH>(a, b, hl, e0, id, pos % BS, row_bytes);
+        }
+      }
 
       float m = -INFINITY, l = 0.f;
       float acc[EPL];
@@ -606,30 +623,33 @@ inline Layout workspace_layout(int32_t batch, int32_t num_heads, int32_t head_di
   return w;
 }
 
-template <class KV, int D, int BS>
+template <class KV, int D, int BS, bool APPEND>
 void launch_decode(const DecodeArgs& a, int wg, hipStream_t stream) {
   const size_t lds = 2 * (static_cast<size_t>(a.batch) * a.groups_y + 1) * sizeof(int32_t);
-  hipLaunchKernelGGL((decode_kernel<KV, D, BS>), dim3(wg), dim3(a.waves_per_group * 64), lds, stream, a);
+  hipLaunchKernelGGL((decode_kernel<KV, D, BS, APPEND>), dim3(wg), dim3(a.waves_per_group * 64), lds, stream, a);
   const int slice_heads = a.waves_per_group * a.heads_per_wave;
   dim3 mgrid(ceil_div(slice_heads, kMergeWaves), a.batch * a.groups_y);
   hipLaunchKernelGGL((decode_merge_kernel<KV::QT, D>), mgrid, dim3(kMergeWaves * 64), 0, stream, a);
 }
 
-template <class KV, int D>
+template <class KV, int D, bool APPEND>
 void launch_decode_bs(const DecodeArgs& a, int wg, int32_t bs, hipStream_t stream) {
   switch (bs) {
-    case 8: launch_decode<KV, D, 8>(a, wg, stream); break;
-    case 16: launch_decode<KV, D, 16>(a, wg, stream); break;
-    default: launch_decode<KV, D, 32>(a, wg, stream); break;
+    case 8: launch_decode<KV, D, 8, APPEND>(a, wg, stream); break;
+    case 16: launch_decode<KV, D, 16, APPEND>(a, wg, stream); break;
+    default: launch_decode<KV, D, 32, APPEND>(a, wg, stream); break;
   }
 }
 
 template <class KV>
-void launch_decode_d(const DecodeArgs& a, int wg, int32_t bs, int32_t d, hipStream_t stream) {
-  if (d == 64)
-    launch_decode_bs<KV, 64>(a, wg, bs, stream);
-  else
-    launch_decode_bs<KV, 128>(a, wg, bs, stream);
+void launch_decode_d(const DecodeArgs& a, int wg, int32_t bs, int32_t d, bool append, hipStream_t stream) {
+  if (append) {
+    if (d == 64) launch_decode_bs<KV, 64, true>(a, wg, bs, stream);
+    else launch_decode_bs<KV, 128, true>(a, wg, bs, stream);
+  } else {
+    if (d == 64) launch_decode_bs<KV, 64, false>(a, wg, bs, stream);
+    else launch_decode_bs<KV, 128, false>(a, wg, bs, stream);
+  }
 }
 
 // Checks of the scalar arguments of a decode call (made before anything else
@@ -659,10 +679,12 @@ inline int prepare_decode(DecodeArgs& a, const void* q, const void* k_cache, con
                      workspace_bytes);
   const Shape sh = decode_shape(num_heads, head_dim, cache_dtype);
   char* base = static_cast<char*>(workspace);
-  a.k = k_cache;
-  a.v = v_cache;
+  a.k = const_cast<void*>(k_cache);
+  a.v = const_cast<void*>(v_cache);
   a.k_scales = nullptr;
   a.v_scales = nullptr;
+  a.k_new = nullptr;
+  a.v_new = nullptr;
   a.ws_plan = reinterpret_cast<int32_t*>(base + ws.plan);
   a.ws_acc = reinterpret_cast<float*>(base + ws.acc);
   a.ws_ml = reinterpret_cast<float2*>(base + ws.ml);
@@ -682,13 +704,19 @@ inline int prepare_decode(DecodeArgs& a, const void* q, const void* k_cache, con
 // prefix arrays; the slices run one after another on the stream and share the
 // workspace.
 template <class Launch>
-int run_sliced(DecodeArgs a, void* out, const void* q, const int32_t* block_tables, int32_t max_blocks_per_seq,
-               const int32_t* seq_lens, int32_t batch, int64_t q_row_bytes, Launch launch) {
+int run_sliced(const DecodeArgs& base, void* out, const void* q, const int32_t* block_tables,
+               int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t batch, int64_t q_row_bytes,
+               Launch launch) {
+  DecodeArgs a = base;
   const int32_t per_launch = kMaxVirtual / a.groups_y;
   for (int32_t b0 = 0; b0 < batch; b0 += per_launch) {
     a.batch = batch - b0 < per_launch ? batch - b0 : per_launch;
     a.out = static_cast<char*>(out) + b0 * q_row_bytes;
     a.q = static_cast<const char*>(q) + b0 * q_row_bytes;
+    if (base.k_new) {
+      a.k_new = static_cast<const char*>(base.k_new) + b0 * q_row_bytes;
+      a.v_new = static_cast<const char*>(base.v_new) + b0 * q_row_bytes;
+    }
     a.tables = block_tables + static_cast<int64_t>(b0) * max_blocks_per_seq;
     a.lens = seq_lens + b0;
     launch(a);

@@ -101,10 +101,55 @@ struct DenseKV {
     }
     softmax_chunk<DT, EPL, LPH>(qv, kr, vr, valid, a.scale_log2, m, l, acc);
   }
+
+  // The new row is already in the cache's dtype: a 16-byte copy per lane.
+  template <int D, int BS, int LPH>
+  __device__ static void store_new(const DecodeArgs& a, int b, int /*head*/, int e0, int32_t blk, int pos,
+                                   int64_t row_bytes) {
+    const int64_t src = (static_cast<int64_t>(b) * a.num_heads * D + e0) * KB;
+    const int64_t dst = (static_cast<int64_t>(blk) * BS + pos) * row_bytes + e0 * KB;
+    *reinterpret_cast<Vec16*>(static_cast<uint8_t*>(a.k) + dst) =
+        *reinterpret_cast<const Vec16*>(static_cast<const uint8_t*>(a.k_new) + src);
+    *reinterpret_cast<Vec16*>(static_cast<uint8_t*>(a.v) + dst) =
+        *reinterpret_cast<const Vec16*>(static_cast<const uint8_t*>(a.v_new) + src);
+  }
 };
 
 bool supported(int32_t head_dim, int32_t block_size, pkv_dtype dtype) {
   return supported_geometry(head_dim, block_size) && is_16_32(dtype);
+}
+
+// Both 16/32-bit decode entry points; k_new != nullptr selects the variant
+// that first stores each sequence's new row at its position L - 1.
+int decode_dense(void* out, const void* q, const void* k_new, const void* v_new, const void* k_cache,
+                 const void* v_cache, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                 const int32_t* seq_lens, int32_t max_seq_len, int32_t batch, int32_t num_heads, int32_t head_dim,
+                 int32_t block_size, int32_t num_blocks, float scale, pkv_dtype dtype, int32_t num_work_groups,
+                 void* workspace, size_t workspace_bytes, hipStream_t stream, const char* what) {
+  if (batch < 0 || num_heads <= 0 || num_blocks <= 0 || max_blocks_per_seq <= 0 || max_seq_len < 0 ||
+      !supported(head_dim, block_size, dtype))
+    return pkv::fail(PKV_ERR_INVALID, "%s: unsupported sizes (batch %d, heads %d, head_dim %d, block %d, blocks %d, "
+                                      "max_blocks %d, max_len %d, dtype %d)", what, batch, num_heads, head_dim,
+                     block_size, num_blocks, max_blocks_per_seq, max_seq_len, static_cast<int>(dtype));
+  const int st = check_decode_scalars(scale, num_work_groups);
+  if (st != PKV_OK) return st;
+  if (batch == 0) return PKV_OK;
+  DecodeArgs a;
+  const int wg = prepare_decode(a, q, k_cache, v_cache, block_tables, max_blocks_per_seq, seq_lens, max_seq_len,
+                                batch, num_heads, head_dim, block_size, num_blocks, scale, dtype, num_work_groups,
+                                workspace, workspace_bytes, out);
+  if (wg <= 0) return wg;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  const bool append = k_new != nullptr;
+  const int64_t row = static_cast<int64_t>(num_heads) * head_dim * dtype_bytes(dtype);
+  return run_sliced(a, out, q, block_tables, max_blocks_per_seq, seq_lens, batch, row, [&](const DecodeArgs& s) {
+    switch (dtype) {
+      case PKV_F32: launch_decode_d<DenseKV<PKV_F32>>(s, wg, block_size, head_dim, append, stream); break;
+      case PKV_F16: launch_decode_d<DenseKV<PKV_F16>>(s, wg, block_size, head_dim, append, stream); break;
+      default: launch_decode_d<DenseKV<PKV_BF16>>(s, wg, block_size, head_dim, append, stream); break;
+    }
+  });
 }
 
 }  // namespace
@@ -177,27 +222,21 @@ PKV_API int pkv_attention_decode(void* out, const void* q, const void* k_cache, 
                                  int32_t block_size, int32_t num_blocks, float scale, pkv_dtype dtype,
                                  int32_t num_work_groups, void* workspace, size_t workspace_bytes,
                                  hipStream_t stream) {
-  if (batch < 0 || num_heads <= 0 || num_blocks <= 0 || max_blocks_per_seq <= 0 || max_seq_len < 0 ||
-      !supported(head_dim, block_size, dtype))
-    return pkv::fail(PKV_ERR_INVALID, "attention_decode: unsupported sizes (batch %d, heads %d, head_dim %d, block %d, "
-                                      "blocks %d, max_blocks %d, max_len %d, dtype %d)", batch, num_heads, head_dim,
-                     block_size, num_blocks, max_blocks_per_seq, max_seq_len, static_cast<int>(dtype));
-  const int st = check_decode_scalars(scale, num_work_groups);
-  if (st != PKV_OK) return st;
-  if (batch == 0) return PKV_OK;
-  DecodeArgs a;
-  const int wg = prepare_decode(a, q, k_cache, v_cache, block_tables, max_blocks_per_seq, seq_lens, max_seq_len,
-                                batch, num_heads, head_dim, block_size, num_blocks, scale, dtype, num_work_groups,
-                                workspace, workspace_bytes, out);
-  if (wg <= 0) return wg;
-  const int64_t row = static_cast<int64_t>(num_heads) * head_dim * dtype_bytes(dtype);
-  return run_sliced(a, out, q, block_tables, max_blocks_per_seq, seq_lens, batch, row, [&](const DecodeArgs& s) {
-    switch (dtype) {
-      case PKV_F32: launch_decode_d<DenseKV<PKV_F32>>(s, wg, block_size, head_dim, stream); break;
-      case PKV_F16: launch_decode_d<DenseKV<PKV_F16>>(s, wg, block_size, head_dim, stream); break;
-      default: launch_decode_d<DenseKV<PKV_BF16>>(s, wg, block_size, head_dim, stream); break;
-    }
-  });
+  return decode_dense(out, q, nullptr, nullptr, k_cache, v_cache, block_tables, max_blocks_per_seq, seq_lens,
+                      max_seq_len, batch, num_heads, head_dim, block_size, num_blocks, scale, dtype, num_work_groups,
+                      workspace, workspace_bytes, stream, "attention_decode");
+}
+
+PKV_API int pkv_append_attention_decode(void* out, const void* q, const void* k_new, const void* v_new,
+                                        void* k_cache, void* v_cache, const int32_t* block_tables,
+                                        int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t max_seq_len,
+                                        int32_t batch, int32_t num_heads, int32_t head_dim, int32_t block_size,
+                                        int32_t num_blocks, float scale, pkv_dtype dtype, int32_t num_work_groups,
+                                        void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (batch > 0 && (!k_new || !v_new)) return pkv::fail(PKV_ERR_INVALID, "append_attention_decode: null new rows");
+  return decode_dense(out, q, k_new, v_new, k_cache, v_cache, block_tables, max_blocks_per_seq, seq_lens,
+                      max_seq_len, batch, num_heads, head_dim, block_size, num_blocks, scale, dtype, num_work_groups,
+                      workspace, workspace_bytes, stream, "append_attention_decode");
 }
 
 }  // extern "C"

@@ -207,6 +207,41 @@ struct Q8KV {
     }
     m = mc;
   }
+
+  // Quantises one row part of 16 elements held by this lane; the LPH lanes of
+  // the head agree on the scale through a DPP maximum.  Every lane of the
+  // head stores the (same) scale, so each reads back its own store.
+  template <int LPH>
+  __device__ static void quant_store(const uint8_t* src, uint8_t* dst, float* scale_dst) {
+    const QReg x = load_q(src);
+    float amax = 0.f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) amax = fmaxf(amax, fabsf(x.f[e]));
+    amax = group_max<LPH>(amax);
+    const float scale = amax / qmax<K>();
+    Vec16 w;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      w.w[i] = 0;
+      if (scale > 0.f) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) w.w[i] |= quant_code<K>(x.f[4 * i + j] / scale) << (8 * j);
+      }
+    }
+    *reinterpret_cast<Vec16*>(dst) = w;
+    *scale_dst = scale;
+  }
+
+  template <int D, int BS, int LPH>
+  __device__ static void store_new(const DecodeArgs& a, int b, int head, int e0, int32_t blk, int pos,
+                                   int64_t row_bytes) {
+    constexpr int QB = dtype_bytes(Q);
+    const int64_t src = (static_cast<int64_t>(b) * a.num_heads * D + e0) * QB;
+    const int64_t dst = (static_cast<int64_t>(blk) * BS + pos) * row_bytes + e0;
+    const int64_t so = (static_cast<int64_t>(blk) * a.num_heads + head) * BS + pos;
+    quant_store<LPH>(static_cast<const uint8_t*>(a.k_new) + src, static_cast<uint8_t*>(a.k) + dst, a.k_scales + so);
+    quant_store<LPH>(static_cast<const uint8_t*>(a.v_new) + src, static_cast<uint8_t*>(a.v) + dst, a.v_scales + so);
+  }
 };
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -227,12 +262,53 @@ void launch_append_q8(int32_t head_dim, dim3 grid, hipStream_t stream, const voi
 }
 
 template <int KT>
-void launch_decode_q8(const DecodeArgs& a, int wg, int32_t bs, int32_t d, pkv_dtype q_dtype, hipStream_t stream) {
+void launch_decode_q8(const DecodeArgs& a, int wg, int32_t bs, int32_t d, pkv_dtype q_dtype, bool append,
+                      hipStream_t stream) {
   switch (q_dtype) {
-    case PKV_F32: launch_decode_d<Q8KV<PKV_F32, KT>>(a, wg, bs, d, stream); break;
-    case PKV_F16: launch_decode_d<Q8KV<PKV_F16, KT>>(a, wg, bs, d, stream); break;
-    default: launch_decode_d<Q8KV<PKV_BF16, KT>>(a, wg, bs, d, stream); break;
+    case PKV_F32: launch_decode_d<Q8KV<PKV_F32, KT>>(a, wg, bs, d, append, stream); break;
+    case PKV_F16: launch_decode_d<Q8KV<PKV_F16, KT>>(a, wg, bs, d, append, stream); break;
+    default: launch_decode_d<Q8KV<PKV_BF16, KT>>(a, wg, bs, d, append, stream); break;
   }
+}
+
+// Both 8-bit decode entry points; k_new != nullptr selects the variant that
+// first quantises and stores each sequence's new row at its position L - 1.
+int decode_q8(void* out, const void* q, const void* k_new, const void* v_new, const void* k_cache,
+              const void* v_cache, const float* k_scales, const float* v_scales, const int32_t* block_tables,
+              int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t max_seq_len, int32_t batch,
+              int32_t num_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
+              pkv_dtype q_dtype, pkv_dtype cache_dtype, int32_t num_work_groups, void* workspace,
+              size_t workspace_bytes, hipStream_t stream, const char* what) {
+  if (batch < 0 || num_heads <= 0 || num_blocks <= 0 || max_blocks_per_seq <= 0 || max_seq_len < 0 ||
+      !supported_geometry(head_dim, block_size) || !is_16_32(q_dtype) || !is_8bit(cache_dtype))
+    return pkv::fail(PKV_ERR_INVALID, "%s: unsupported sizes (batch %d, heads %d, head_dim %d, block %d, blocks %d, "
+                                      "max_blocks %d, max_len %d, q dtype %d, cache dtype %d)", what, batch,
+                     num_heads, head_dim, block_size, num_blocks, max_blocks_per_seq, max_seq_len,
+                     static_cast<int>(q_dtype), static_cast<int>(cache_dtype));
+  const int st = check_decode_scalars(scale, num_work_groups);
+  if (st != PKV_OK) return st;
+  if (batch == 0) return PKV_OK;
+  if (!k_scales || !v_scales) return pkv::fail(PKV_ERR_INVALID, "%s: null scale pool", what);
+  if (!aligned16(q) || !aligned16(out) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(k_scales) ||
+      !aligned16(v_scales))
+    return pkv::fail(PKV_ERR_INVALID, "%s: q, out, pools and scales must be 16-byte aligned", what);
+  DecodeArgs a;
+  const int wg = prepare_decode(a, q, k_cache, v_cache, block_tables, max_blocks_per_seq, seq_lens, max_seq_len,
+                                batch, num_heads, head_dim, block_size, num_blocks, scale, cache_dtype,
+                                num_work_groups, workspace, workspace_bytes, out);
+  if (wg <= 0) return wg;
+  a.k_scales = const_cast<float*>(k_scales);
+  a.v_scales = const_cast<float*>(v_scales);
+  a.k_new = k_new;
+  a.v_new = v_new;
+  const bool append = k_new != nullptr;
+  const int64_t row = static_cast<int64_t>(num_heads) * head_dim * dtype_bytes(q_dtype);
+  return run_sliced(a, out, q, block_tables, max_blocks_per_seq, seq_lens, batch, row, [&](const DecodeArgs& s) {
+    if (cache_dtype == PKV_I8)
+      launch_decode_q8<PKV_I8>(s, wg, block_size, head_dim, q_dtype, append, stream);
+    else
+      launch_decode_q8<PKV_FP8_E4M3>(s, wg, block_size, head_dim, q_dtype, append, stream);
+  });
 }
 
 }  // namespace
@@ -285,33 +361,26 @@ PKV_API int pkv_attention_decode_quant(void* out, const void* q, const void* k_c
                                        int32_t num_blocks, float scale, pkv_dtype q_dtype, pkv_dtype cache_dtype,
                                        int32_t num_work_groups, void* workspace, size_t workspace_bytes,
                                        hipStream_t stream) {
-  if (batch < 0 || num_heads <= 0 || num_blocks <= 0 || max_blocks_per_seq <= 0 || max_seq_len < 0 ||
-      !supported_geometry(head_dim, block_size) || !is_16_32(q_dtype) || !is_8bit(cache_dtype))
-    return pkv::fail(PKV_ERR_INVALID, "attention_decode_quant: unsupported sizes (batch %d, heads %d, head_dim %d, "
-                                      "block %d, blocks %d, max_blocks %d, max_len %d, q dtype %d, cache dtype %d)",
-                     batch, num_heads, head_dim, block_size, num_blocks, max_blocks_per_seq, max_seq_len,
-                     static_cast<int>(q_dtype), static_cast<int>(cache_dtype));
-  const int st = check_decode_scalars(scale, num_work_groups);
-  if (st != PKV_OK) return st;
-  if (batch == 0) return PKV_OK;
-  if (!k_scales || !v_scales) return pkv::fail(PKV_ERR_INVALID, "attention_decode_quant: null scale pool");
-  if (!aligned16(q) || !aligned16(out) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(k_scales) ||
-      !aligned16(v_scales))
-    return pkv::fail(PKV_ERR_INVALID, "attention_decode_quant: q, out, pools and scales must be 16-byte aligned");
-  DecodeArgs a;
-  const int wg = prepare_decode(a, q, k_cache, v_cache, block_tables, max_blocks_per_seq, seq_lens, max_seq_len,
-                                batch, num_heads, head_dim, block_size, num_blocks, scale, cache_dtype,
-                                num_work_groups, workspace, workspace_bytes, out);
-  if (wg <= 0) return wg;
-  a.k_scales = k_scales;
-  a.v_scales = v_scales;
-  const int64_t row = static_cast<int64_t>(num_heads) * head_dim * dtype_bytes(q_dtype);
-  return run_sliced(a, out, q, block_tables, max_blocks_per_seq, seq_lens, batch, row, [&](const DecodeArgs& s) {
-    if (cache_dtype == PKV_I8)
-      launch_decode_q8<PKV_I8>(s, wg, block_size, head_dim, q_dtype, stream);
-    else
-      launch_decode_q8<PKV_FP8_E4M3>(s, wg, block_size, head_dim, q_dtype, stream);
-  });
+  return decode_q8(out, q, nullptr, nullptr, k_cache, v_cache, k_scales, v_scales, block_tables, max_blocks_per_seq,
+                   seq_lens, max_seq_len, batch, num_heads, head_dim, block_size, num_blocks, scale, q_dtype,
+                   cache_dtype, num_work_groups, workspace, workspace_bytes, stream, "attention_decode_quant");
+}
+
+PKV_API int pkv_append_attention_decode_quant(void* out, const void* q, const void* k_new, const void* v_new,
+                                              void* k_cache, void* v_cache, float* k_scales, float* v_scales,
+                                              const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                              const int32_t* seq_lens, int32_t max_seq_len, int32_t batch,
+                                              int32_t num_heads, int32_t head_dim, int32_t block_size,
+                                              int32_t num_blocks, float scale, pkv_dtype q_dtype,
+                                              pkv_dtype cache_dtype, int32_t num_work_groups, void* workspace,
+                                              size_t workspace_bytes, hipStream_t stream) {
+  if (batch > 0 && (!k_new || !v_new))
+    return pkv::fail(PKV_ERR_INVALID, "append_attention_decode_quant: null new rows");
+  if (batch > 0 && (!aligned16(k_new) || !aligned16(v_new)))
+    return pkv::fail(PKV_ERR_INVALID, "append_attention_decode_quant: new rows must be 16-byte aligned");
+  return decode_q8(out, q, k_new, v_new, k_cache, v_cache, k_scales, v_scales, block_tables, max_blocks_per_seq,
+                   seq_lens, max_seq_len, batch, num_heads, head_dim, block_size, num_blocks, scale, q_dtype,
+                   cache_dtype, num_work_groups, workspace, workspace_bytes, stream, "append_attention_decode_quant");
 }
 
 }  // extern "C"

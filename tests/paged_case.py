@@ -154,6 +154,13 @@ def build(wl: workloads.Workload, device="cuda", extra_blocks: int = 1, check_po
     kd = [rows_of(b, "k")[done[b]: done[b] + step[b]] for b in range(B)]
     vd = [rows_of(b, "v")[done[b]: done[b] + step[b]] for b in range(B)]
     write(dslots, np.concatenate(kd, axis=0), np.concatenate(vd, axis=0), dpairs)
+    # the decode step's rows, one per sequence (zeros where length is 0)
+    sd_in = workloads.storage_np_dtype(dt)
+    dec_k = np.zeros((B, h, d), dtype=sd_in)
+    dec_v = np.zeros((B, h, d), dtype=sd_in)
+    for b in range(B):
+        if step[b]:
+            dec_k[b], dec_v[b] = kd[b][0], vd[b][0]
     for b in range(B):
         assert tables[b, : nblk[b]].tolist() == orows[b]
 
@@ -162,6 +169,7 @@ def build(wl: workloads.Workload, device="cuda", extra_blocks: int = 1, check_po
     c.tables_np, c.nblk, c.orows = tables, nblk, orows
     c.k_cache, c.v_cache, c.ok_pool, c.ov_pool = kc, vc, okp, ovp
     c.kv = kv
+    c.dec_k, c.dec_v = dec_k, dec_v
     if quant:
         c.k_scales, c.v_scales, c.ok_scales, c.ov_scales = ks, vs, oks, ovs
     c.cow_pairs = [tuple(p) for p in opairs] + [tuple(p) for p in dpairs]
