@@ -97,6 +97,16 @@ class OracleAllocator:
     def num_free(self) -> int:
         return len(self.free)
 
+    def available(self) -> int:
+        """Blocks a reservation may take (the free queue; a prefix cache adds its evictable blocks)."""
+        return len(self.free)
+
+    def _snapshot(self):
+        return deque(self.free), list(self.ref)
+
+    def _restore(self, snap) -> None:
+        self.free, self.ref = snap
+
     def free_list(self) -> list:
         return list(self.free)
 
@@ -145,7 +155,7 @@ class OracleAllocator:
         cow = 0
         if n_new > 0 and cur_len % bs != 0 and self.ref[row[cur_len // bs]] > 1:
             cow = 1
-        if fresh + cow > len(self.free):
+        if fresh + cow > self.available():
             raise AllocatorError(ERR_NO_BLOCKS, "out of blocks")
         slots, pairs = [], []
         written = set()
@@ -167,7 +177,7 @@ class OracleAllocator:
 
     def reserve_batch(self, rows: list, cur_lens, n_new):
         """Reserve for several sequences in ascending index order, all or nothing."""
-        saved_free, saved_ref = deque(self.free), list(self.ref)
+        snap = self._snapshot()
         saved_rows = [list(r) for r in rows]
         slots, pairs = [], []
         try:
@@ -176,7 +186,7 @@ class OracleAllocator:
                 slots.extend(s)
                 pairs.extend(p)
         except AllocatorError:
-            self.free, self.ref = saved_free, saved_ref
+            self._restore(snap)
             for r, old in zip(rows, saved_rows):
                 r[:] = old
             raise
