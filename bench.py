@@ -61,6 +61,9 @@ def parse():
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="llama7b_layer", choices=["llama7b_layer", "long13b", "full7b_step"])
+    p.add_argument("--component", default="decode", choices=["decode", "prefix_cache"],
+                   help="decode: the decode step (default, the headline line); prefix_cache: host prefix-cache "
+                        "operations on a shared-system-prompt request stream")
     p.add_argument("--block-size", type=int, default=16, help="block size of the long13b workload")
     p.add_argument("--work-groups", type=int, default=0, help="decode work-groups (0 = library choice)")
     p.add_argument("--ring", type=int, default=4, help="host staging buffers (how many steps the host may run ahead)")
@@ -138,8 +141,80 @@ def cpu_baseline(wl, sample_rows, target_s, kv):
                       f"one layer), {spent:.1f} s of oracle time"}
 
 
+def run_prefix_cache(args):
+    """Host prefix-cache throughput: requests that share a 1500-token system
+    prompt and add ~100 tokens of their own (the example of
+    icman.com.cn/news/78786 §3.1), block 16.  One request = match its prompt,
+    reserve the unmatched tail, record its full blocks, release it later (a
+    sliding window of 64 live requests).  Reports requests/s of the C++
+    cache and, beside it, of the oracle doing the same operations."""
+    import paged_attention_amd as pkv
+    from oracle import prefix_cache as opc
+
+    bs, n_req, window, prompt_len = 16, 4000, 64, 1500
+    rng = np.random.default_rng(11)
+    prompt = rng.integers(0, 32000, prompt_len).astype(np.int32)
+    reqs = [np.concatenate([prompt, rng.integers(0, 32000, int(rng.integers(50, 151))).astype(np.int32)])
+            for _ in range(n_req)]
+    num_blocks = (window + 2) * (-(-(prompt_len + 150) // bs)) * 2
+
+    def drive(alloc, match, reserve, register, release, count):
+        live, hit_blocks, need_blocks = [], 0, 0
+        t0 = time.perf_counter()
+        for i in range(count):
+            toks = reqs[i]
+            row = match(toks)
+            hits = len(row)
+            hit_blocks += hits
+            need_blocks += len(toks) // bs
+            row = reserve(row, hits * bs, len(toks) - hits * bs)
+            register(toks, row, hits)
+            live.append(row)
+            if len(live) > window:
+                release(live.pop(0))
+        return time.perf_counter() - t0, hit_blocks, need_blocks
+
+    a = pkv.BlockAllocator(num_blocks, bs)
+    a.enable_prefix_cache()
+
+    def lib_reserve(row, cur, n):
+        a.reserve(row, cur, n)
+        return row
+
+    dt, hits, need = drive(a, lambda t: a.prefix_match(t, 1 << 20), lib_reserve,
+                           lambda t, r, first: a.prefix_register(t, r, len(r), first), a.release, n_req)
+    o = opc.OracleCachingAllocator(num_blocks, bs)
+
+    def o_reserve(row, cur, n):
+        o.reserve(row, cur, n)
+        return row
+
+    n_oracle = 400
+    dto, _, _ = drive(o, lambda t: o.match(t, 1 << 20), o_reserve,
+                      lambda t, r, first: o.register(t, r, len(r), first), lambda r: o.release(r, len(r)), n_oracle)
+    prefill_saved = hits * bs / sum(len(r) for r in reqs)
+    rec = {
+        "metric": "prefix-cache host operations (match + reserve + register + release) per second",
+        "value": round(n_req / dt, 1), "unit": "requests/s", "n_gpus": 0, "steps": n_req, "warmup": 0,
+        "ms_per_step": round(dt / n_req * 1e3, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "int32 token ids, SHA-256 keys", "data": "synthetic (seeded token ids)",
+        "config": {"workload": f"{n_req} requests sharing a {prompt_len}-token system prompt plus U[50,150] own "
+                               f"tokens, block {bs}, {window} live requests", "pool_blocks": num_blocks},
+        "hit_blocks_per_request": round(hits / n_req, 2),
+        "full_blocks_per_request": round(need / n_req, 2),
+        "prefill_tokens_saved_frac": round(prefill_saved, 4),
+        "us_per_request_block": round(dt / max(1, need) * 1e6, 3),
+        "cpu_baseline": {"value": round(n_oracle / dto, 1), "unit": "requests/s", "cores": 1, "kind": "oracle",
+                         "sample": f"the Python oracle (hashlib SHA-256) on the first {n_oracle} requests"},
+    }
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     args = parse()
+    if args.component == "prefix_cache":
+        run_prefix_cache(args)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported by this single-GPU build "
               f"(how the path would shard is described in the design notes)", file=sys.stderr)

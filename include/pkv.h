@@ -99,19 +99,22 @@ PKV_API int pkv_allocator_create(int32_t num_blocks, int32_t block_size, const i
                                  pkv_allocator** out);
 PKV_API void pkv_allocator_destroy(pkv_allocator* a);
 
-/* Pop the head of the free queue; its count becomes 1.  PKV_ERR_NO_BLOCKS
- * when empty — the pool is full and the caller queues the request
- * (hnwysp.cn/news/103996 §4.4 alloc_block). */
+/* Pop the head of the free queue (with the prefix cache on and the queue
+ * empty: evict the least recently released cached block); its count becomes
+ * 1.  PKV_ERR_NO_BLOCKS when nothing is available — the pool is full and the
+ * caller queues the request (hnwysp.cn/news/103996 §4.4 alloc_block). */
 PKV_API int pkv_block_alloc(pkv_allocator* a, int32_t* block_out);
 /* Share a block: count + 1.  PKV_ERR_REFCOUNT if the block is free
  * (hnwysp.cn/news/103996 §3.3: a prefix hit raises the count). */
 PKV_API int pkv_block_incref(pkv_allocator* a, int32_t block);
 /* Drop one reference; at zero the block joins the tail of the free queue
- * (hnwysp.cn/news/103996 §4.4 free_block; icman.com.cn/news/78786 §3.3).
+ * (hnwysp.cn/news/103996 §4.4 free_block; icman.com.cn/news/78786 §3.3), or
+ * the prefix cache's evictable list if it holds a key.
  * PKV_ERR_REFCOUNT if the block is already free. */
 PKV_API int pkv_block_decref(pkv_allocator* a, int32_t block);
 /* Reference count (>= 0) of a block, or PKV_ERR_BAD_BLOCK. */
 PKV_API int pkv_block_refcount(const pkv_allocator* a, int32_t block);
+/* Blocks in the free queue (evictable cached blocks are not counted). */
 PKV_API int32_t pkv_num_free(const pkv_allocator* a);
 PKV_API int32_t pkv_num_blocks(const pkv_allocator* a);
 PKV_API int32_t pkv_block_size(const pkv_allocator* a);
@@ -159,6 +162,65 @@ PKV_API int pkv_seq_reserve_batch(pkv_allocator* a, int32_t* tables, int32_t row
  * changes nothing.  Finished, cancelled and failed requests all go through
  * this one call (m.lqnn.cn/news/240480 §5.3; icman.com.cn/news/78786 §6.3). */
 PKV_API int pkv_seq_release(pkv_allocator* a, const int32_t* row, int32_t n_blocks);
+
+/* ---------------------------------------------------------------------------
+ * Block-level prefix cache (host, inside the allocator; off until enabled)
+ *
+ * Requests that share a token prefix share the blocks holding its K/V
+ * (icman.com.cn/news/78786 §3.1-§3.4; hnwysp.cn/news/103996 §4.2, §4.3;
+ * m.lqnn.cn/news/240480 §3.2 step 1).  Each full block of a sequence can be
+ * recorded under a key naming the token prefix that ends with it:
+ *   key_i = SHA-256(key_{i-1} || tokens of block i as little-endian int32),
+ *   key_{-1} = 32 zero bytes
+ * (a collision-resistant hash over the token sequence itself, extended block
+ * by block, icman.com.cn/news/78786 §3.2, §4.4).  A new request's blocks are
+ * matched from the first one until the first miss; a hit increments the
+ * block's count and joins the request's table with no copy (§3.4).  A cached
+ * block whose count falls to zero is not freed: it waits in a
+ * least-recently-released list and can still be matched.  Allocation takes
+ * the free queue first; only when it is empty is the least recently released
+ * cached block evicted (its key dropped) and handed out, so "available"
+ * blocks = free + evictable (§3.3; hnwysp.cn/news/103996 §3.5).  Only full
+ * blocks are cached, so copy-on-write never meets a cached block.
+ * ------------------------------------------------------------------------- */
+
+/* Turn the prefix cache on (idempotent; O(num_blocks) host memory). */
+PKV_API int pkv_prefix_cache_enable(pkv_allocator* a);
+
+/* Chained keys of the full blocks of tokens[0 .. n_tokens): writes
+ * min(n_tokens / block_size, capacity) keys of 32 bytes to keys_out and
+ * returns that count (or a negative status).  Needs no allocator. */
+PKV_API int pkv_prefix_block_keys(const int32_t* tokens, int32_t n_tokens, int32_t block_size, uint8_t* keys_out,
+                                  int32_t capacity);
+
+/* Longest cached prefix of tokens[0 .. n_tokens), at most row_capacity
+ * blocks: the matched block ids go to row_out[0 .. *n_blocks_out) (the
+ * start of the request's table row; its first *n_blocks_out * block_size
+ * tokens need no prefill) and each matched block's count is incremented.
+ * The caller then reserves the rest with pkv_seq_reserve from cur_len =
+ * *n_blocks_out * block_size.  PKV_ERR_INVALID if the cache is off. */
+PKV_API int pkv_prefix_match(pkv_allocator* a, const int32_t* tokens, int32_t n_tokens, int32_t* row_out,
+                             int32_t row_capacity, int32_t* n_blocks_out);
+
+/* Record a sequence's full blocks under their keys once their K/V are
+ * written: blocks row[first_block .. min(n_blocks, n_tokens / block_size)).
+ * Blocks before first_block are the ones pkv_prefix_match returned for
+ * these tokens: the key chain resumes from the key of row[first_block - 1]
+ * (which must be cached), so matched blocks are not hashed again.  A key
+ * already recorded keeps its first block (this one stays an ordinary block);
+ * a block already recorded under the same key is skipped.  Every block
+ * recorded must be held (count >= 1), and a block recorded under a different
+ * key is PKV_ERR_INVALID; both are checked before anything changes.
+ * *n_new_out (may be NULL) = blocks newly recorded. */
+PKV_API int pkv_prefix_register(pkv_allocator* a, const int32_t* tokens, int32_t n_tokens, const int32_t* row,
+                                int32_t n_blocks, int32_t first_block, int32_t* n_new_out);
+
+/* Blocks currently holding a key (held or evictable). */
+PKV_API int32_t pkv_prefix_cached_blocks(const pkv_allocator* a);
+
+/* Evictable cached blocks (count zero), least recently released first: writes
+ * up to `capacity` ids, returns how many. */
+PKV_API int pkv_prefix_lru(const pkv_allocator* a, int32_t* out, int32_t capacity);
 
 /* ---------------------------------------------------------------------------
  * Device operations

@@ -110,10 +110,30 @@ class OracleCachingAllocator(OracleAllocator):
             self.ref[b] += 1
         return hits
 
-    def register(self, tokens, row, n_blocks: int) -> int:
-        """Record the full blocks of a sequence under their keys; returns how many were new."""
-        keys = block_keys(tokens, self.block_size)[:n_blocks]
-        for i, key in enumerate(keys):
+    def register(self, tokens, row, n_blocks: int, first_block: int = 0) -> int:
+        """Record the full blocks ``row[first_block:]`` of a sequence under their keys; returns how many were new.
+
+        Blocks before ``first_block`` are the ones ``match`` returned for
+        these tokens; the key chain resumes from the key of the last of them.
+        """
+        if n_blocks > len(row):
+            raise AllocatorError(ERR_INVALID, "row holds fewer blocks than n_blocks")
+        n = min(n_blocks, len(tokens) // self.block_size)
+        if first_block < 0 or first_block > n:
+            raise AllocatorError(ERR_INVALID, "first_block out of range")
+        prev = ZERO_KEY
+        if first_block > 0:
+            b = int(row[first_block - 1])
+            if b not in self.key_of:
+                raise AllocatorError(ERR_INVALID, f"block {b} before first_block is not cached")
+            prev = self.key_of[b]
+        toks = np.asarray(tokens, dtype="<i4")
+        bs = self.block_size
+        keys = []
+        for i in range(first_block, n):
+            prev = hashlib.sha256(prev + toks[i * bs:(i + 1) * bs].tobytes()).digest()
+            keys.append(prev)
+        for i, key in zip(range(first_block, n), keys):
             b = int(row[i])
             self._check(b)
             if self.ref[b] < 1:
@@ -121,7 +141,7 @@ class OracleCachingAllocator(OracleAllocator):
             if b in self.key_of and self.key_of[b] != key:
                 raise AllocatorError(ERR_INVALID, f"block {b} already holds another key")
         new = 0
-        for i, key in enumerate(keys):
+        for i, key in zip(range(first_block, n), keys):
             b = int(row[i])
             if key in self.index or b in self.key_of:
                 continue

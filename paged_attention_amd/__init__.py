@@ -85,6 +85,12 @@ def _load():
         "pkv_seq_reserve": (ctypes.c_int, [vp, p32, i32, p32, i32, i32, p64, p32, p32]),
         "pkv_seq_reserve_batch": (ctypes.c_int, [vp, p32, i32, p32, p32, p32, i32, p64, p32, i32, p32]),
         "pkv_seq_release": (ctypes.c_int, [vp, p32, i32]),
+        "pkv_prefix_cache_enable": (ctypes.c_int, [vp]),
+        "pkv_prefix_block_keys": (ctypes.c_int, [p32, i32, i32, vp, i32]),
+        "pkv_prefix_match": (ctypes.c_int, [vp, p32, i32, p32, i32, p32]),
+        "pkv_prefix_register": (ctypes.c_int, [vp, p32, i32, p32, i32, i32, p32]),
+        "pkv_prefix_cached_blocks": (i32, [vp]),
+        "pkv_prefix_lru": (ctypes.c_int, [vp, p32, i32]),
         "pkv_append": (ctypes.c_int, [vp, vp, i32, vp, vp, vp, i32, i32, i32, i32, ctypes.c_int, vp]),
         "pkv_copy_blocks": (ctypes.c_int, [ctypes.POINTER(vp), ctypes.POINTER(vp), i32, vp, i32, i32, sz, vp]),
         "pkv_decode_work_groups": (i32, [ctypes.c_int]),
@@ -250,6 +256,47 @@ class BlockAllocator:
     def release_table_row(self, tables: np.ndarray, i: int, n_blocks: int) -> None:
         row = np.ascontiguousarray(tables[i, :n_blocks])
         self.release(row)
+
+    # -- prefix cache --------------------------------------------------
+    def enable_prefix_cache(self) -> None:
+        _check(_lib.pkv_prefix_cache_enable(self._h))
+
+    def prefix_match(self, tokens, capacity: int) -> list:
+        """Blocks of the longest cached prefix of ``tokens`` (at most ``capacity``); each is incremented."""
+        toks = np.ascontiguousarray(tokens, dtype=np.int32)
+        capacity = max(0, min(capacity, len(toks) // self.block_size))   # only full blocks can match
+        out = np.empty(max(1, capacity), dtype=np.int32)
+        n = ctypes.c_int32(0)
+        _check(_lib.pkv_prefix_match(self._h, _i32p(toks) if len(toks) else None, len(toks), _i32p(out),
+                                     capacity, ctypes.byref(n)))
+        return out[:n.value].tolist()
+
+    def prefix_register(self, tokens, row, n_blocks: int, first_block: int = 0) -> int:
+        """Record the full blocks of a sequence under their prefix keys; returns how many were new.
+        ``first_block`` = blocks ``prefix_match`` returned for these tokens (not hashed again)."""
+        toks = np.ascontiguousarray(tokens, dtype=np.int32)
+        arr = np.ascontiguousarray(row, dtype=np.int32)
+        n = ctypes.c_int32(0)
+        _check(_lib.pkv_prefix_register(self._h, _i32p(toks) if len(toks) else None, len(toks),
+                                        _i32p(arr) if len(arr) else None, n_blocks, first_block, ctypes.byref(n)))
+        return n.value
+
+    def prefix_cached(self) -> int:
+        return _check(_lib.pkv_prefix_cached_blocks(self._h))
+
+    def prefix_lru(self) -> list:
+        buf = np.zeros(max(1, self.num_blocks), dtype=np.int32)
+        n = _check(_lib.pkv_prefix_lru(self._h, _i32p(buf), self.num_blocks))
+        return buf[:n].tolist()
+
+
+def prefix_block_keys(tokens, block_size: int) -> list:
+    """Chained SHA-256 keys (32 bytes each) of the full blocks of ``tokens``."""
+    toks = np.ascontiguousarray(tokens, dtype=np.int32)
+    n = len(toks) // block_size if block_size > 0 else 0
+    out = np.zeros(max(1, 32 * n), dtype=np.uint8)
+    got = _check(_lib.pkv_prefix_block_keys(_i32p(toks) if len(toks) else None, len(toks), block_size, _ptr(out), n))
+    return [out[32 * i:32 * (i + 1)].tobytes() for i in range(got)]
 
 
 # ---------------------------------------------------------------------------
@@ -649,5 +696,5 @@ __all__ = [
     "pkv_attention_decode", "pkv_decode_workspace_bytes", "pkv_decode_work_groups",
     "decode_workspace", "PreparedDecode", "PreparedAppend", "version", "LIB_PATH",
     "pkv_append_quant", "pkv_attention_decode_quant", "PreparedDecodeQuant", "PreparedAppendQuant",
-    "CACHE_FORMATS", "pkv_append_attention_decode", "pkv_append_attention_decode_quant", "PreparedAppendDecode",
+    "CACHE_FORMATS", "prefix_block_keys", "pkv_append_attention_decode", "pkv_append_attention_decode_quant", "PreparedAppendDecode",
 ]

@@ -141,7 +141,7 @@ def _random_trace(seed, impl_factory):
             for b in hm:
                 m.drop(b)
             continue
-        log_o.append(("register", o.register(toks, row, len(row))))
+        log_o.append(("register", o.register(toks, row, len(row), len(ho) if rng.random() < 0.5 else 0)))
         log_m.append(("register", m.register(toks, mrow, len(mrow))))
         live.append((toks, row))
         log_o.append(("state", o.free_list(), o.lru_order(), list(o.ref)))
