@@ -61,9 +61,10 @@ def parse():
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="llama7b_layer", choices=["llama7b_layer", "long13b", "full7b_step"])
-    p.add_argument("--component", default="decode", choices=["decode", "prefix_cache"],
+    p.add_argument("--component", default="decode", choices=["decode", "prefix_cache", "swap"],
                    help="decode: the decode step (default, the headline line); prefix_cache: host prefix-cache "
-                        "operations on a shared-system-prompt request stream")
+                        "operations on a shared-system-prompt request stream; swap: preemption swap of a "
+                        "request's blocks to pinned host memory and back")
     p.add_argument("--block-size", type=int, default=16, help="block size of the long13b workload")
     p.add_argument("--work-groups", type=int, default=0, help="decode work-groups (0 = library choice)")
     p.add_argument("--ring", type=int, default=4, help="host staging buffers (how many steps the host may run ahead)")
@@ -210,10 +211,94 @@ def run_prefix_cache(args):
     print(json.dumps(rec), flush=True)
 
 
+HOST_LINK_PEAK_GBS = 64.0  # PCIe 5.0 x16, one direction (MI355X host interface)
+
+
+def run_swap(args):
+    """Preemption swap of one 2048-token request of the 7B shape (32 layers,
+    K and V, fp16, block 16: 128 blocks x 64 pools of 128 KiB = 1 GiB) to
+    pinned host memory and back with pkv_swap_blocks, timed with HIP events."""
+    import torch
+
+    import paged_attention_amd as pkv
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    layers, bs, H, D = 32, 16, 32, 128
+    n_dev, n_host, n_swap = 512, 128, 128
+    pools = [torch.randn((n_dev, bs, H, D), device=dev, dtype=torch.float32).half() for _ in range(2 * layers)]
+    host = [torch.empty((n_host, bs, H, D), dtype=torch.float16).pin_memory() for _ in range(2 * layers)]
+    rng = np.random.default_rng(5)
+    dev_ids = rng.permutation(n_dev)[:n_swap].astype(np.int32)      # the request's scattered blocks
+    host_ids = rng.permutation(n_host)[:n_swap].astype(np.int32)
+    out_pairs = torch.from_numpy(np.stack([dev_ids, host_ids], 1).copy()).to(dev)
+    in_ids = rng.permutation(n_dev)[:n_swap].astype(np.int32)       # swapped back in elsewhere
+    in_pairs = torch.from_numpy(np.stack([host_ids, in_ids], 1).copy()).to(dev)
+    nbytes = n_swap * len(pools) * bs * H * D * 2
+    stream = torch.cuda.current_stream()
+    times = {"out": [], "in": []}
+    for it in range(args.warmup + args.steps):
+        for name, dst, src, pr in (("out", host, pools, out_pairs), ("in", pools, host, in_pairs)):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            pkv.pkv_swap_blocks(dst, src, pr)
+            e1.record(stream)
+            e1.synchronize()
+            if it >= args.warmup:
+                times[name].append(e0.elapsed_time(e1) / 1e3)
+    # the round trip is exact
+    ok = all(torch.equal(pools[i][in_ids[j]], pools[i][dev_ids[j]]) for i in (0, 63) for j in (0, 77))
+    # reference: one contiguous 1 GiB pinned <-> device copy through the runtime
+    big_d = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    big_h = torch.empty(nbytes, dtype=torch.uint8).pin_memory()
+    ref = {}
+    for name, (dst, src) in (("out", (big_h, big_d)), ("in", (big_d, big_h))):
+        ts = []
+        for _ in range(3):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            dst.copy_(src, non_blocking=True)
+            e1.record(stream)
+            e1.synchronize()
+            ts.append(e0.elapsed_time(e1) / 1e3)
+        ref[name] = round(nbytes / min(ts) / 1e9, 2)
+    # oracle on the host: the same block copies between numpy pools, bounded sample
+    from oracle import pool as opool
+    hp = [np.zeros((n_host, bs, H, D), dtype=np.float16) for _ in range(4)]
+    dp = [pools[i].cpu().numpy() for i in range(4)]
+    t0 = time.perf_counter()
+    opool.swap_blocks(hp, dp, list(zip(dev_ids.tolist(), host_ids.tolist())))
+    cpu_s = time.perf_counter() - t0
+    cpu_bytes = n_swap * 4 * bs * H * D * 2
+    gbs = {k: nbytes / float(np.median(v)) / 1e9 for k, v in times.items()}
+    rec = {
+        "metric": "preemption swap GB/s (device <-> pinned host, whole blocks)",
+        "value": round(min(gbs.values()), 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(float(np.median(times["out"]) + np.median(times["in"])) * 1e3, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+        "data": "synthetic (random K/V rows)",
+        "config": {"workload": f"swap out and back in one request of {n_swap * bs} tokens, 7B shape: {layers} layers "
+                               f"x K,V x {n_swap} blocks of {bs * H * D * 2 // 1024} KiB ({nbytes / 2**30:.2f} GiB "
+                               "each way)", "round_trip_exact": bool(ok)},
+        "swap_out_gbs": round(gbs["out"], 2), "swap_in_gbs": round(gbs["in"], 2),
+        "runtime_copy_1gib_gbs": ref,
+        "roofline": {"bound": "host-link", "achieved": round(min(gbs.values()), 2), "peak": HOST_LINK_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(min(gbs.values()) / HOST_LINK_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "swap_blocks_kernel"},
+        "cpu_baseline": {"value": round(cpu_bytes / cpu_s / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+                         "sample": f"oracle.pool.swap_blocks of the same {n_swap} blocks for 4 of the 64 pools "
+                                   "(numpy host copies)"},
+    }
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     args = parse()
     if args.component == "prefix_cache":
         run_prefix_cache(args)
+        return
+    if args.component == "swap":
+        run_swap(args)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported by this single-GPU build "

@@ -250,6 +250,25 @@ PKV_API int pkv_copy_blocks(void* const* k_caches, void* const* v_caches, int32_
                             const int32_t* pairs, int32_t n_pairs, int32_t num_blocks, size_t bytes_per_block,
                             hipStream_t stream);
 
+/* Swap whole blocks between two pool sets, for preemption: one side device
+ * pools, the other pinned host pools (hipHostMalloc), or both device.  A
+ * preempted request's blocks are swapped out to host memory and back in when
+ * blocks free up, instead of being recomputed (icman.com.cn/news/78786 §4.2;
+ * the host tier of l189.com/news/1438543 §3).  For every pool i < num_pools
+ * and pair j: block pairs[j][1] of dst_pools[i] becomes a bit copy of block
+ * pairs[j][0] of src_pools[i] (bytes_per_block each, a multiple of 16; pools
+ * 16-byte aligned).  dst_pools / src_pools are HOST arrays of num_pools
+ * pointers (typically K and V of every layer, plus the scale pools of an
+ * 8-bit cache in a second call); pairs: int32 [n_pairs][2] (device or pinned
+ * host).  Pair ids outside [0, src_num_blocks) / [0, dst_num_blocks) are
+ * skipped; destinations must be distinct (a host-side pkv_allocator for the
+ * swap space hands out such ids).  Every pool and the pairs are checked with
+ * hipPointerGetAttributes before the launch: pageable host memory is
+ * PKV_ERR_INVALID.  One launch per 64 pools; asynchronous on `stream`. */
+PKV_API int pkv_swap_blocks(void* const* dst_pools, const void* const* src_pools, int32_t num_pools,
+                            const int32_t* pairs, int32_t n_pairs, int32_t src_num_blocks, int32_t dst_num_blocks,
+                            size_t bytes_per_block, hipStream_t stream);
+
 /* Work-groups a decode call launches when called with num_work_groups = 0,
  * for caches of `cache_dtype`: one per compute unit of the current device
  * for F32/F16/BF16 caches (256 on MI355X), two per compute unit for I8 and

@@ -50,3 +50,19 @@ def copy_blocks(k_pools, v_pools, pairs) -> None:
         for s, d in zip(srcs, dsts):
             kp[d] = kp[s]
             vp[d] = vp[s]
+
+
+def swap_blocks(dst_pools, src_pools, pairs) -> None:
+    """Copy block ``s`` of every source pool to block ``d`` of the matching destination pool.
+
+    Preemption moves a request's blocks to host memory and back instead of
+    recomputing them (icman.com.cn/news/78786 §4.2): a whole-block bit copy
+    between two pools, like copy-on-write but across pools.  Destinations
+    must be distinct.
+    """
+    dsts = [int(d) for _, d in pairs]
+    if len(set(dsts)) != len(dsts):
+        raise ValueError("swap destinations repeat")
+    for dp, sp in zip(dst_pools, src_pools):
+        for s, d in pairs:
+            dp[int(d)] = sp[int(s)]

@@ -94,6 +94,7 @@ def _load():
         "pkv_append": (ctypes.c_int, [vp, vp, i32, vp, vp, vp, i32, i32, i32, i32, ctypes.c_int, vp]),
         "pkv_copy_blocks": (ctypes.c_int, [ctypes.POINTER(vp), ctypes.POINTER(vp), i32, vp, i32, i32, sz, vp]),
         "pkv_decode_work_groups": (i32, [ctypes.c_int]),
+        "pkv_swap_blocks": (ctypes.c_int, [ctypes.POINTER(vp), ctypes.POINTER(vp), i32, vp, i32, i32, i32, sz, vp]),
         "pkv_decode_workspace_bytes": (sz, [i32, i32, i32, ctypes.c_int, i32]),
         "pkv_attention_decode": (ctypes.c_int, [vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, i32, i32,
                                                 ctypes.c_float, ctypes.c_int, i32, vp, sz, vp]),
@@ -383,6 +384,27 @@ def pkv_copy_blocks(k_caches, v_caches, pairs, stream=None) -> None:
     bytes_per_block = k_caches[0][0].numel() * k_caches[0].element_size()
     _check(_lib.pkv_copy_blocks(karr, varr, nl, _dev(pairs, "pairs", torch.int32, pinned_ok=True), pairs.shape[0], nb,
                                 bytes_per_block, _stream(stream)))
+
+
+def pkv_swap_blocks(dst_pools, src_pools, pairs, stream=None) -> None:
+    """Copy blocks ``pairs[i, 0]`` of every source pool to ``pairs[i, 1]`` of the matching destination
+    pool; one side is device memory, the other device or pinned host memory (preemption swap)."""
+    torch = _torch()
+    if len(dst_pools) != len(src_pools) or not dst_pools:
+        raise InvalidArgument(PKV_ERR_INVALID, "swap_blocks: need matching non-empty pool lists")
+    per_block = src_pools[0][0].numel() * src_pools[0].element_size()
+    for t in list(dst_pools) + list(src_pools):
+        if t.dim() < 2 or t[0].numel() * t.element_size() != per_block or not t.is_contiguous():
+            raise InvalidArgument(PKV_ERR_INVALID, "swap_blocks: pools must be contiguous [num_blocks][...] alike")
+        if not (t.is_cuda or t.is_pinned()):
+            raise InvalidArgument(PKV_ERR_INVALID, "swap_blocks: pools must be device or pinned host tensors")
+    if pairs.dim() != 2 or pairs.shape[1] != 2:
+        raise InvalidArgument(PKV_ERR_INVALID, "swap_blocks: pairs must be [n][2]")
+    n = len(dst_pools)
+    darr = (ctypes.c_void_p * n)(*[t.data_ptr() for t in dst_pools])
+    sarr = (ctypes.c_void_p * n)(*[t.data_ptr() for t in src_pools])
+    _check(_lib.pkv_swap_blocks(darr, sarr, n, _dev(pairs, "pairs", torch.int32, pinned_ok=True), pairs.shape[0],
+                                src_pools[0].shape[0], dst_pools[0].shape[0], per_block, _stream(stream)))
 
 
 def pkv_decode_work_groups(cache_dtype: str = "f16") -> int:
@@ -696,5 +718,5 @@ __all__ = [
     "pkv_attention_decode", "pkv_decode_workspace_bytes", "pkv_decode_work_groups",
     "decode_workspace", "PreparedDecode", "PreparedAppend", "version", "LIB_PATH",
     "pkv_append_quant", "pkv_attention_decode_quant", "PreparedDecodeQuant", "PreparedAppendQuant",
-    "CACHE_FORMATS", "prefix_block_keys", "pkv_append_attention_decode", "pkv_append_attention_decode_quant", "PreparedAppendDecode",
+    "CACHE_FORMATS", "prefix_block_keys", "pkv_swap_blocks", "pkv_append_attention_decode", "pkv_append_attention_decode_quant", "PreparedAppendDecode",
 ]

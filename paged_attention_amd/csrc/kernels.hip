@@ -1,48 +1,10 @@
-// K/V scatter, whole-block copy and decode attention for 16/32-bit caches
-// (fp32, fp16, bf16), plus their C entry points.  The decode kernel and its
-// launch geometry are shared with the 8-bit path (decode_common.h); this file
-// supplies the format policy that loads and scores 16-bit or 32-bit rows.
+// Decode attention for 16/32-bit caches (fp32, fp16, bf16) and its C entry
+// points.  The decode kernel and its launch geometry are shared with the
+// 8-bit path (decode_common.h); this file supplies the format policy that
+// loads and scores 16-bit or 32-bit rows.
 #include "decode_common.h"
 
 namespace {
-
-// ---- append ----------------------------------------------------------------
-
-__global__ void __launch_bounds__(256) append_kernel(const Vec16* __restrict__ k_new, const Vec16* __restrict__ v_new,
-                                                     const int64_t* __restrict__ slots, Vec16* __restrict__ k_cache,
-                                                     Vec16* __restrict__ v_cache, int32_t num_tokens, int32_t row_vec,
-                                                     int64_t total_slots) {
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  const int64_t t = i / row_vec;
-  if (t >= num_tokens) return;
-  const int64_t j = i - t * row_vec;
-  const int64_t s = slots[t];
-  if (s < 0 || s >= total_slots) return;
-  k_cache[s * row_vec + j] = k_new[t * row_vec + j];
-  v_cache[s * row_vec + j] = v_new[t * row_vec + j];
-}
-
-// ---- block copy ------------------------------------------------------------
-
-constexpr int kCopyLayers = 32;  // layer pointers carried per launch
-
-struct LayerPtrs {
-  Vec16* k[kCopyLayers];
-  Vec16* v[kCopyLayers];
-};
-
-__global__ void __launch_bounds__(256) copy_blocks_kernel(LayerPtrs ptrs, const int32_t* __restrict__ pairs,
-                                                          int32_t num_blocks, int64_t vec_per_block) {
-  const int pair = blockIdx.x;
-  const int layer = blockIdx.y;
-  const int32_t src = pairs[2 * pair];
-  const int32_t dst = pairs[2 * pair + 1];
-  if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks || src == dst) return;
-  Vec16* base = blockIdx.z == 0 ? ptrs.k[layer] : ptrs.v[layer];
-  const Vec16* from = base + static_cast<int64_t>(src) * vec_per_block;
-  Vec16* to = base + static_cast<int64_t>(dst) * vec_per_block;
-  for (int64_t i = threadIdx.x; i < vec_per_block; i += blockDim.x) to[i] = from[i];
-}
 
 // ---- decode attention (16/32-bit caches) ------------------------------------
 
@@ -155,50 +117,6 @@ int decode_dense(void* out, const void* q, const void* k_new, const void* v_new,
 }  // namespace
 
 extern "C" {
-
-PKV_API int pkv_append(const void* k_new, const void* v_new, int32_t num_tokens, const int64_t* slot_mapping,
-                       void* k_cache, void* v_cache, int32_t num_blocks, int32_t block_size, int32_t num_heads,
-                       int32_t head_dim, pkv_dtype dtype, hipStream_t stream) {
-  if (num_tokens < 0 || num_blocks <= 0 || num_heads <= 0 || !supported(head_dim, block_size, dtype))
-    return pkv::fail(PKV_ERR_INVALID, "append: unsupported sizes (tokens %d, blocks %d, heads %d, head_dim %d, "
-                                      "block %d, dtype %d)", num_tokens, num_blocks, num_heads, head_dim, block_size,
-                     static_cast<int>(dtype));
-  if (num_tokens == 0) return PKV_OK;
-  if (!k_new || !v_new || !slot_mapping || !k_cache || !v_cache) return pkv::fail(PKV_ERR_INVALID, "append: null pointer");
-  const int64_t row_vec = static_cast<int64_t>(num_heads) * head_dim * dtype_bytes(dtype) / 16;
-  const int64_t total = static_cast<int64_t>(num_tokens) * row_vec;
-  const int64_t blocks = (total + 255) / 256;
-  if (blocks > 0x7fffffff) return pkv::fail(PKV_ERR_INVALID, "append: too many tokens");
-  hipLaunchKernelGGL(append_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, stream,
-                     static_cast<const Vec16*>(k_new), static_cast<const Vec16*>(v_new), slot_mapping,
-                     static_cast<Vec16*>(k_cache), static_cast<Vec16*>(v_cache), num_tokens,
-                     static_cast<int32_t>(row_vec), static_cast<int64_t>(num_blocks) * block_size);
-  return check_launch("append");
-}
-
-PKV_API int pkv_copy_blocks(void* const* k_caches, void* const* v_caches, int32_t num_layers, const int32_t* pairs,
-                            int32_t n_pairs, int32_t num_blocks, size_t bytes_per_block, hipStream_t stream) {
-  if (num_layers < 0 || n_pairs < 0 || num_blocks <= 0 || bytes_per_block == 0 || bytes_per_block % 16 != 0)
-    return pkv::fail(PKV_ERR_INVALID, "copy_blocks: bad sizes (layers %d, pairs %d, blocks %d, bytes %zu)", num_layers,
-                     n_pairs, num_blocks, bytes_per_block);
-  if (n_pairs == 0 || num_layers == 0) return PKV_OK;
-  if (!k_caches || !v_caches || !pairs) return pkv::fail(PKV_ERR_INVALID, "copy_blocks: null pointer");
-  if (n_pairs > 0x7fffffff / 2) return pkv::fail(PKV_ERR_INVALID, "copy_blocks: too many pairs");
-  for (int32_t l0 = 0; l0 < num_layers; l0 += kCopyLayers) {
-    const int32_t nl = num_layers - l0 < kCopyLayers ? num_layers - l0 : kCopyLayers;
-    LayerPtrs ptrs{};
-    for (int32_t i = 0; i < nl; ++i) {
-      if (!k_caches[l0 + i] || !v_caches[l0 + i]) return pkv::fail(PKV_ERR_INVALID, "copy_blocks: null layer pool");
-      ptrs.k[i] = static_cast<Vec16*>(k_caches[l0 + i]);
-      ptrs.v[i] = static_cast<Vec16*>(v_caches[l0 + i]);
-    }
-    hipLaunchKernelGGL(copy_blocks_kernel, dim3(n_pairs, nl, 2), dim3(256), 0, stream, ptrs, pairs, num_blocks,
-                       static_cast<int64_t>(bytes_per_block / 16));
-    int st = check_launch("copy_blocks");
-    if (st != PKV_OK) return st;
-  }
-  return PKV_OK;
-}
 
 PKV_API int32_t pkv_decode_work_groups(pkv_dtype cache_dtype) {
   if (!is_16_32(cache_dtype) && !is_8bit(cache_dtype))
