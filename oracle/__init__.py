@@ -10,7 +10,9 @@ package imports nothing from the product package.
 Floating point is carried in float64 on inputs upcast from their stored dtype;
 integer and byte work (allocator, slot mapping, scatter, block copy) is exact.
 
-Sources (the pages are cited by address and section; none carries a title line):
+Sources (the pages are cited by address and section; none carries a title line;
+``zskr.cn/news/1363082.html`` — windowed KV eviction with recomputation — is
+cited for the cumulative score only):
 
 * ``hnwysp.cn/news/103996`` — KV-cache sizing, shared pool, paging, block table
   with refcounts and copy-on-write, ``alloc_block``/``free_block``.
@@ -29,6 +31,10 @@ Modules:
 * :mod:`oracle.attention` — decode attention by its plain definition.
 * :mod:`oracle.quant` — 8-bit (int8 / FP8 E4M3) K/V rows: per-row absmax
   quantisation on write, exact dequantisation and attention on read.
+* :mod:`oracle.prefix_cache` — block-level prefix cache over the allocator
+  (chained SHA-256 keys, match to the first miss, LRU of zero-count blocks).
+* :mod:`oracle.scores` — cumulative attention score per cached token
+  (decayed running sum of the head-mean softmax weight).
 
 Parity status: every function is pinned by ``tests/test_oracle_*.py`` against
 closed forms printed on the pages, hand-derived traces, library routines
@@ -36,4 +42,4 @@ closed forms printed on the pages, hand-derived traces, library routines
 ``float8_e4m3fn`` type) and invariants; none is "parity unpinned".
 """
 
-from . import allocator, attention, pool, quant, sizes  # noqa: F401
+from . import allocator, attention, pool, prefix_cache, quant, scores, sizes  # noqa: F401
