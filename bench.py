@@ -72,6 +72,8 @@ def parse():
                    help="where kernels read step metadata: pinned host memory in place, or a device copy")
     p.add_argument("--kv-dtype", choices=["auto", "i8", "fp8"], default="auto",
                    help="K/V cache storage: the workload's dtype (auto) or an 8-bit format")
+    p.add_argument("--scores", action="store_true",
+                   help="also update cumulative attention scores per cached token (16/32-bit caches)")
     p.add_argument("--fused", action="store_true",
                    help="scatter and attend in one launch per layer (pkv_append_attention_decode)")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target length of the oracle timing sample")
@@ -416,6 +418,10 @@ def main():
         d_meta = None
         metas = [split(hm) for hm in h_meta]
     per_slot = {}
+    score_bufs = []
+    if args.scores and (kv != "dense" or args.fused):
+        print("--scores runs with a 16/32-bit cache and separate launches", file=sys.stderr)
+        sys.exit(2)
     fused = args.fused
     for r in range(ring):
         key = metas[r][0].data_ptr()
@@ -431,6 +437,15 @@ def main():
                                                             v_caches[l], tb_t, ln_t, max_len, scale=wl.scale,
                                                             work_groups=wgs, workspace=workspace, **qk))
                 per_slot[key] = (None, calls_l)
+            elif kv == "dense" and args.scores:
+                if not score_bufs:
+                    score_bufs.extend([torch.zeros((B, max_len), dtype=torch.float32, device=dev) for _ in range(NL)])
+                per_slot[key] = (
+                    [pkv.PreparedAppend(k_new[0, l], v_new[0, l], sl_t, k_caches[l], v_caches[l])
+                     for l in range(NL)],
+                    [pkv.PreparedDecode(out, q_all[0, l], k_caches[l], v_caches[l], tb_t, ln_t, max_len,
+                                        scale=wl.scale, work_groups=wgs, workspace=workspace,
+                                        scores=score_bufs[l], decay=0.995) for l in range(NL)])
             elif kv == "dense":
                 per_slot[key] = (
                     [pkv.PreparedAppend(k_new[0, l], v_new[0, l], sl_t, k_caches[l], v_caches[l])
@@ -565,7 +580,7 @@ def main():
         "config": {"workload": wl.title + ("" if kv == "dense" else f"; K/V cache {kv} + f32 scale per (token, head)"),
                    "kv_cache": wl.dtype if kv == "dense" else kv, "q_dtype": wl.dtype, "layers": NL, "batch": B, "heads": H, "head_dim": D, "block_size": bs,
                    "pool_blocks": wl.num_blocks, "work_groups": wgs, "metadata": mode,
-                   "launches_per_layer": 1 if fused else 2,
+                   "launches_per_layer": 1 if fused else 2, "cumulative_scores": bool(args.scores),
                    "mean_seq_len": round(kv_per_call / tok_bytes / B, 1), "cow_pairs": n_pairs[0]},
         "hbm_peak_frac": round(value / HBM_PEAK_GBS, 4),
         "token_steps_per_s": round(B * args.steps / elapsed, 1),

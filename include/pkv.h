@@ -412,6 +412,54 @@ PKV_API int pkv_append_attention_decode_quant(void* out, const void* q, const vo
                                               pkv_dtype cache_dtype, int32_t num_work_groups, void* workspace,
                                               size_t workspace_bytes, hipStream_t stream);
 
+/* ---------------------------------------------------------------------------
+ * Cumulative attention score per cached token
+ *
+ * A cached token's importance is the attention past queries paid to it:
+ * after each step every key position adds the weight it received, and the
+ * running total decays exponentially once per step (zskr.cn/news/1363082.html
+ * §3.1 cumulative attention score, §4.1 decay factor).  For every sequence b
+ * and logical position t < L = seq_lens[b]:
+ *   scores[b][t] = decay * scores[b][t] + (1/H) sum_h p_{b,h}(t)
+ * where p_{b,h} is this step's softmax distribution of head h (the weights
+ * the decode output is averaged with).  Positions >= L and sequences with an
+ * invalid length are untouched; a row starts from zero when its sequence
+ * starts (the caller zeroes it).  The decode launch stores each position's
+ * scaled logit and each head's final softmax (max, sum) in
+ * `scores_workspace`; a third kernel on the stream folds them into `scores`.
+ * ------------------------------------------------------------------------- */
+
+/* Bytes of the score workspace: float32 logits [batch][num_heads][max_seq_len]
+ * and float2 [batch][num_heads], each region 256-byte aligned; 0 for an
+ * invalid shape. */
+PKV_API size_t pkv_decode_scores_workspace_bytes(int32_t batch, int32_t num_heads, int32_t max_seq_len);
+
+/* pkv_attention_decode plus the score update above.  scores: device float32
+ * [batch][score_stride], score_stride >= max_seq_len, updated in place;
+ * decay: finite (e.g. 0.995); scores_workspace: device memory of at least
+ * pkv_decode_scores_workspace_bytes(batch, num_heads, max_seq_len).  `out`
+ * is pkv_attention_decode's result (a separate kernel instantiation: it may
+ * differ from it in the last place). */
+PKV_API int pkv_attention_decode_scores(void* out, const void* q, const void* k_cache, const void* v_cache,
+                                        const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                        const int32_t* seq_lens, int32_t max_seq_len, int32_t batch,
+                                        int32_t num_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                        float scale, pkv_dtype dtype, int32_t num_work_groups, void* workspace,
+                                        size_t workspace_bytes, float* scores, int32_t score_stride, float decay,
+                                        void* scores_workspace, size_t scores_workspace_bytes, hipStream_t stream);
+
+/* The same for an 8-bit cache (pkv_attention_decode_quant plus scores). */
+PKV_API int pkv_attention_decode_quant_scores(void* out, const void* q, const void* k_cache, const void* v_cache,
+                                              const float* k_scales, const float* v_scales,
+                                              const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                              const int32_t* seq_lens, int32_t max_seq_len, int32_t batch,
+                                              int32_t num_heads, int32_t head_dim, int32_t block_size,
+                                              int32_t num_blocks, float scale, pkv_dtype q_dtype,
+                                              pkv_dtype cache_dtype, int32_t num_work_groups, void* workspace,
+                                              size_t workspace_bytes, float* scores, int32_t score_stride,
+                                              float decay, void* scores_workspace, size_t scores_workspace_bytes,
+                                              hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

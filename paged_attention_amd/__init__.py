@@ -103,6 +103,14 @@ def _load():
         "pkv_attention_decode_quant": (ctypes.c_int, [vp, vp, vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, i32,
                                                       i32, ctypes.c_float, ctypes.c_int, ctypes.c_int, i32, vp, sz,
                                                       vp]),
+        "pkv_decode_scores_workspace_bytes": (sz, [i32, i32, i32]),
+        "pkv_attention_decode_scores": (ctypes.c_int, [vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, i32, i32,
+                                                       ctypes.c_float, ctypes.c_int, i32, vp, sz, vp, i32,
+                                                       ctypes.c_float, vp, sz, vp]),
+        "pkv_attention_decode_quant_scores": (ctypes.c_int, [vp, vp, vp, vp, vp, vp, vp, i32, vp, i32, i32, i32,
+                                                             i32, i32, i32, ctypes.c_float, ctypes.c_int,
+                                                             ctypes.c_int, i32, vp, sz, vp, i32, ctypes.c_float,
+                                                             vp, sz, vp]),
         "pkv_append_attention_decode": (ctypes.c_int, [vp, vp, vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, i32,
                                                        i32, ctypes.c_float, ctypes.c_int, i32, vp, sz, vp]),
         "pkv_append_attention_decode_quant": (ctypes.c_int, [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, i32, i32,
@@ -477,12 +485,17 @@ class PreparedDecode:
     """
 
     def __init__(self, out, q, k_cache, v_cache, block_tables, seq_lens, max_seq_len, scale=None, work_groups=0,
-                 workspace=None, stream=None):
+                 workspace=None, stream=None, scores=None, decay=0.995, scores_ws=None):
         self._args, ws = _decode_args(out, q, k_cache, v_cache, block_tables, seq_lens, max_seq_len, scale,
                                       work_groups, workspace, stream)
         self._keep = (k_cache, v_cache, block_tables, seq_lens, ws)
         self._shape, self._dtype = tuple(q.shape), q.dtype
         self._fn = _lib.pkv_attention_decode
+        if scores is not None:   # also update cumulative attention scores
+            extra, sws = _score_args(scores, q, max_seq_len, decay, scores_ws)
+            self._args = self._args[:-1] + extra + self._args[-1:]
+            self._keep = self._keep + (scores, sws)
+            self._fn = _lib.pkv_attention_decode_scores
         self._ti = 4   # argument index of block_tables (max_blocks and seq_lens follow)
 
     def _swap(self, i, t, what):
@@ -643,6 +656,55 @@ class PreparedAppendQuant(PreparedDecode):
 
 
 # ---------------------------------------------------------------------------
+# cumulative attention scores
+# ---------------------------------------------------------------------------
+
+def pkv_decode_scores_workspace_bytes(batch, num_heads, max_seq_len) -> int:
+    return int(_lib.pkv_decode_scores_workspace_bytes(batch, num_heads, max_seq_len))
+
+
+def scores_workspace(batch, num_heads, max_seq_len, device="cuda"):
+    """Allocate the workspace a score-updating decode call needs (a uint8 tensor)."""
+    torch = _torch()
+    need = pkv_decode_scores_workspace_bytes(batch, num_heads, max_seq_len)
+    return torch.empty(max(need, 1), dtype=torch.uint8, device=device)
+
+
+def _score_args(scores, q, max_seq_len, decay, scores_ws):
+    torch = _torch()
+    batch = q.shape[0]
+    if scores.dim() != 2 or scores.shape[0] != batch or scores.shape[1] < max_seq_len:
+        raise InvalidArgument(PKV_ERR_INVALID, "scores must be float32 [batch][>= max_seq_len]")
+    if scores_ws is None:
+        scores_ws = scores_workspace(batch, q.shape[1], int(max_seq_len), q.device)
+    return [_dev(scores, "scores", torch.float32), scores.shape[1], float(decay), _dev(scores_ws, "scores_ws"),
+            scores_ws.numel() * scores_ws.element_size()], scores_ws
+
+
+def pkv_attention_decode_scores(out, q, k_cache, v_cache, block_tables, seq_lens, max_seq_len, scores, decay,
+                                scale=None, work_groups=0, workspace=None, scores_ws=None, stream=None) -> None:
+    """Decode attention that also updates ``scores[b][t] = decay * scores[b][t] + mean_h p_{b,h}(t)``."""
+    if q.shape[0] == 0:
+        return
+    args, _ = _decode_args(out, q, k_cache, v_cache, block_tables, seq_lens, max_seq_len, scale, work_groups,
+                           workspace, stream)
+    extra, _ = _score_args(scores, q, max_seq_len, decay, scores_ws)
+    _check(_lib.pkv_attention_decode_scores(*(args[:-1] + extra + args[-1:])))
+
+
+def pkv_attention_decode_quant_scores(out, q, k_cache, v_cache, k_scales, v_scales, block_tables, seq_lens,
+                                      max_seq_len, cache_dtype, scores, decay, scale=None, work_groups=0,
+                                      workspace=None, scores_ws=None, stream=None) -> None:
+    """pkv_attention_decode_scores for an 8-bit cache."""
+    if q.shape[0] == 0:
+        return
+    args, _ = _decode_quant_args(out, q, k_cache, v_cache, k_scales, v_scales, block_tables, seq_lens, max_seq_len,
+                                 cache_dtype, scale, work_groups, workspace, stream)
+    extra, _ = _score_args(scores, q, max_seq_len, decay, scores_ws)
+    _check(_lib.pkv_attention_decode_quant_scores(*(args[:-1] + extra + args[-1:])))
+
+
+# ---------------------------------------------------------------------------
 # scatter + decode in one launch
 # ---------------------------------------------------------------------------
 
@@ -718,5 +780,6 @@ __all__ = [
     "pkv_attention_decode", "pkv_decode_workspace_bytes", "pkv_decode_work_groups",
     "decode_workspace", "PreparedDecode", "PreparedAppend", "version", "LIB_PATH",
     "pkv_append_quant", "pkv_attention_decode_quant", "PreparedDecodeQuant", "PreparedAppendQuant",
-    "CACHE_FORMATS", "prefix_block_keys", "pkv_swap_blocks", "pkv_append_attention_decode", "pkv_append_attention_decode_quant", "PreparedAppendDecode",
+    "CACHE_FORMATS", "prefix_block_keys", "pkv_swap_blocks", "pkv_attention_decode_scores",
+    "pkv_attention_decode_quant_scores", "pkv_decode_scores_workspace_bytes", "scores_workspace", "pkv_append_attention_decode", "pkv_append_attention_decode_quant", "PreparedAppendDecode",
 ]

@@ -207,6 +207,12 @@ struct DecodeArgs {
   float* v_scales;
   const void* k_new;      // appending variant: [batch][H][D] new rows in q's dtype (else unused)
   const void* v_new;
+  float* logits;          // score variant: [batch][H][logit_stride] scaled logits (log2 units), else null
+  float2* final_ml;       // score variant: [batch][H] final (max, sum) of each softmax
+  float* scores;          // score variant: [batch][score_stride] cumulative scores, updated in place
+  int32_t logit_stride;   // = max_seq_len
+  int32_t score_stride;
+  float decay;
   const int32_t* tables;
   const int32_t* lens;
   float* ws_acc;      // [partial slot][H][D]
@@ -274,13 +280,47 @@ __device__ __forceinline__ bool length_ok(int L, const DecodeArgs& a) {
   return L >= 0 && L <= a.max_seq_len && static_cast<int64_t>(L) <= static_cast<int64_t>(a.max_blocks) * BS;
 }
 
+// Lane-wise select v = take ? x : v, written as v_cndmask_b32 with a wave
+// mask: as a C++ select over elements of a register array the compiler may
+// fold the chain into an indexed load from a stack copy of the array.
+__device__ __forceinline__ float select_lanes(bool take, float x, float v) {
+  const uint64_t mask = __builtin_amdgcn_ballot_w64(take);
+  float r;
+  asm("v_cndmask_b32_e64 %0, %1, %2, %3" : "=v"(r) : "v"(v), "v"(x), "s"(mask));
+  return r;
+}
+
+// Stores the chunk's scaled logits s[0 .. valid) of this lane's head at
+// row[0 ..): lane c of the head's LPH lanes (all of which hold every s[u]
+// after the DPP sum) stores positions c, c + W, ... (W = min(LPH, kChunk)),
+// so the head's 8 logits leave in one contiguous store.  Lanes whose head
+// slot is beyond the head count carry row == nullptr and store nothing.
+template <int LPH>
+__device__ __forceinline__ void store_logits(float* row, const float (&s)[kChunk], int c, int valid) {
+  constexpr int W = LPH < kChunk ? LPH : kChunk;
+#pragma unroll
+  for (int k = 0; k < kChunk / W; ++k) {
+    float v = s[k * W];
+#pragma unroll
+    for (int u = 1; u < W; ++u) v = select_lanes(c == u, s[k * W + u], v);
+    const int tok = k * W + c;
+    if (row != nullptr && c < W && tok < valid) row[tok] = v;
+  }
+}
+
+// Kernel variants: plain decode, decode that first stores each sequence's new
+// row (APPEND), decode that also records logits and final softmax states for
+// the cumulative scores (SCORES).
+enum DecodeMode { kPlain = 0, kAppend = 1, kScores = 2 };
+
 // The decode kernel.  KV (a format policy) supplies:
 //   QT, KB, EPL, kMaxWaves       q/out dtype, cache bytes per element, cache
 //                                elements per lane (16 / KB), launch bound;
 //   QReg load_q(const uint8_t*)  this lane's EPL query elements;
 //   chunk<D, BS, LPH>(...)       load kChunk rows of K/V from block `blk`
 //                                starting at in-block position pos0 and fold
-//                                them into the online softmax state;
+//                                them into the online softmax state (and,
+//                                given a logit row, store the scaled logits);
 //   store_new<D, BS, LPH>(...)   (APPEND) store this lane's part of the
 //                                sequence's new K/V row at a pool position.
 // With APPEND the launch first stores each sequence's new row (k_new[b],
@@ -288,8 +328,10 @@ __device__ __forceinline__ bool length_ok(int L, const DecodeArgs& a) {
 // work-group whose range holds a sequence's last chunk is the only one that
 // reads position L - 1, and it stores the row itself, lane by lane, before
 // reading it back with the same lanes: no other work-group is involved.
-template <class KV, int D, int BS, bool APPEND>
+template <class KV, int D, int BS, int MODE>
 __global__ void __launch_bounds__(KV::kMaxWaves * 64) decode_kernel(DecodeArgs a) {
+  constexpr bool APPEND = MODE == kAppend;
+  constexpr bool SCORES = MODE == kScores;
   constexpr int EPL = KV::EPL;
   constexpr int LPH = D / EPL;   // lanes holding one head's row
   constexpr int HPW = 64 / LPH;  // heads per wavefront
@@ -401,6 +443,8 @@ __global__ void __launch_bounds__(KV::kMaxWaves * 64) decode_kernel(DecodeArgs a
 #pragma unroll
       for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
       bool bad_block = false;
+      float* lrow = SCORES && head_ok ? a.logits + (static_cast<int64_t>(b) * a.num_heads + h) * a.logit_stride
+                                      : nullptr;
       int win = -kTableWindow;  // first block index held in `tbl`
       int32_t tbl = 0;
       for (int t0 = t_begin; t0 < t_end; t0 += kChunk) {
@@ -415,11 +459,12 @@ __global__ void __launch_bounds__(KV::kMaxWaves * 64) decode_kernel(DecodeArgs a
         }
         const int32_t blk = __builtin_amdgcn_readlane(tbl, j - win);
         // rows past the segment repeat its last row (masked)
-        KV::template chunk<D, BS, LPH>(qv, a, kp, vp, blk, t0 % BS, hl, row_bytes, t_end - 1 - t0, t_end - t0, m, l,
-                                       acc);
+        KV::template chunk<D, BS, LPH, SCORES>(qv, a, kp, vp, blk, t0 % BS, hl, row_bytes, t_end - 1 - t0,
+                                               t_end - t0, m, l, acc, lrow != nullptr ? lrow + t0 : nullptr, c);
       }
       if (bad_block) l = __builtin_nanf("");
       if (head_ok) {
+        if (SCORES && whole && c == 0) a.final_ml[static_cast<int64_t>(b) * a.num_heads + h] = make_float2(m, l);
         if (whole) {
           const float inv = 1.f / l;
           float o[EPL];
@@ -517,6 +562,7 @@ __global__ void __launch_bounds__(kMergeWaves * 64) decode_merge_kernel(DecodeAr
     o.w += __shfl_xor(o.w, off, 64);
   }
   if (grp != 0) return;
+  if (a.final_ml != nullptr && sub == 0) a.final_ml[static_cast<int64_t>(b) * a.num_heads + h] = make_float2(mx, sum);
   const float inv = 1.f / sum;
   const int64_t out_idx = (static_cast<int64_t>(b) * a.num_heads + h) * D + sub * 4;
   if constexpr (DT == PKV_F32) {
@@ -533,6 +579,42 @@ __global__ void __launch_bounds__(kMergeWaves * 64) decode_merge_kernel(DecodeAr
     }
     *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + out_idx) = make_uint2(lo, hi);
   }
+}
+
+// Cumulative attention scores: one thread per (sequence, position t < L):
+//   scores[b][t] = decay * scores[b][t] + (1/H) sum_h 2^(logit[b][h][t] - M[b][h]) / S[b][h]
+// with (M, S) each head's final softmax max and sum.  A wavefront reads 64
+// consecutive positions of one head per load; a thread issues the loads of
+// kScoreHeads heads before using any, so their latencies overlap.  Sequences
+// whose length the decode kernel refused (it attended to nothing) are left
+// untouched.
+constexpr int kScoreHeads = 16;
+
+__global__ void __launch_bounds__(256) score_kernel(DecodeArgs a) {
+  const int b = blockIdx.y;
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  const int L = a.lens[b];
+  const bool ok = L >= 0 && L <= a.max_seq_len &&
+                  static_cast<int64_t>(L) <= static_cast<int64_t>(a.max_blocks) * a.block_size;
+  if (!ok || t >= L) return;
+  const float* lg = a.logits + static_cast<int64_t>(b) * a.num_heads * a.logit_stride + t;
+  const float2* ml = a.final_ml + static_cast<int64_t>(b) * a.num_heads;
+  float acc = 0.f;
+  for (int h0 = 0; h0 < a.num_heads; h0 += kScoreHeads) {
+    float x[kScoreHeads];
+    float2 f[kScoreHeads];
+#pragma unroll
+    for (int k = 0; k < kScoreHeads; ++k) {
+      const int h = h0 + k < a.num_heads ? h0 + k : a.num_heads - 1;
+      x[k] = lg[static_cast<int64_t>(h) * a.logit_stride];
+      f[k] = ml[h];
+    }
+#pragma unroll
+    for (int k = 0; k < kScoreHeads; ++k)
+      if (h0 + k < a.num_heads) acc += __builtin_amdgcn_exp2f(x[k] - f[k].x) / f[k].y;
+  }
+  float* sp = a.scores + static_cast<int64_t>(b) * a.score_stride + t;
+  *sp = a.decay * *sp + acc / static_cast<float>(a.num_heads);
 }
 
 // ---- host helpers ----------------------------------------------------------
@@ -623,33 +705,80 @@ inline Layout workspace_layout(int32_t batch, int32_t num_heads, int32_t head_di
   return w;
 }
 
-template <class KV, int D, int BS, bool APPEND>
+template <class KV, int D, int BS, int MODE>
 void launch_decode(const DecodeArgs& a, int wg, hipStream_t stream) {
   const size_t lds = 2 * (static_cast<size_t>(a.batch) * a.groups_y + 1) * sizeof(int32_t);
-  hipLaunchKernelGGL((decode_kernel<KV, D, BS, APPEND>), dim3(wg), dim3(a.waves_per_group * 64), lds, stream, a);
+  hipLaunchKernelGGL((decode_kernel<KV, D, BS, MODE>), dim3(wg), dim3(a.waves_per_group * 64), lds, stream, a);
   const int slice_heads = a.waves_per_group * a.heads_per_wave;
   dim3 mgrid(ceil_div(slice_heads, kMergeWaves), a.batch * a.groups_y);
   hipLaunchKernelGGL((decode_merge_kernel<KV::QT, D>), mgrid, dim3(kMergeWaves * 64), 0, stream, a);
+  if (MODE == kScores && a.max_seq_len > 0)
+    hipLaunchKernelGGL(score_kernel, dim3(ceil_div(a.max_seq_len, 256), a.batch), dim3(256), 0, stream, a);
 }
 
-template <class KV, int D, bool APPEND>
+template <class KV, int D, int MODE>
 void launch_decode_bs(const DecodeArgs& a, int wg, int32_t bs, hipStream_t stream) {
   switch (bs) {
-    case 8: launch_decode<KV, D, 8, APPEND>(a, wg, stream); break;
-    case 16: launch_decode<KV, D, 16, APPEND>(a, wg, stream); break;
-    default: launch_decode<KV, D, 32, APPEND>(a, wg, stream); break;
+    case 8: launch_decode<KV, D, 8, MODE>(a, wg, stream); break;
+    case 16: launch_decode<KV, D, 16, MODE>(a, wg, stream); break;
+    default: launch_decode<KV, D, 32, MODE>(a, wg, stream); break;
   }
 }
 
+template <class KV, int MODE>
+void launch_decode_m(const DecodeArgs& a, int wg, int32_t bs, int32_t d, hipStream_t stream) {
+  if (d == 64) launch_decode_bs<KV, 64, MODE>(a, wg, bs, stream);
+  else launch_decode_bs<KV, 128, MODE>(a, wg, bs, stream);
+}
+
+// The mode follows from the arguments: new rows given -> APPEND, a score
+// request -> SCORES (the entry points never ask for both).
 template <class KV>
-void launch_decode_d(const DecodeArgs& a, int wg, int32_t bs, int32_t d, bool append, hipStream_t stream) {
-  if (append) {
-    if (d == 64) launch_decode_bs<KV, 64, true>(a, wg, bs, stream);
-    else launch_decode_bs<KV, 128, true>(a, wg, bs, stream);
-  } else {
-    if (d == 64) launch_decode_bs<KV, 64, false>(a, wg, bs, stream);
-    else launch_decode_bs<KV, 128, false>(a, wg, bs, stream);
-  }
+void launch_decode_d(const DecodeArgs& a, int wg, int32_t bs, int32_t d, hipStream_t stream) {
+  if (a.k_new != nullptr) launch_decode_m<KV, kAppend>(a, wg, bs, d, stream);
+  else if (a.logits != nullptr) launch_decode_m<KV, kScores>(a, wg, bs, d, stream);
+  else launch_decode_m<KV, kPlain>(a, wg, bs, d, stream);
+}
+
+// Cumulative-score workspace: logits [batch][H][max_seq_len] float32, then the
+// final (max, sum) [batch][H] float2, each region 256-byte aligned.
+inline size_t scores_workspace_bytes(int32_t batch, int32_t num_heads, int32_t max_seq_len) {
+  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+  return up(static_cast<size_t>(batch) * num_heads * max_seq_len * sizeof(float)) +
+         up(static_cast<size_t>(batch) * num_heads * sizeof(float2));
+}
+
+// The optional cumulative-score request of a decode call.
+struct ScoreRequest {
+  float* scores;
+  int32_t score_stride;
+  float decay;
+  void* workspace;
+  size_t workspace_bytes;
+};
+
+inline int attach_scores(DecodeArgs& a, const ScoreRequest* sc, int32_t batch, int32_t num_heads,
+                         int32_t max_seq_len, const char* what) {
+  if (sc == nullptr) return PKV_OK;
+  if (sc->scores == nullptr || sc->workspace == nullptr)
+    return pkv::fail(PKV_ERR_INVALID, "%s: null score buffer or score workspace", what);
+  if (sc->score_stride < max_seq_len)
+    return pkv::fail(PKV_ERR_INVALID, "%s: score_stride %d below max_seq_len %d", what, sc->score_stride,
+                     max_seq_len);
+  if (!std::isfinite(sc->decay)) return pkv::fail(PKV_ERR_INVALID, "%s: decay must be finite", what);
+  const size_t need = scores_workspace_bytes(batch, num_heads, max_seq_len);
+  if (sc->workspace_bytes < need)
+    return pkv::fail(PKV_ERR_INVALID, "%s: score workspace of %zu bytes needed, %zu given", what, need,
+                     sc->workspace_bytes);
+  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+  char* base = static_cast<char*>(sc->workspace);
+  a.logits = reinterpret_cast<float*>(base);
+  a.final_ml = reinterpret_cast<float2*>(base + up(static_cast<size_t>(batch) * num_heads * max_seq_len * 4));
+  a.scores = sc->scores;
+  a.logit_stride = max_seq_len;
+  a.score_stride = sc->score_stride;
+  a.decay = sc->decay;
+  return PKV_OK;
 }
 
 // Checks of the scalar arguments of a decode call (made before anything else
@@ -685,6 +814,12 @@ inline int prepare_decode(DecodeArgs& a, const void* q, const void* k_cache, con
   a.v_scales = nullptr;
   a.k_new = nullptr;
   a.v_new = nullptr;
+  a.logits = nullptr;
+  a.final_ml = nullptr;
+  a.scores = nullptr;
+  a.logit_stride = 0;
+  a.score_stride = 0;
+  a.decay = 0.f;
   a.ws_plan = reinterpret_cast<int32_t*>(base + ws.plan);
   a.ws_acc = reinterpret_cast<float*>(base + ws.acc);
   a.ws_ml = reinterpret_cast<float2*>(base + ws.ml);
@@ -716,6 +851,11 @@ int run_sliced(const DecodeArgs& base, void* out, const void* q, const int32_t* 
     if (base.k_new) {
       a.k_new = static_cast<const char*>(base.k_new) + b0 * q_row_bytes;
       a.v_new = static_cast<const char*>(base.v_new) + b0 * q_row_bytes;
+    }
+    if (base.logits) {
+      a.logits = base.logits + static_cast<int64_t>(b0) * base.num_heads * base.logit_stride;
+      a.final_ml = base.final_ml + static_cast<int64_t>(b0) * base.num_heads;
+      a.scores = base.scores + static_cast<int64_t>(b0) * base.score_stride;
     }
     a.tables = block_tables + static_cast<int64_t>(b0) * max_blocks_per_seq;
     a.lens = seq_lens + b0;

@@ -10,9 +10,10 @@ namespace {
 
 // One online-softmax step over a chunk of kChunk tokens whose K/V rows are
 // already in registers.  `valid` = tokens of the chunk inside the segment.
-template <int DT, int EPL, int LPH>
+template <int DT, int EPL, int LPH, bool SCORES>
 __device__ __forceinline__ void softmax_chunk(const Vec16& qv, const Vec16* kr, const Vec16* vr, int valid,
-                                              float scale_log2, float& m, float& l, float* acc) {
+                                              float scale_log2, float& m, float& l, float* acc, float* logit_row,
+                                              int lane_c) {
   float s[kChunk];
   float mc = m;
 #pragma unroll
@@ -20,6 +21,7 @@ __device__ __forceinline__ void softmax_chunk(const Vec16& qv, const Vec16* kr, 
     s[u] = group_sum<LPH>(dot16<DT>(qv, kr[u], 0.f)) * scale_log2;
     if (u < valid) mc = fmaxf(mc, s[u]);
   }
+  if constexpr (SCORES) store_logits<LPH>(logit_row, s, lane_c, valid);
   const float alpha = __builtin_amdgcn_exp2f(m - mc);
   l *= alpha;
 #pragma unroll
@@ -49,10 +51,10 @@ struct DenseKV {
 
   __device__ static Vec16 load_q(const uint8_t* p) { return *reinterpret_cast<const Vec16*>(p); }
 
-  template <int D, int BS, int LPH>
+  template <int D, int BS, int LPH, bool SCORES>
   __device__ static void chunk(const Vec16& qv, const DecodeArgs& a, const uint8_t* kp, const uint8_t* vp, int32_t blk,
                                int pos0, int /*head*/, int64_t row_bytes, int lastu, int valid, float& m, float& l,
-                               float* acc) {
+                               float* acc, float* logit_row, int lane_c) {
     const int64_t base = (static_cast<int64_t>(blk) * BS + pos0) * row_bytes;
     Vec16 kr[kChunk], vr[kChunk];
 #pragma unroll
@@ -61,7 +63,7 @@ struct DenseKV {
       kr[u] = *reinterpret_cast<const Vec16*>(kp + ro);
       vr[u] = *reinterpret_cast<const Vec16*>(vp + ro);
     }
-    softmax_chunk<DT, EPL, LPH>(qv, kr, vr, valid, a.scale_log2, m, l, acc);
+    softmax_chunk<DT, EPL, LPH, SCORES>(qv, kr, vr, valid, a.scale_log2, m, l, acc, logit_row, lane_c);
   }
 
   // The new row is already in the cache's dtype: a 16-byte copy per lane.
@@ -87,7 +89,8 @@ int decode_dense(void* out, const void* q, const void* k_new, const void* v_new,
                  const void* v_cache, const int32_t* block_tables, int32_t max_blocks_per_seq,
                  const int32_t* seq_lens, int32_t max_seq_len, int32_t batch, int32_t num_heads, int32_t head_dim,
                  int32_t block_size, int32_t num_blocks, float scale, pkv_dtype dtype, int32_t num_work_groups,
-                 void* workspace, size_t workspace_bytes, hipStream_t stream, const char* what) {
+                 void* workspace, size_t workspace_bytes, hipStream_t stream, const char* what,
+                 const ScoreRequest* sc = nullptr) {
   if (batch < 0 || num_heads <= 0 || num_blocks <= 0 || max_blocks_per_seq <= 0 || max_seq_len < 0 ||
       !supported(head_dim, block_size, dtype))
     return pkv::fail(PKV_ERR_INVALID, "%s: unsupported sizes (batch %d, heads %d, head_dim %d, block %d, blocks %d, "
@@ -103,13 +106,14 @@ int decode_dense(void* out, const void* q, const void* k_new, const void* v_new,
   if (wg <= 0) return wg;
   a.k_new = k_new;
   a.v_new = v_new;
-  const bool append = k_new != nullptr;
+  const int sst = attach_scores(a, sc, batch, num_heads, max_seq_len, what);
+  if (sst != PKV_OK) return sst;
   const int64_t row = static_cast<int64_t>(num_heads) * head_dim * dtype_bytes(dtype);
   return run_sliced(a, out, q, block_tables, max_blocks_per_seq, seq_lens, batch, row, [&](const DecodeArgs& s) {
     switch (dtype) {
-      case PKV_F32: launch_decode_d<DenseKV<PKV_F32>>(s, wg, block_size, head_dim, append, stream); break;
-      case PKV_F16: launch_decode_d<DenseKV<PKV_F16>>(s, wg, block_size, head_dim, append, stream); break;
-      default: launch_decode_d<DenseKV<PKV_BF16>>(s, wg, block_size, head_dim, append, stream); break;
+      case PKV_F32: launch_decode_d<DenseKV<PKV_F32>>(s, wg, block_size, head_dim, stream); break;
+      case PKV_F16: launch_decode_d<DenseKV<PKV_F16>>(s, wg, block_size, head_dim, stream); break;
+      default: launch_decode_d<DenseKV<PKV_BF16>>(s, wg, block_size, head_dim, stream); break;
     }
   });
 }
@@ -143,6 +147,25 @@ PKV_API int pkv_attention_decode(void* out, const void* q, const void* k_cache, 
   return decode_dense(out, q, nullptr, nullptr, k_cache, v_cache, block_tables, max_blocks_per_seq, seq_lens,
                       max_seq_len, batch, num_heads, head_dim, block_size, num_blocks, scale, dtype, num_work_groups,
                       workspace, workspace_bytes, stream, "attention_decode");
+}
+
+PKV_API size_t pkv_decode_scores_workspace_bytes(int32_t batch, int32_t num_heads, int32_t max_seq_len) {
+  if (batch < 0 || num_heads <= 0 || max_seq_len < 0) return 0;
+  return scores_workspace_bytes(batch, num_heads, max_seq_len);
+}
+
+PKV_API int pkv_attention_decode_scores(void* out, const void* q, const void* k_cache, const void* v_cache,
+                                        const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                        const int32_t* seq_lens, int32_t max_seq_len, int32_t batch,
+                                        int32_t num_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                        float scale, pkv_dtype dtype, int32_t num_work_groups, void* workspace,
+                                        size_t workspace_bytes, float* scores, int32_t score_stride, float decay,
+                                        void* scores_workspace, size_t scores_workspace_bytes,
+                                        hipStream_t stream) {
+  const ScoreRequest sc{scores, score_stride, decay, scores_workspace, scores_workspace_bytes};
+  return decode_dense(out, q, nullptr, nullptr, k_cache, v_cache, block_tables, max_blocks_per_seq, seq_lens,
+                      max_seq_len, batch, num_heads, head_dim, block_size, num_blocks, scale, dtype, num_work_groups,
+                      workspace, workspace_bytes, stream, "attention_decode_scores", &sc);
 }
 
 PKV_API int pkv_append_attention_decode(void* out, const void* q, const void* k_new, const void* v_new,

@@ -157,10 +157,10 @@ struct Q8KV {
     }
   }
 
-  template <int D, int BS, int LPH>
+  template <int D, int BS, int LPH, bool SCORES>
   __device__ static void chunk(const QReg& q, const DecodeArgs& a, const uint8_t* kp, const uint8_t* vp, int32_t blk,
                                int pos0, int head, int64_t row_bytes, int lastu, int valid, float& m, float& l,
-                               float* acc) {
+                               float* acc, float* logit_row, int lane_c) {
     const int64_t base = (static_cast<int64_t>(blk) * BS + pos0) * row_bytes;
     Vec16 kr[kChunk], vr[kChunk];
 #pragma unroll
@@ -191,6 +191,7 @@ struct Q8KV {
       s[u] = group_sum<LPH>(d) * (ks[u] * a.scale_log2);
       if (u < valid) mc = fmaxf(mc, s[u]);
     }
+    if constexpr (SCORES) store_logits<LPH>(logit_row, s, lane_c, valid);
     const float alpha = __builtin_amdgcn_exp2f(m - mc);
     l *= alpha;
 #pragma unroll
@@ -262,12 +263,11 @@ void launch_append_q8(int32_t head_dim, dim3 grid, hipStream_t stream, const voi
 }
 
 template <int KT>
-void launch_decode_q8(const DecodeArgs& a, int wg, int32_t bs, int32_t d, pkv_dtype q_dtype, bool append,
-                      hipStream_t stream) {
+void launch_decode_q8(const DecodeArgs& a, int wg, int32_t bs, int32_t d, pkv_dtype q_dtype, hipStream_t stream) {
   switch (q_dtype) {
-    case PKV_F32: launch_decode_d<Q8KV<PKV_F32, KT>>(a, wg, bs, d, append, stream); break;
-    case PKV_F16: launch_decode_d<Q8KV<PKV_F16, KT>>(a, wg, bs, d, append, stream); break;
-    default: launch_decode_d<Q8KV<PKV_BF16, KT>>(a, wg, bs, d, append, stream); break;
+    case PKV_F32: launch_decode_d<Q8KV<PKV_F32, KT>>(a, wg, bs, d, stream); break;
+    case PKV_F16: launch_decode_d<Q8KV<PKV_F16, KT>>(a, wg, bs, d, stream); break;
+    default: launch_decode_d<Q8KV<PKV_BF16, KT>>(a, wg, bs, d, stream); break;
   }
 }
 
@@ -278,7 +278,7 @@ int decode_q8(void* out, const void* q, const void* k_new, const void* v_new, co
               int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t max_seq_len, int32_t batch,
               int32_t num_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
               pkv_dtype q_dtype, pkv_dtype cache_dtype, int32_t num_work_groups, void* workspace,
-              size_t workspace_bytes, hipStream_t stream, const char* what) {
+              size_t workspace_bytes, hipStream_t stream, const char* what, const ScoreRequest* sc = nullptr) {
   if (batch < 0 || num_heads <= 0 || num_blocks <= 0 || max_blocks_per_seq <= 0 || max_seq_len < 0 ||
       !supported_geometry(head_dim, block_size) || !is_16_32(q_dtype) || !is_8bit(cache_dtype))
     return pkv::fail(PKV_ERR_INVALID, "%s: unsupported sizes (batch %d, heads %d, head_dim %d, block %d, blocks %d, "
@@ -301,13 +301,14 @@ int decode_q8(void* out, const void* q, const void* k_new, const void* v_new, co
   a.v_scales = const_cast<float*>(v_scales);
   a.k_new = k_new;
   a.v_new = v_new;
-  const bool append = k_new != nullptr;
+  const int sst = attach_scores(a, sc, batch, num_heads, max_seq_len, what);
+  if (sst != PKV_OK) return sst;
   const int64_t row = static_cast<int64_t>(num_heads) * head_dim * dtype_bytes(q_dtype);
   return run_sliced(a, out, q, block_tables, max_blocks_per_seq, seq_lens, batch, row, [&](const DecodeArgs& s) {
     if (cache_dtype == PKV_I8)
-      launch_decode_q8<PKV_I8>(s, wg, block_size, head_dim, q_dtype, append, stream);
+      launch_decode_q8<PKV_I8>(s, wg, block_size, head_dim, q_dtype, stream);
     else
-      launch_decode_q8<PKV_FP8_E4M3>(s, wg, block_size, head_dim, q_dtype, append, stream);
+      launch_decode_q8<PKV_FP8_E4M3>(s, wg, block_size, head_dim, q_dtype, stream);
   });
 }
 
@@ -364,6 +365,23 @@ PKV_API int pkv_attention_decode_quant(void* out, const void* q, const void* k_c
   return decode_q8(out, q, nullptr, nullptr, k_cache, v_cache, k_scales, v_scales, block_tables, max_blocks_per_seq,
                    seq_lens, max_seq_len, batch, num_heads, head_dim, block_size, num_blocks, scale, q_dtype,
                    cache_dtype, num_work_groups, workspace, workspace_bytes, stream, "attention_decode_quant");
+}
+
+PKV_API int pkv_attention_decode_quant_scores(void* out, const void* q, const void* k_cache, const void* v_cache,
+                                              const float* k_scales, const float* v_scales,
+                                              const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                              const int32_t* seq_lens, int32_t max_seq_len, int32_t batch,
+                                              int32_t num_heads, int32_t head_dim, int32_t block_size,
+                                              int32_t num_blocks, float scale, pkv_dtype q_dtype,
+                                              pkv_dtype cache_dtype, int32_t num_work_groups, void* workspace,
+                                              size_t workspace_bytes, float* scores, int32_t score_stride,
+                                              float decay, void* scores_workspace, size_t scores_workspace_bytes,
+                                              hipStream_t stream) {
+  const ScoreRequest sc{scores, score_stride, decay, scores_workspace, scores_workspace_bytes};
+  return decode_q8(out, q, nullptr, nullptr, k_cache, v_cache, k_scales, v_scales, block_tables, max_blocks_per_seq,
+                   seq_lens, max_seq_len, batch, num_heads, head_dim, block_size, num_blocks, scale, q_dtype,
+                   cache_dtype, num_work_groups, workspace, workspace_bytes, stream, "attention_decode_quant_scores",
+                   &sc);
 }
 
 PKV_API int pkv_append_attention_decode_quant(void* out, const void* q, const void* k_new, const void* v_new,
