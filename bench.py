@@ -60,7 +60,8 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=10)
-    p.add_argument("--workload", default="llama7b_layer", choices=["llama7b_layer", "long13b", "full7b_step"])
+    p.add_argument("--workload", default="llama7b_layer",
+                   choices=["llama7b_layer", "prefix_cow", "long13b", "full7b_step"])
     p.add_argument("--component", default="decode", choices=["decode", "prefix_cache", "swap"],
                    help="decode: the decode step (default, the headline line); prefix_cache: host prefix-cache "
                         "operations on a shared-system-prompt request stream; swap: preemption swap of a "
@@ -318,6 +319,8 @@ def main():
         wl = workloads.llama7b_layer()
     elif args.workload == "long13b":
         wl = workloads.long13b(args.block_size)
+    elif args.workload == "prefix_cow":
+        wl = workloads.prefix_cow()
     else:
         # 32 layers; the pool takes 85 % of the free device memory.
         free, _ = torch.cuda.mem_get_info()
@@ -353,12 +356,24 @@ def main():
             nblk[s] = len(row)
             done[s] = wl.prefix_len
     hist = np.maximum(lens0 - 1 - done, 0)
-    sl, pr = alloc.reserve_batch(tables, nblk, done, hist)
-    assert len(pr) == 0
+    sl, hist_pairs = alloc.reserve_batch(tables, nblk, done, hist)
     history.append(sl)
     cur = (done + hist).astype(np.int32)
+    # A shared prefix that ends inside a block is copied for every sharer but
+    # the last at its first private token: rows of the prefix are written,
+    # then those blocks copied, then the private rows.
+    n_first = len(history[0]) if len(history) > 1 else 0
     slots_hist = torch.from_numpy(np.concatenate(history)).to(dev)
     n_hist = slots_hist.numel()
+    d_hist_pairs = torch.from_numpy(np.asarray(hist_pairs, dtype=np.int32).reshape(-1, 2)).to(dev)
+    # Shared full blocks are read once per sharer (logical bytes) but need
+    # leave HBM only once (unique bytes); sharing no longer changes once the
+    # history is in place (new tokens land in private blocks).
+    shared_extra_tokens = 0
+    for blk_id in {int(x) for b in range(B) for x in tables[b, : nblk[b]]}:
+        r = alloc.refcount(blk_id)
+        if r > 1:
+            shared_extra_tokens += (r - 1) * bs
     k_caches, v_caches, k_scales, v_scales = [], [], [], []
     gen = torch.Generator(device=dev)
     for layer in range(NL):
@@ -368,8 +383,12 @@ def main():
             k_scales.append(torch.empty((wl.num_blocks, H, bs), dtype=torch.float32, device=dev))
             v_scales.append(torch.empty_like(k_scales[-1]))
         gen.manual_seed(5000 + layer)
-        for a0 in range(0, n_hist, 1 << 16):   # history rows drawn on the device, in slices
-            a1 = min(n_hist, a0 + (1 << 16))
+        cuts = sorted({0, n_first, n_hist} | set(range(0, n_hist, 1 << 16)))
+        for a0, a1 in zip(cuts[:-1], cuts[1:]):   # history rows drawn on the device, in slices
+            if a0 == n_first and n_first > 0 and len(hist_pairs):
+                pkv.pkv_copy_blocks([kc], [vc], d_hist_pairs)
+                if kv != "dense":
+                    pkv.pkv_copy_blocks([k_scales[-1]], [v_scales[-1]], d_hist_pairs)
             kr = torch.randn((a1 - a0, H, D), generator=gen, device=dev, dtype=torch.float32).to(tdt)
             vr = torch.randn((a1 - a0, H, D), generator=gen, device=dev, dtype=torch.float32).to(tdt)
             if kv == "dense":
@@ -519,11 +538,16 @@ def main():
                             for i in range(args.warmup, total_steps) for layer in range(NL)])) / 1e3
     kv_total = float(sum(kv_bytes))
     value = kv_total / elapsed / 1e9
+    unique_total = kv_total - shared_extra_tokens * tok_bytes * NL * len(kv_bytes)
+    unique_gbs = unique_total / elapsed / 1e9
     # Algorithmic bytes of one decode-attention call (mean over timed steps, one
     # layer): K+V rows read (8-bit: codes and scales) + q in + out +
     # block-table entries + lengths.
     kv_per_call = float(np.mean(kv_bytes)) / NL
-    algo = kv_per_call + 2 * B * H * D * esz + 4 * float(np.mean(table_entries)) + 4 * B
+    # With shared blocks only the unique bytes must leave HBM (the rest are
+    # cache hits), so the roofline counts unique K/V bytes.
+    unique_kv_per_call = kv_per_call - shared_extra_tokens * tok_bytes
+    algo = unique_kv_per_call + 2 * B * H * D * esz + 4 * float(np.mean(table_entries)) + 4 * B
     if fused:   # the launch also reads the new rows and writes them (8-bit: codes and scales) into the pools
         algo += 2 * B * H * D * esz + B * tok_bytes
     achieved = algo / attn_s / 1e9
@@ -582,13 +606,15 @@ def main():
                    "pool_blocks": wl.num_blocks, "work_groups": wgs, "metadata": mode,
                    "launches_per_layer": 1 if fused else 2, "cumulative_scores": bool(args.scores),
                    "mean_seq_len": round(kv_per_call / tok_bytes / B, 1), "cow_pairs": n_pairs[0]},
-        "hbm_peak_frac": round(value / HBM_PEAK_GBS, 4),
+        "hbm_peak_frac": round(unique_gbs / HBM_PEAK_GBS, 4),
+        "unique_kv_gbs": round(unique_gbs, 2),
         "token_steps_per_s": round(B * args.steps / elapsed, 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "kernel": ("pkv_append_attention_decode" if fused else "pkv_attention_decode")
                      + ("_quant" if kv != "dense" else "") + " (decode_kernel + decode_merge_kernel)",
-                     "avg_call_us": round(attn_s * 1e6, 2), "algorithmic_bytes_per_call": int(algo)},
+                     "avg_call_us": round(attn_s * 1e6, 2), "algorithmic_bytes_per_call": int(algo),
+                     "logical_kv_bytes_per_call": int(kv_per_call)},
         "cpu_baseline": cpu,
     }
     rec.update(extra)
