@@ -24,7 +24,9 @@ outputs stay in the workload's dtype.
 
 Prints one JSON line.  ``value`` is KV GB/s over the whole timed step (K+V
 bytes attention reads / step time).  ``roofline`` reports the decode-attention
-call (decode kernel + merge kernel) timed with HIP events on its stream, and
+call (decode kernel + merge kernel) timed with HIP events that the call itself
+records at its first kernel's start and its last kernel's end
+(pkv_time_next_decode), and
 the HBM traffic rocprofv3 counted for it when the recorded counters belong to
 the current kernel source.  ``cpu_baseline`` times the oracle on a bounded
 sample of the same workload on the host cores.
@@ -77,6 +79,8 @@ def parse():
                    help="also update cumulative attention scores per cached token (16/32-bit caches)")
     p.add_argument("--fused", action="store_true",
                    help="scatter and attend in one launch per layer (pkv_append_attention_decode)")
+    p.add_argument("--time-every", type=int, default=8,
+                   help="time the attention call on every N-th timed step (timing a call costs the step ~6 us)")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target length of the oracle timing sample")
     p.add_argument("--no-cpu", action="store_true", help="skip the cpu_baseline leg")
     p.add_argument("--copy-calibration", action="store_true",
@@ -482,8 +486,21 @@ def main():
     torch.cuda.synchronize()
 
     ones = np.ones(B, dtype=np.int32)
-    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(NL)]
-          for _ in range(total_steps)]
+    # The decode call's own first-kernel start and last-kernel end
+    # (pkv_time_next_decode): an event recorded between the append and the
+    # decode kernel would delay the decode kernel's start by about 4 us and
+    # count that delay as attention time.  Timing a call still costs its step
+    # about 6 us of queue time, so only every time_every-th timed step is
+    # timed (all layers of it).  Each event is recorded once here so that its
+    # HIP event exists.
+    every = max(1, args.time_every)
+    timed = [i for i in range(args.warmup, total_steps) if (i - args.warmup) % every == 0]
+    ev = {i: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(NL)]
+          for i in timed}
+    for pairs in ev.values():
+        for e0, e1 in pairs:
+            e0.record(stream)
+            e1.record(stream)
     released = [torch.cuda.Event() for _ in range(ring)]
     kv_bytes, table_entries, n_pairs = [], [], [0]
 
@@ -510,13 +527,14 @@ def main():
         appends, decodes = calls[r]
         for layer in range(NL):
             if fused:                                                  # 4 + 5 in one launch
-                ev[i][layer][0].record(stream)
+                if i in ev:
+                    pkv.pkv_time_next_decode(*ev[i][layer])
                 decodes[layer].launch(q_all[i, layer], k_new[i, layer], v_new[i, layer])
             else:
                 appends[layer].launch(k_new[i, layer], v_new[i, layer])    # 4. scatter new rows
-                ev[i][layer][0].record(stream)
+                if i in ev:
+                    pkv.pkv_time_next_decode(*ev[i][layer])
                 decodes[layer].launch(q_all[i, layer])                     # 5. decode attention
-            ev[i][layer][1].record(stream)
         if d_meta is None:                                             # read in place until here
             released[r].record(stream)
         h_done[r] = released[r]
@@ -534,20 +552,20 @@ def main():
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
-    attn_s = float(np.mean([ev[i][layer][0].elapsed_time(ev[i][layer][1])
-                            for i in range(args.warmup, total_steps) for layer in range(NL)])) / 1e3
+    attn_s = float(np.mean([ev[i][layer][0].elapsed_time(ev[i][layer][1]) for i in timed for layer in range(NL)])) / 1e3
     kv_total = float(sum(kv_bytes))
     value = kv_total / elapsed / 1e9
     unique_total = kv_total - shared_extra_tokens * tok_bytes * NL * len(kv_bytes)
     unique_gbs = unique_total / elapsed / 1e9
-    # Algorithmic bytes of one decode-attention call (mean over timed steps, one
-    # layer): K+V rows read (8-bit: codes and scales) + q in + out +
-    # block-table entries + lengths.
-    kv_per_call = float(np.mean(kv_bytes)) / NL
+    # Algorithmic bytes of one decode-attention call (mean over the steps whose
+    # calls were timed, one layer): K+V rows read (8-bit: codes and scales) +
+    # q in + out + block-table entries + lengths.
+    sampled = [i - args.warmup for i in timed]
+    kv_per_call = float(np.mean([kv_bytes[s] for s in sampled])) / NL
     # With shared blocks only the unique bytes must leave HBM (the rest are
     # cache hits), so the roofline counts unique K/V bytes.
     unique_kv_per_call = kv_per_call - shared_extra_tokens * tok_bytes
-    algo = unique_kv_per_call + 2 * B * H * D * esz + 4 * float(np.mean(table_entries)) + 4 * B
+    algo = unique_kv_per_call + 2 * B * H * D * esz + 4 * float(np.mean([table_entries[s] for s in sampled])) + 4 * B
     if fused:   # the launch also reads the new rows and writes them (8-bit: codes and scales) into the pools
         algo += 2 * B * H * D * esz + B * tok_bytes
     achieved = algo / attn_s / 1e9
@@ -614,7 +632,9 @@ def main():
                      "kernel": ("pkv_append_attention_decode" if fused else "pkv_attention_decode")
                      + ("_quant" if kv != "dense" else "") + " (decode_kernel + decode_merge_kernel)",
                      "avg_call_us": round(attn_s * 1e6, 2), "algorithmic_bytes_per_call": int(algo),
-                     "logical_kv_bytes_per_call": int(kv_per_call)},
+                     "logical_kv_bytes_per_call": int(kv_per_call), "timed_calls": len(timed) * NL,
+                     "timing": "kernel timestamps of the call's first and last kernel, every "
+                               f"{every}-th timed step"},
         "cpu_baseline": cpu,
     }
     rec.update(extra)

@@ -79,6 +79,19 @@ PKV_API const char* pkv_last_error(void);
 /* Library interface version (major * 100 + minor). */
 PKV_API int pkv_version(void);
 
+/* Kernel timing of the calling thread's next decode-attention call (any
+ * pkv_*attention_decode* entry point): `start` is recorded when that call's
+ * first kernel starts and `stop` when its last kernel ends, as timestamps of
+ * those kernels themselves (hipExtLaunchKernelGGL), so no extra packet
+ * enters the queue — on MI355X an event recorded between two kernels delays
+ * the second one's start by about 4 us, which would be counted as the
+ * call's time.  Either event may be null.  The caller creates both
+ * (hipEventCreate, timing enabled) and reads them with hipEventElapsedTime
+ * after the stream has passed the call.  The request is consumed by the next
+ * decode call on this thread, whether that call succeeds or not (a call that
+ * fails before enqueueing leaves the events unrecorded).  Always PKV_OK. */
+PKV_API int pkv_time_next_decode(hipEvent_t start, hipEvent_t stop);
+
 /* ---------------------------------------------------------------------------
  * Host block allocator
  *

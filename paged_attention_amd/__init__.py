@@ -71,6 +71,7 @@ def _load():
         "pkv_strerror": (ctypes.c_char_p, [ctypes.c_int]),
         "pkv_last_error": (ctypes.c_char_p, []),
         "pkv_version": (ctypes.c_int, []),
+        "pkv_time_next_decode": (ctypes.c_int, [vp, vp]),
         "pkv_allocator_create": (ctypes.c_int, [i32, i32, p32, ctypes.POINTER(vp)]),
         "pkv_allocator_destroy": (None, [vp]),
         "pkv_block_alloc": (ctypes.c_int, [vp, p32]),
@@ -413,6 +414,28 @@ def pkv_swap_blocks(dst_pools, src_pools, pairs, stream=None) -> None:
     sarr = (ctypes.c_void_p * n)(*[t.data_ptr() for t in src_pools])
     _check(_lib.pkv_swap_blocks(darr, sarr, n, _dev(pairs, "pairs", torch.int32, pinned_ok=True), pairs.shape[0],
                                 src_pools[0].shape[0], dst_pools[0].shape[0], per_block, _stream(stream)))
+
+
+def _event_handle(ev):
+    if ev is None:
+        return None
+    if isinstance(ev, int):
+        return ev
+    h = ev.cuda_event   # torch.cuda.Event: the HIP event exists once it has been recorded
+    if not h:
+        raise InvalidArgument(PKV_ERR_INVALID, "time_next_decode: record the event once before passing it")
+    return h
+
+
+def pkv_time_next_decode(start=None, stop=None) -> None:
+    """Kernel timestamps of this thread's next decode-attention call.
+
+    ``start`` / ``stop`` are ``torch.cuda.Event(enable_timing=True)`` objects
+    that have been recorded at least once (or raw HIP event handles); the next
+    decode call records ``start`` at the start of its first kernel and
+    ``stop`` at the end of its last, with no extra packet on the queue.
+    """
+    _check(_lib.pkv_time_next_decode(_event_handle(start), _event_handle(stop)))
 
 
 def pkv_decode_work_groups(cache_dtype: str = "f16") -> int:

@@ -29,6 +29,7 @@
 // gets its own copy of the templates it instantiates.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -133,6 +134,13 @@ __device__ __forceinline__ void store_row(uint8_t* p, const float* in) {
   static_assert(N % per == 0, "whole 16-byte stores only");
 #pragma unroll
   for (int k = 0; k < N / per; ++k) reinterpret_cast<Vec16*>(p)[k] = pack16<DT>(in + k * per);
+}
+
+// A 16-byte load marked non-temporal (`nt`): for rows a call reads once,
+// so that the stream does not displace other lines in the caches.
+__device__ __forceinline__ Vec16 stream_load(const uint8_t* p) {
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  return __builtin_bit_cast(Vec16, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p)));
 }
 
 // DPP lane permutes inside a row of 16 lanes.
@@ -705,39 +713,48 @@ inline Layout workspace_layout(int32_t batch, int32_t num_heads, int32_t head_di
   return w;
 }
 
+// Kernels of one launch_decode: the decode kernel, the merge kernel and, for
+// a score request, the score kernel.  `tm.start` goes with the first of them
+// and `tm.stop` with the last (kernel timestamps, no extra queue packets).
 template <class KV, int D, int BS, int MODE>
-void launch_decode(const DecodeArgs& a, int wg, hipStream_t stream) {
+void launch_decode(const DecodeArgs& a, int wg, hipStream_t stream, const pkv::CallEvents& tm) {
   const size_t lds = 2 * (static_cast<size_t>(a.batch) * a.groups_y + 1) * sizeof(int32_t);
-  hipLaunchKernelGGL((decode_kernel<KV, D, BS, MODE>), dim3(wg), dim3(a.waves_per_group * 64), lds, stream, a);
+  const bool scores = MODE == kScores && a.max_seq_len > 0;
+  hipExtLaunchKernelGGL((decode_kernel<KV, D, BS, MODE>), dim3(wg), dim3(a.waves_per_group * 64), lds, stream,
+                        tm.start, nullptr, 0, a);
   const int slice_heads = a.waves_per_group * a.heads_per_wave;
   dim3 mgrid(ceil_div(slice_heads, kMergeWaves), a.batch * a.groups_y);
-  hipLaunchKernelGGL((decode_merge_kernel<KV::QT, D>), mgrid, dim3(kMergeWaves * 64), 0, stream, a);
-  if (MODE == kScores && a.max_seq_len > 0)
-    hipLaunchKernelGGL(score_kernel, dim3(ceil_div(a.max_seq_len, 256), a.batch), dim3(256), 0, stream, a);
+  hipExtLaunchKernelGGL((decode_merge_kernel<KV::QT, D>), mgrid, dim3(kMergeWaves * 64), 0, stream, nullptr,
+                        scores ? nullptr : tm.stop, 0, a);
+  if (scores)
+    hipExtLaunchKernelGGL(score_kernel, dim3(ceil_div(a.max_seq_len, 256), a.batch), dim3(256), 0, stream, nullptr,
+                          tm.stop, 0, a);
 }
 
 template <class KV, int D, int MODE>
-void launch_decode_bs(const DecodeArgs& a, int wg, int32_t bs, hipStream_t stream) {
+void launch_decode_bs(const DecodeArgs& a, int wg, int32_t bs, hipStream_t stream, const pkv::CallEvents& tm) {
   switch (bs) {
-    case 8: launch_decode<KV, D, 8, MODE>(a, wg, stream); break;
-    case 16: launch_decode<KV, D, 16, MODE>(a, wg, stream); break;
-    default: launch_decode<KV, D, 32, MODE>(a, wg, stream); break;
+    case 8: launch_decode<KV, D, 8, MODE>(a, wg, stream, tm); break;
+    case 16: launch_decode<KV, D, 16, MODE>(a, wg, stream, tm); break;
+    default: launch_decode<KV, D, 32, MODE>(a, wg, stream, tm); break;
   }
 }
 
 template <class KV, int MODE>
-void launch_decode_m(const DecodeArgs& a, int wg, int32_t bs, int32_t d, hipStream_t stream) {
-  if (d == 64) launch_decode_bs<KV, 64, MODE>(a, wg, bs, stream);
-  else launch_decode_bs<KV, 128, MODE>(a, wg, bs, stream);
+void launch_decode_m(const DecodeArgs& a, int wg, int32_t bs, int32_t d, hipStream_t stream,
+                     const pkv::CallEvents& tm) {
+  if (d == 64) launch_decode_bs<KV, 64, MODE>(a, wg, bs, stream, tm);
+  else launch_decode_bs<KV, 128, MODE>(a, wg, bs, stream, tm);
 }
 
 // The mode follows from the arguments: new rows given -> APPEND, a score
 // request -> SCORES (the entry points never ask for both).
 template <class KV>
-void launch_decode_d(const DecodeArgs& a, int wg, int32_t bs, int32_t d, hipStream_t stream) {
-  if (a.k_new != nullptr) launch_decode_m<KV, kAppend>(a, wg, bs, d, stream);
-  else if (a.logits != nullptr) launch_decode_m<KV, kScores>(a, wg, bs, d, stream);
-  else launch_decode_m<KV, kPlain>(a, wg, bs, d, stream);
+void launch_decode_d(const DecodeArgs& a, int wg, int32_t bs, int32_t d, hipStream_t stream,
+                     const pkv::CallEvents& tm) {
+  if (a.k_new != nullptr) launch_decode_m<KV, kAppend>(a, wg, bs, d, stream, tm);
+  else if (a.logits != nullptr) launch_decode_m<KV, kScores>(a, wg, bs, d, stream, tm);
+  else launch_decode_m<KV, kPlain>(a, wg, bs, d, stream, tm);
 }
 
 // Cumulative-score workspace: logits [batch][H][max_seq_len] float32, then the
@@ -835,16 +852,19 @@ inline int prepare_decode(DecodeArgs& a, const void* q, const void* k_cache, con
   return wg;
 }
 
-// Runs `launch(a)` over slices of the batch small enough for the on-chip
+// Runs `launch(a, tm)` over slices of the batch small enough for the on-chip
 // prefix arrays; the slices run one after another on the stream and share the
-// workspace.
+// workspace.  The timing events go to the first slice's first kernel and the
+// last slice's last kernel.
 template <class Launch>
 int run_sliced(const DecodeArgs& base, void* out, const void* q, const int32_t* block_tables,
                int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t batch, int64_t q_row_bytes,
-               Launch launch) {
+               const pkv::CallEvents& timing, Launch launch) {
   DecodeArgs a = base;
   const int32_t per_launch = kMaxVirtual / a.groups_y;
   for (int32_t b0 = 0; b0 < batch; b0 += per_launch) {
+    const pkv::CallEvents tm{b0 == 0 ? timing.start : nullptr,
+                             b0 + per_launch >= batch ? timing.stop : nullptr};
     a.batch = batch - b0 < per_launch ? batch - b0 : per_launch;
     a.out = static_cast<char*>(out) + b0 * q_row_bytes;
     a.q = static_cast<const char*>(q) + b0 * q_row_bytes;
@@ -859,7 +879,7 @@ int run_sliced(const DecodeArgs& base, void* out, const void* q, const int32_t* 
     }
     a.tables = block_tables + static_cast<int64_t>(b0) * max_blocks_per_seq;
     a.lens = seq_lens + b0;
-    launch(a);
+    launch(a, tm);
     const int st = check_launch("attention_decode");
     if (st != PKV_OK) return st;
   }

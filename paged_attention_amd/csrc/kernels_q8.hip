@@ -163,11 +163,17 @@ struct Q8KV {
                                float* acc, float* logit_row, int lane_c) {
     const int64_t base = (static_cast<int64_t>(blk) * BS + pos0) * row_bytes;
     Vec16 kr[kChunk], vr[kChunk];
+    // As in the 16/32-bit path, K codes take ordinary loads and V codes
+    // non-temporal ones.  Measured on MI355X, us per call (ordinary / V
+    // non-temporal / both): FP8 7B-shaped layer 65.7 / 63.0 / 68.3; int8
+    // 13B-shaped long context 151.0 / 128.7 / -; FP8 with 64 sequences
+    // sharing a 520-token prefix 75.4 / 82.6 / - (the one workload here that
+    // loses: sharers re-read V prefix blocks that are no longer cached).
 #pragma unroll
     for (int u = 0; u < kChunk; ++u) {
       const int64_t ro = base + static_cast<int64_t>(u < lastu ? u : lastu) * row_bytes;
       kr[u] = *reinterpret_cast<const Vec16*>(kp + ro);
-      vr[u] = *reinterpret_cast<const Vec16*>(vp + ro);
+      vr[u] = stream_load(vp + ro);
     }
     // Scales of the chunk's 8 positions (positions past the segment are
     // read but never used: their weights are selected to zero).
@@ -263,11 +269,12 @@ void launch_append_q8(int32_t head_dim, dim3 grid, hipStream_t stream, const voi
 }
 
 template <int KT>
-void launch_decode_q8(const DecodeArgs& a, int wg, int32_t bs, int32_t d, pkv_dtype q_dtype, hipStream_t stream) {
+void launch_decode_q8(const DecodeArgs& a, int wg, int32_t bs, int32_t d, pkv_dtype q_dtype, hipStream_t stream,
+                      const pkv::CallEvents& tm) {
   switch (q_dtype) {
-    case PKV_F32: launch_decode_d<Q8KV<PKV_F32, KT>>(a, wg, bs, d, stream); break;
-    case PKV_F16: launch_decode_d<Q8KV<PKV_F16, KT>>(a, wg, bs, d, stream); break;
-    default: launch_decode_d<Q8KV<PKV_BF16, KT>>(a, wg, bs, d, stream); break;
+    case PKV_F32: launch_decode_d<Q8KV<PKV_F32, KT>>(a, wg, bs, d, stream, tm); break;
+    case PKV_F16: launch_decode_d<Q8KV<PKV_F16, KT>>(a, wg, bs, d, stream, tm); break;
+    default: launch_decode_d<Q8KV<PKV_BF16, KT>>(a, wg, bs, d, stream, tm); break;
   }
 }
 
@@ -279,6 +286,7 @@ int decode_q8(void* out, const void* q, const void* k_new, const void* v_new, co
               int32_t num_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
               pkv_dtype q_dtype, pkv_dtype cache_dtype, int32_t num_work_groups, void* workspace,
               size_t workspace_bytes, hipStream_t stream, const char* what, const ScoreRequest* sc = nullptr) {
+  const pkv::CallEvents timing = pkv::take_call_events();  // consumed by this call, whatever its outcome
   if (batch < 0 || num_heads <= 0 || num_blocks <= 0 || max_blocks_per_seq <= 0 || max_seq_len < 0 ||
       !supported_geometry(head_dim, block_size) || !is_16_32(q_dtype) || !is_8bit(cache_dtype))
     return pkv::fail(PKV_ERR_INVALID, "%s: unsupported sizes (batch %d, heads %d, head_dim %d, block %d, blocks %d, "
@@ -304,12 +312,13 @@ int decode_q8(void* out, const void* q, const void* k_new, const void* v_new, co
   const int sst = attach_scores(a, sc, batch, num_heads, max_seq_len, what);
   if (sst != PKV_OK) return sst;
   const int64_t row = static_cast<int64_t>(num_heads) * head_dim * dtype_bytes(q_dtype);
-  return run_sliced(a, out, q, block_tables, max_blocks_per_seq, seq_lens, batch, row, [&](const DecodeArgs& s) {
-    if (cache_dtype == PKV_I8)
-      launch_decode_q8<PKV_I8>(s, wg, block_size, head_dim, q_dtype, stream);
-    else
-      launch_decode_q8<PKV_FP8_E4M3>(s, wg, block_size, head_dim, q_dtype, stream);
-  });
+  return run_sliced(a, out, q, block_tables, max_blocks_per_seq, seq_lens, batch, row, timing,
+                    [&](const DecodeArgs& s, const pkv::CallEvents& tm) {
+                      if (cache_dtype == PKV_I8)
+                        launch_decode_q8<PKV_I8>(s, wg, block_size, head_dim, q_dtype, stream, tm);
+                      else
+                        launch_decode_q8<PKV_FP8_E4M3>(s, wg, block_size, head_dim, q_dtype, stream, tm);
+                    });
 }
 
 }  // namespace

@@ -7,6 +7,15 @@ namespace pkv {
 
 namespace {
 thread_local char g_last_error[512] = "";
+thread_local CallEvents g_call_events;
+}
+
+void set_call_events(const CallEvents& e) { g_call_events = e; }
+
+CallEvents take_call_events() {
+  const CallEvents e = g_call_events;
+  g_call_events = CallEvents{};
+  return e;
 }
 
 int fail(int status, const char* fmt, ...) {
@@ -40,5 +49,10 @@ PKV_API const char* pkv_strerror(int status) {
 PKV_API const char* pkv_last_error(void) { return pkv::last_error(); }
 
 PKV_API int pkv_version(void) { return 100; }
+
+PKV_API int pkv_time_next_decode(hipEvent_t start, hipEvent_t stop) {
+  pkv::set_call_events(pkv::CallEvents{start, stop});
+  return PKV_OK;
+}
 
 }  // extern "C"

@@ -12,4 +12,13 @@ int fail(int status, const char* fmt, ...) __attribute__((format(printf, 2, 3)))
 void clear_error();
 const char* last_error();
 
+// The calling thread's pending kernel-timing request for its next decode call
+// (pkv_time_next_decode); taking it clears it.
+struct CallEvents {
+  hipEvent_t start = nullptr;  // recorded at the start of the call's first kernel
+  hipEvent_t stop = nullptr;   // recorded at the end of its last kernel
+};
+void set_call_events(const CallEvents& e);
+CallEvents take_call_events();
+
 }  // namespace pkv

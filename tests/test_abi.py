@@ -109,6 +109,14 @@ def test_quant_calls_reject_bad_arguments_before_launch():
     assert append(hd=80) == pkv.PKV_ERR_INVALID
 
 
+def test_time_next_decode_takes_null_events():
+    assert pkv._lib.pkv_time_next_decode(None, None) == pkv.PKV_OK
+    # consumed by the next decode call, here one refused before any launch
+    st = pkv._lib.pkv_attention_decode(None, None, None, None, None, 1, None, 1, 1, 4, 100, 16, 4, 1.0,
+                                       pkv.PKV_F16, 0, None, 0, None)
+    assert st == pkv.PKV_ERR_INVALID
+
+
 def test_workspace_queries():
     up = lambda x: -(-x // 256) * 256  # noqa: E731
     b, h, d, wg = 32, 32, 128, 512
