@@ -35,6 +35,7 @@ sample of the same workload on the host cores.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -69,6 +70,9 @@ def parse():
                         "operations on a shared-system-prompt request stream; swap: preemption swap of a "
                         "request's blocks to pinned host memory and back")
     p.add_argument("--block-size", type=int, default=16, help="block size of the long13b workload")
+    p.add_argument("--layers", type=int, default=0,
+                   help="layers per step (0 = the workload's own); each layer has its own cache, so with the "
+                        "single-layer workloads N > 1 keeps one call's K rows from still being cached at the next")
     p.add_argument("--work-groups", type=int, default=0, help="decode work-groups (0 = library choice)")
     p.add_argument("--ring", type=int, default=4, help="host staging buffers (how many steps the host may run ahead)")
     p.add_argument("--metadata", choices=["pinned", "device"], default="pinned",
@@ -330,6 +334,8 @@ def main():
         free, _ = torch.cuda.mem_get_info()
         per_block = 32 * 2 * 16 * 32 * 128 * 2
         wl = workloads.full7b_step(int(0.85 * free) // per_block)
+    if args.layers > 0:
+        wl = dataclasses.replace(wl, num_layers=args.layers, title=f"{wl.title}; {args.layers} layers")
     B, H, D, bs, NL = wl.batch, wl.num_heads, wl.head_dim, wl.block_size, wl.num_layers
     tdt = {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32}[wl.dtype]
     esz = wl.dtype_bytes
@@ -569,7 +575,8 @@ def main():
     if fused:   # the launch also reads the new rows and writes them (8-bit: codes and scales) into the pools
         algo += 2 * B * H * D * esz + B * tok_bytes
     achieved = algo / attn_s / 1e9
-    traffic = recorded_traffic(args.workload + ("" if kv == "dense" else f"/{kv}") + ("/fused" if fused else ""))
+    traffic = recorded_traffic(args.workload + ("" if kv == "dense" else f"/{kv}") + ("/fused" if fused else "")
+                               + (f"/layers{args.layers}" if args.layers > 0 else ""))
 
     extra = {}
     if args.copy_calibration:

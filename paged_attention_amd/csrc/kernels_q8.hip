@@ -20,9 +20,10 @@
 //
 // Decode reuses the stream-K kernel of decode_common.h with a policy whose
 // lanes hold 16 codes (one 16-byte load per lane per token for K and for V),
-// turn them into floats (v_cvt_pk_f32_fp8 for E4M3, signed byte extraction
-// for int8), fold the K scale into the score and the V scale into the
-// softmax weight.
+// fold the K scale into the score and the V scale into the softmax weight.
+// For q.k over FP8 codes, fp16 and bf16 queries meet the codes as 16-bit
+// pairs in dot2 instructions; otherwise the codes become floats
+// (v_cvt_pk_f32_fp8 for E4M3, signed byte conversion for int8).
 #include "decode_common.h"
 
 namespace {
@@ -125,16 +126,63 @@ struct Q8KV {
   static constexpr int KB = 1;
   static constexpr int EPL = 16;
   static constexpr int kMaxWaves = 8;
+  // q.k on 16-bit pairs (see qk16).
+  static constexpr bool kPairQK = K == PKV_FP8_E4M3 && (Q == PKV_F16 || Q == PKV_BF16);
   struct QReg {
-    float f[16];
+    float f[16];     // the lane's 16 query elements as floats
+    uint32_t p[8];   // the same elements as raw 16-bit pairs (fp16 / bf16 queries)
   };
 
   __device__ static QReg load_q(const uint8_t* p) {
     constexpr int per = 16 / dtype_bytes(Q);
     QReg r;
 #pragma unroll
-    for (int k = 0; k < 16 / per; ++k) unpack16<Q>(reinterpret_cast<const Vec16*>(p)[k], r.f + k * per);
+    for (int k = 0; k < 16 / per; ++k) {
+      const Vec16 v = reinterpret_cast<const Vec16*>(p)[k];
+      unpack16<Q>(v, r.f + k * per);
+      if constexpr (Q != PKV_F32) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) r.p[4 * k + i] = v.w[i];
+      }
+    }
     return r;
+  }
+
+  // q.k over one 16-byte load of K codes (this lane's 16 elements), float32
+  // accumulation.  With kPairQK two FP8 codes at a time become an f16 or bf16
+  // pair (v_cvt_scalef32_pk_*_fp8 with scale 1: every E4M3 value is exact in
+  // both) that a dot2 instruction multiplies with the matching pair of q.
+  // Otherwise the codes are widened to floats.  (An int8 form, the f16 value
+  // 1152 + c built by a byte permute with 1152 * sum(q) taken off afterwards,
+  // measured no faster and loses bits of q.k for large queries.)
+  __device__ static float qk16(const QReg& q, const Vec16& w) {
+    if constexpr (kPairQK) {
+      float d = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if constexpr (Q == PKV_F16) {
+          const half2v lo = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w.w[i], 1.f, false);
+          const half2v hi = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w.w[i], 1.f, true);
+          d = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2v, q.p[2 * i]), lo, d, false);
+          d = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2v, q.p[2 * i + 1]), hi, d, false);
+        } else {
+          const auto lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.w[i], 1.f, false);
+          const auto hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.w[i], 1.f, true);
+          d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf162v, q.p[2 * i]), __builtin_bit_cast(bf162v, lo),
+                                              d, false);
+          d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf162v, q.p[2 * i + 1]),
+                                              __builtin_bit_cast(bf162v, hi), d, false);
+        }
+      }
+      return d;
+    } else {
+      float c[16];
+      codes16(w, c);
+      float d = 0.f;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) d = fmaf(q.f[e], c[e], d);
+      return d;
+    }
   }
 
   // The 16 code values of one 16-byte load, in byte order (unscaled).
@@ -189,12 +237,7 @@ struct Q8KV {
     float mc = m;
 #pragma unroll
     for (int u = 0; u < kChunk; ++u) {
-      float c[16];
-      codes16(kr[u], c);
-      float d = 0.f;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) d = fmaf(q.f[e], c[e], d);
-      s[u] = group_sum<LPH>(d) * (ks[u] * a.scale_log2);
+      s[u] = group_sum<LPH>(qk16(q, kr[u])) * (ks[u] * a.scale_log2);
       if (u < valid) mc = fmaxf(mc, s[u]);
     }
     if constexpr (SCORES) store_logits<LPH>(logit_row, s, lane_c, valid);
