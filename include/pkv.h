@@ -442,9 +442,10 @@ PKV_API int pkv_append_attention_decode_quant(void* out, const void* q, const vo
  * `scores_workspace`; a third kernel on the stream folds them into `scores`.
  * ------------------------------------------------------------------------- */
 
-/* Bytes of the score workspace: float32 logits [batch][num_heads][max_seq_len]
- * and float2 [batch][num_heads], each region 256-byte aligned; 0 for an
- * invalid shape. */
+/* Bytes of the score workspace: float32 logits [batch][num_heads][S] with S =
+ * max_seq_len rounded up to a multiple of 32 (so that 32 positions of a head
+ * fill one 128-byte line), and float2 [batch][num_heads], each region
+ * 256-byte aligned; 0 for an invalid shape. */
 PKV_API size_t pkv_decode_scores_workspace_bytes(int32_t batch, int32_t num_heads, int32_t max_seq_len);
 
 /* pkv_attention_decode plus the score update above.  scores: device float32

@@ -218,7 +218,7 @@ struct DecodeArgs {
   float* logits;          // score variant: [batch][H][logit_stride] scaled logits (log2 units), else null
   float2* final_ml;       // score variant: [batch][H] final (max, sum) of each softmax
   float* scores;          // score variant: [batch][score_stride] cumulative scores, updated in place
-  int32_t logit_stride;   // = max_seq_len
+  int32_t logit_stride;   // max_seq_len rounded up to kLogitGroup
   int32_t score_stride;
   float decay;
   const int32_t* tables;
@@ -288,31 +288,47 @@ __device__ __forceinline__ bool length_ok(int L, const DecodeArgs& a) {
   return L >= 0 && L <= a.max_seq_len && static_cast<int64_t>(L) <= static_cast<int64_t>(a.max_blocks) * BS;
 }
 
-// Lane-wise select v = take ? x : v, written as v_cndmask_b32 with a wave
-// mask: as a C++ select over elements of a register array the compiler may
-// fold the chain into an indexed load from a stack copy of the array.
-__device__ __forceinline__ float select_lanes(bool take, float x, float v) {
-  const uint64_t mask = __builtin_amdgcn_ballot_w64(take);
-  float r;
-  asm("v_cndmask_b32_e64 %0, %1, %2, %3" : "=v"(r) : "v"(v), "v"(x), "s"(mask));
-  return r;
+// Scaled logits (score variant) leave the decode kernel in whole 128-byte
+// lines: a head's logits for kLogitGroup consecutive positions (four chunks)
+// are collected in LDS and then stored by the head's lanes 16 bytes each.
+// Storing each chunk's 32 bytes as it was scored left partly written lines,
+// which the read stream evicted from L2 before the next chunk completed them
+// (on MI355X a line lives ~5 us in L2 under this stream); the partial writes
+// cost 10 us of a 120 us call on the 7B-shaped layer.  Logit rows are padded
+// to a multiple of kLogitGroup positions so that the groups are aligned.
+constexpr int kLogitGroup = 32;
+
+inline int32_t padded_logit_stride(int32_t max_seq_len) {
+  return static_cast<int32_t>((static_cast<int64_t>(max_seq_len) + kLogitGroup - 1) / kLogitGroup * kLogitGroup);
 }
 
-// Stores the chunk's scaled logits s[0 .. valid) of this lane's head at
-// row[0 ..): lane c of the head's LPH lanes (all of which hold every s[u]
-// after the DPP sum) stores positions c, c + W, ... (W = min(LPH, kChunk)),
-// so the head's 8 logits leave in one contiguous store.  Lanes whose head
-// slot is beyond the head count carry row == nullptr and store nothing.
+// The chunk's 8 logits into the head's LDS slot at the chunk's offset in its
+// group; every lane of the head holds all of them after the DPP sum, and the
+// head's first lane writes them.
+__device__ __forceinline__ void stage_logits(float* slot, const float (&s)[kChunk], int c) {
+  if (c == 0) {
+    reinterpret_cast<float4*>(slot)[0] = make_float4(s[0], s[1], s[2], s[3]);
+    reinterpret_cast<float4*>(slot)[1] = make_float4(s[4], s[5], s[6], s[7]);
+  }
+}
+
+// Stores a head's staged group starting at position g0 into its logit row,
+// only positions in [t_begin, t_end) (the segment this work-group owns; the
+// rest of the group belongs to other work-groups or lies past the length).
 template <int LPH>
-__device__ __forceinline__ void store_logits(float* row, const float (&s)[kChunk], int c, int valid) {
-  constexpr int W = LPH < kChunk ? LPH : kChunk;
+__device__ __forceinline__ void flush_logits(const float* slot, float* row, int g0, int t_begin, int t_end, int c) {
 #pragma unroll
-  for (int k = 0; k < kChunk / W; ++k) {
-    float v = s[k * W];
+  for (int qd = c; qd < kLogitGroup / 4; qd += LPH) {
+    const int t = g0 + 4 * qd;
+    const float4 v = reinterpret_cast<const float4*>(slot)[qd];
+    if (t >= t_begin && t + 4 <= t_end) {
+      *reinterpret_cast<float4*>(row + t) = v;
+    } else {
+      const float w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-    for (int u = 1; u < W; ++u) v = select_lanes(c == u, s[k * W + u], v);
-    const int tok = k * W + c;
-    if (row != nullptr && c < W && tok < valid) row[tok] = v;
+      for (int j = 0; j < 4; ++j)
+        if (t + j >= t_begin && t + j < t_end) row[t + j] = w[j];
+    }
   }
 }
 
@@ -351,6 +367,8 @@ __global__ void __launch_bounds__(KV::kMaxWaves * 64) decode_kernel(DecodeArgs a
 
   extern __shared__ int32_t s_dyn[];
   __shared__ int32_t s_waves[kMaxWaves + 1];
+  // score variant: one staged logit group per head slot of every wavefront
+  __shared__ __align__(16) float s_logits[SCORES ? KV::kMaxWaves * HPW * kLogitGroup : 4];
   const int nv = a.batch * a.groups_y;
   int32_t* s_pref = s_dyn;           // [nv + 1]: first chunk of each virtual sequence
   int32_t* s_part = s_dyn + nv + 1;  // [nv + 1]: first partial slot of each virtual sequence
@@ -453,6 +471,7 @@ __global__ void __launch_bounds__(KV::kMaxWaves * 64) decode_kernel(DecodeArgs a
       bool bad_block = false;
       float* lrow = SCORES && head_ok ? a.logits + (static_cast<int64_t>(b) * a.num_heads + h) * a.logit_stride
                                       : nullptr;
+      float* lslot = SCORES ? s_logits + (wave * HPW + r) * kLogitGroup : nullptr;
       int win = -kTableWindow;  // first block index held in `tbl`
       int32_t tbl = 0;
       for (int t0 = t_begin; t0 < t_end; t0 += kChunk) {
@@ -468,7 +487,13 @@ __global__ void __launch_bounds__(KV::kMaxWaves * 64) decode_kernel(DecodeArgs a
         const int32_t blk = __builtin_amdgcn_readlane(tbl, j - win);
         // rows past the segment repeat its last row (masked)
         KV::template chunk<D, BS, LPH, SCORES>(qv, a, kp, vp, blk, t0 % BS, hl, row_bytes, t_end - 1 - t0,
-                                               t_end - t0, m, l, acc, lrow != nullptr ? lrow + t0 : nullptr, c);
+                                               t_end - t0, m, l, acc,
+                                               SCORES ? lslot + (t0 & (kLogitGroup - 1)) : nullptr, c);
+        if constexpr (SCORES) {
+          const int next = t0 + kChunk;
+          if (lrow != nullptr && ((next & (kLogitGroup - 1)) == 0 || next >= t_end))
+            flush_logits<LPH>(lslot, lrow, t0 & ~(kLogitGroup - 1), t_begin, t_end, c);
+        }
       }
       if (bad_block) l = __builtin_nanf("");
       if (head_ok) {
@@ -757,11 +782,11 @@ void launch_decode_d(const DecodeArgs& a, int wg, int32_t bs, int32_t d, hipStre
   else launch_decode_m<KV, kPlain>(a, wg, bs, d, stream, tm);
 }
 
-// Cumulative-score workspace: logits [batch][H][max_seq_len] float32, then the
-// final (max, sum) [batch][H] float2, each region 256-byte aligned.
+// Cumulative-score workspace: logits [batch][H][padded_logit_stride] float32,
+// then the final (max, sum) [batch][H] float2, each region 256-byte aligned.
 inline size_t scores_workspace_bytes(int32_t batch, int32_t num_heads, int32_t max_seq_len) {
   auto up = [](size_t x) { return (x + 255) / 256 * 256; };
-  return up(static_cast<size_t>(batch) * num_heads * max_seq_len * sizeof(float)) +
+  return up(static_cast<size_t>(batch) * num_heads * padded_logit_stride(max_seq_len) * sizeof(float)) +
          up(static_cast<size_t>(batch) * num_heads * sizeof(float2));
 }
 
@@ -784,15 +809,16 @@ inline int attach_scores(DecodeArgs& a, const ScoreRequest* sc, int32_t batch, i
                      max_seq_len);
   if (!std::isfinite(sc->decay)) return pkv::fail(PKV_ERR_INVALID, "%s: decay must be finite", what);
   const size_t need = scores_workspace_bytes(batch, num_heads, max_seq_len);
+  const int32_t stride = padded_logit_stride(max_seq_len);
   if (sc->workspace_bytes < need)
     return pkv::fail(PKV_ERR_INVALID, "%s: score workspace of %zu bytes needed, %zu given", what, need,
                      sc->workspace_bytes);
   auto up = [](size_t x) { return (x + 255) / 256 * 256; };
   char* base = static_cast<char*>(sc->workspace);
   a.logits = reinterpret_cast<float*>(base);
-  a.final_ml = reinterpret_cast<float2*>(base + up(static_cast<size_t>(batch) * num_heads * max_seq_len * 4));
+  a.final_ml = reinterpret_cast<float2*>(base + up(static_cast<size_t>(batch) * num_heads * stride * 4));
   a.scores = sc->scores;
-  a.logit_stride = max_seq_len;
+  a.logit_stride = stride;
   a.score_stride = sc->score_stride;
   a.decay = sc->decay;
   return PKV_OK;

@@ -12,7 +12,7 @@ namespace {
 // already in registers.  `valid` = tokens of the chunk inside the segment.
 template <int DT, int EPL, int LPH, bool SCORES>
 __device__ __forceinline__ void softmax_chunk(const Vec16& qv, const Vec16* kr, const Vec16* vr, int valid,
-                                              float scale_log2, float& m, float& l, float* acc, float* logit_row,
+                                              float scale_log2, float& m, float& l, float* acc, float* logit_slot,
                                               int lane_c) {
   float s[kChunk];
   float mc = m;
@@ -21,7 +21,7 @@ __device__ __forceinline__ void softmax_chunk(const Vec16& qv, const Vec16* kr, 
     s[u] = group_sum<LPH>(dot16<DT>(qv, kr[u], 0.f)) * scale_log2;
     if (u < valid) mc = fmaxf(mc, s[u]);
   }
-  if constexpr (SCORES) store_logits<LPH>(logit_row, s, lane_c, valid);
+  if constexpr (SCORES) stage_logits(logit_slot, s, lane_c);
   const float alpha = __builtin_amdgcn_exp2f(m - mc);
   l *= alpha;
 #pragma unroll
@@ -54,7 +54,7 @@ struct DenseKV {
   template <int D, int BS, int LPH, bool SCORES>
   __device__ static void chunk(const Vec16& qv, const DecodeArgs& a, const uint8_t* kp, const uint8_t* vp, int32_t blk,
                                int pos0, int /*head*/, int64_t row_bytes, int lastu, int valid, float& m, float& l,
-                               float* acc, float* logit_row, int lane_c) {
+                               float* acc, float* logit_slot, int lane_c) {
     const int64_t base = (static_cast<int64_t>(blk) * BS + pos0) * row_bytes;
     Vec16 kr[kChunk], vr[kChunk];
     // K rows take ordinary loads, V rows non-temporal ones.  Measured on
@@ -70,7 +70,7 @@ struct DenseKV {
       kr[u] = *reinterpret_cast<const Vec16*>(kp + ro);
       vr[u] = stream_load(vp + ro);
     }
-    softmax_chunk<DT, EPL, LPH, SCORES>(qv, kr, vr, valid, a.scale_log2, m, l, acc, logit_row, lane_c);
+    softmax_chunk<DT, EPL, LPH, SCORES>(qv, kr, vr, valid, a.scale_log2, m, l, acc, logit_slot, lane_c);
   }
 
   // The new row is already in the cache's dtype: a 16-byte copy per lane.

@@ -208,7 +208,7 @@ struct Q8KV {
   template <int D, int BS, int LPH, bool SCORES>
   __device__ static void chunk(const QReg& q, const DecodeArgs& a, const uint8_t* kp, const uint8_t* vp, int32_t blk,
                                int pos0, int head, int64_t row_bytes, int lastu, int valid, float& m, float& l,
-                               float* acc, float* logit_row, int lane_c) {
+                               float* acc, float* logit_slot, int lane_c) {
     const int64_t base = (static_cast<int64_t>(blk) * BS + pos0) * row_bytes;
     Vec16 kr[kChunk], vr[kChunk];
     // As in the 16/32-bit path, K codes take ordinary loads and V codes
@@ -240,7 +240,7 @@ struct Q8KV {
       s[u] = group_sum<LPH>(qk16(q, kr[u])) * (ks[u] * a.scale_log2);
       if (u < valid) mc = fmaxf(mc, s[u]);
     }
-    if constexpr (SCORES) store_logits<LPH>(logit_row, s, lane_c, valid);
+    if constexpr (SCORES) stage_logits(logit_slot, s, lane_c);
     const float alpha = __builtin_amdgcn_exp2f(m - mc);
     l *= alpha;
 #pragma unroll
