@@ -81,6 +81,8 @@ def parse():
                    help="K/V cache storage: the workload's dtype (auto) or an 8-bit format")
     p.add_argument("--scores", action="store_true",
                    help="also update cumulative attention scores per cached token (16/32-bit caches)")
+    p.add_argument("--grouped", action="store_true",
+                   help="decode with pkv_attention_decode_grouped: shared prefixes read once per tile of sequences")
     p.add_argument("--fused", action="store_true",
                    help="scatter and attend in one launch per layer (pkv_append_attention_decode)")
     p.add_argument("--time-every", type=int, default=8,
@@ -415,6 +417,18 @@ def main():
     out = torch.empty((B, H, D), dtype=tdt, device=dev)
     wgs = args.work_groups or pkv.pkv_decode_work_groups(wl.dtype if kv == "dense" else kv)
     workspace = pkv.decode_workspace(B, H, D, wl.dtype if kv == "dense" else kv, wgs, device=dev)
+    prefix = None
+    if args.grouped:
+        if kv != "dense" or args.fused or args.scores or wl.dtype not in ("f16", "bf16"):
+            print("--grouped runs with an fp16/bf16 cache, separate launches and no scores", file=sys.stderr)
+            sys.exit(2)
+        # Groups from the tables and the first step's lengths.  New tokens land
+        # in private blocks, so the shared prefixes (capped by each length) stay
+        # valid for every later step.
+        spb, tiles = pkv.prefix_tiles(tables, (cur + 1).astype(np.int32), bs)
+        prefix = (torch.from_numpy(spb).to(dev), torch.from_numpy(tiles).to(dev))
+        workspace = torch.empty(pkv.pkv_decode_grouped_workspace_bytes(B, H, D, wl.dtype, wgs), dtype=torch.uint8,
+                                device=dev)
     # Step metadata is one packed buffer: slots (int64), lengths and block
     # tables (int32).  Host side: a ring of pinned buffers, so the host can
     # prepare step i+1 while step i's kernels still read (or copy) slot i.
@@ -480,7 +494,8 @@ def main():
                     [pkv.PreparedAppend(k_new[0, l], v_new[0, l], sl_t, k_caches[l], v_caches[l])
                      for l in range(NL)],
                     [pkv.PreparedDecode(out, q_all[0, l], k_caches[l], v_caches[l], tb_t, ln_t, max_len,
-                                        scale=wl.scale, work_groups=wgs, workspace=workspace) for l in range(NL)])
+                                        scale=wl.scale, work_groups=wgs, workspace=workspace, prefix=prefix)
+                     for l in range(NL)])
             else:
                 per_slot[key] = (
                     [pkv.PreparedAppendQuant(k_new[0, l], v_new[0, l], sl_t, k_caches[l], v_caches[l],
@@ -576,6 +591,7 @@ def main():
         algo += 2 * B * H * D * esz + B * tok_bytes
     achieved = algo / attn_s / 1e9
     traffic = recorded_traffic(args.workload + ("" if kv == "dense" else f"/{kv}") + ("/fused" if fused else "")
+                               + ("/grouped" if prefix is not None else "")
                                + (f"/layers{args.layers}" if args.layers > 0 else ""))
 
     extra = {}
@@ -630,14 +646,17 @@ def main():
                    "kv_cache": wl.dtype if kv == "dense" else kv, "q_dtype": wl.dtype, "layers": NL, "batch": B, "heads": H, "head_dim": D, "block_size": bs,
                    "pool_blocks": wl.num_blocks, "work_groups": wgs, "metadata": mode,
                    "launches_per_layer": 1 if fused else 2, "cumulative_scores": bool(args.scores),
+                   "grouped_prefix_tiles": None if prefix is None else int(prefix[1].shape[0]),
                    "mean_seq_len": round(kv_per_call / tok_bytes / B, 1), "cow_pairs": n_pairs[0]},
         "hbm_peak_frac": round(unique_gbs / HBM_PEAK_GBS, 4),
         "unique_kv_gbs": round(unique_gbs, 2),
         "token_steps_per_s": round(B * args.steps / elapsed, 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "kernel": ("pkv_append_attention_decode" if fused else "pkv_attention_decode")
-                     + ("_quant" if kv != "dense" else "") + " (decode_kernel + decode_merge_kernel)",
+                     "kernel": ("pkv_attention_decode_grouped (prefix_kernel + decode_kernel + decode_merge_kernel)"
+                                if prefix is not None else
+                                ("pkv_append_attention_decode" if fused else "pkv_attention_decode")
+                                + ("_quant" if kv != "dense" else "") + " (decode_kernel + decode_merge_kernel)"),
                      "avg_call_us": round(attn_s * 1e6, 2), "algorithmic_bytes_per_call": int(algo),
                      "logical_kv_bytes_per_call": int(kv_per_call), "timed_calls": len(timed) * NL,
                      "timing": "kernel timestamps of the call's first and last kernel, every "

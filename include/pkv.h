@@ -474,6 +474,74 @@ PKV_API int pkv_attention_decode_quant_scores(void* out, const void* q, const vo
                                               float decay, void* scores_workspace, size_t scores_workspace_bytes,
                                               hipStream_t stream);
 
+/* ---------------------------------------------------------------------------
+ * Grouped decode: shared prefixes read once per group.
+ *
+ * Sequences forked from one prompt, or matched in the prefix cache, begin
+ * with the same physical blocks (hnwysp.cn/news/103996 §3.3;
+ * icman.com.cn/news/78786 §3.1).  Plain decode reads such a prefix once per
+ * sequence.  The grouped call reads it once per tile of up to 16 sequences
+ * and head, with the tile's queries against the prefix as two small matrix
+ * products on the matrix cores (scores = K Q^T, weighted values = V^T P^T,
+ * with P split into two 16-bit parts so that the weights keep float32
+ * precision), and seeds each sequence's online softmax over its own
+ * positions with the prefix's (max, sum, weighted values).  The result
+ * equals pkv_attention_decode.
+ * ------------------------------------------------------------------------- */
+
+#define PKV_PREFIX_TILE_SEQS 16    /* sequences per prefix tile */
+#define PKV_PREFIX_TILE_INTS 18    /* int32 per tile: prefix blocks, member count, 16 sequence indices */
+#define PKV_PREFIX_MAX_BLOCKS 1024 /* longest prefix a tile may cover, in blocks */
+
+/* Host helper: groups the batch's sequences by shared leading blocks.
+ * tables: host int32 [batch][max_blocks_per_seq]; seq_lens: host int32
+ * [batch] (this step's lengths).  Sequences with the same first block id
+ * form a group when there are at least max(2, min_sharers) of them; the
+ * group's prefix is the longest run of leading ids all its members share,
+ * capped for every member at the whole blocks before its last position
+ * ((L - 1) / block_size), so each member keeps at least one position of
+ * its own, and at PKV_PREFIX_MAX_BLOCKS (positions past it are read per
+ * sequence).  A group with a prefix of at least one block is cut into tiles
+ * of at most PKV_PREFIX_TILE_SEQS members in ascending sequence order.
+ * Out: seq_prefix_blocks[b] = the prefix of b's group in blocks, or 0;
+ * tiles: int32 [max_tiles][PKV_PREFIX_TILE_INTS], each
+ * {prefix blocks, member count, member indices..., -1 padding}, the first
+ * member's table row being the one the tile reads; *num_tiles.  At most
+ * (batch + 1) / 2 tiles are ever needed.  PKV_ERR_INVALID if more than
+ * max_tiles are needed (nothing written). */
+PKV_API int pkv_prefix_tiles(const int32_t* tables, int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                             int32_t batch, int32_t block_size, int32_t min_sharers, int32_t* seq_prefix_blocks,
+                             int32_t* tiles, int32_t max_tiles, int32_t* num_tiles);
+
+/* Workspace bytes of pkv_attention_decode_grouped: the plain decode
+ * workspace plus float32 [batch][num_heads][head_dim + 4] prefix states. */
+PKV_API size_t pkv_decode_grouped_workspace_bytes(int32_t batch, int32_t num_heads, int32_t head_dim,
+                                                  pkv_dtype dtype, int32_t num_work_groups);
+
+/* pkv_attention_decode with shared prefixes read once per tile.
+ * seq_prefix_blocks: int32 [batch] (device or pinned host), tiles: int32
+ * [num_tiles][PKV_PREFIX_TILE_INTS] (device or pinned host), as written by
+ * pkv_prefix_tiles from the same tables and lengths; num_tiles on the host.
+ * dtype f16 or bf16 (a cache of another type returns PKV_ERR_INVALID).  The
+ * caller guarantees that the members of a tile share their first
+ * seq_prefix_blocks blocks and that every sequence with seq_prefix_blocks
+ * > 0 is a member of exactly one tile with that prefix; the prefix is read
+ * from the first member's row; a tile's prefix is at most
+ * PKV_PREFIX_MAX_BLOCKS blocks (a longer tile's members get NaN rows).  A
+ * member whose length is refused, or not
+ * longer than its prefix, is attended as an ungrouped sequence (with the
+ * plain call's handling of refused lengths); out-of-range sequence indices
+ * in a tile are skipped.  A prefix block id outside [0, num_blocks) makes
+ * the tile's members NaN.  Every other argument is that of
+ * pkv_attention_decode; workspace: pkv_decode_grouped_workspace_bytes. */
+PKV_API int pkv_attention_decode_grouped(void* out, const void* q, const void* k_cache, const void* v_cache,
+                                         const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                         const int32_t* seq_lens, int32_t max_seq_len, int32_t batch,
+                                         int32_t num_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                         float scale, pkv_dtype dtype, const int32_t* seq_prefix_blocks,
+                                         const int32_t* tiles, int32_t num_tiles, int32_t num_work_groups,
+                                         void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

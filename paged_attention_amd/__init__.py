@@ -72,6 +72,10 @@ def _load():
         "pkv_last_error": (ctypes.c_char_p, []),
         "pkv_version": (ctypes.c_int, []),
         "pkv_time_next_decode": (ctypes.c_int, [vp, vp]),
+        "pkv_prefix_tiles": (ctypes.c_int, [p32, i32, p32, i32, i32, i32, p32, p32, i32, vp]),
+        "pkv_decode_grouped_workspace_bytes": (sz, [i32, i32, i32, ctypes.c_int, i32]),
+        "pkv_attention_decode_grouped": (ctypes.c_int, [vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, i32, i32,
+                                                        ctypes.c_float, ctypes.c_int, vp, vp, i32, i32, vp, sz, vp]),
         "pkv_allocator_create": (ctypes.c_int, [i32, i32, p32, ctypes.POINTER(vp)]),
         "pkv_allocator_destroy": (None, [vp]),
         "pkv_block_alloc": (ctypes.c_int, [vp, p32]),
@@ -497,6 +501,68 @@ def pkv_attention_decode(out, q, k_cache, v_cache, block_tables, seq_lens, max_s
     _check(_lib.pkv_attention_decode(*args))
 
 
+PREFIX_TILE_SEQS, PREFIX_TILE_INTS, PREFIX_MAX_BLOCKS = 16, 18, 1024
+
+
+def prefix_tiles(tables, seq_lens, block_size: int, min_sharers: int = 2):
+    """Groups of sequences sharing leading blocks (pkv_prefix_tiles), on the host.
+
+    ``tables`` [B][max_blocks] and ``seq_lens`` [B] are host int32 arrays (this
+    step's); returns ``(seq_prefix_blocks [B], tiles [n][PREFIX_TILE_INTS])``,
+    both int32 numpy arrays.
+    """
+    tables = np.ascontiguousarray(tables, dtype=np.int32)
+    lens = np.ascontiguousarray(seq_lens, dtype=np.int32)
+    if tables.ndim != 2 or lens.shape != (tables.shape[0],):
+        raise InvalidArgument(PKV_ERR_INVALID, "prefix_tiles: tables must be [B][max_blocks], lens [B]")
+    batch, maxb = tables.shape
+    cap = max(1, (batch + 1) // 2)
+    spb = np.zeros(max(batch, 1), dtype=np.int32)
+    tiles = np.full((cap, PREFIX_TILE_INTS), -1, dtype=np.int32)
+    n = ctypes.c_int32(0)
+    _check(_lib.pkv_prefix_tiles(_ptr(tables), maxb, _ptr(lens), batch, int(block_size), int(min_sharers), _ptr(spb),
+                                 _ptr(tiles), cap, ctypes.byref(n)))
+    return spb[:batch].copy(), tiles[: n.value].copy()
+
+
+def pkv_decode_grouped_workspace_bytes(batch, num_heads, head_dim, dtype, work_groups=0) -> int:
+    return int(_lib.pkv_decode_grouped_workspace_bytes(batch, num_heads, head_dim, DTYPE_CODES[dtype], work_groups))
+
+
+def _grouped_args(out, q, k_cache, v_cache, block_tables, seq_lens, max_seq_len, seq_prefix_blocks, tiles, scale,
+                  work_groups, workspace, stream):
+    torch = _torch()
+    batch, h, d = q.shape
+    if workspace is None:
+        need = pkv_decode_grouped_workspace_bytes(max(batch, 1), h, d, _DT_NAMES[_dtype_code(q)], work_groups)
+        if need == 0:
+            raise InvalidArgument(PKV_ERR_INVALID, "attention_decode_grouped: unsupported sizes")
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    args, _ = _decode_args(out, q, k_cache, v_cache, block_tables, seq_lens, max_seq_len, scale, work_groups,
+                           workspace, stream)
+    if seq_prefix_blocks.shape != (batch,) or tiles.dim() != 2 or tiles.shape[1] != PREFIX_TILE_INTS:
+        raise InvalidArgument(PKV_ERR_INVALID, "attention_decode_grouped: seq_prefix_blocks [B], tiles [n][18]")
+    grouped = [_dev(seq_prefix_blocks, "seq_prefix_blocks", torch.int32, pinned_ok=True),
+               _dev(tiles, "tiles", torch.int32, pinned_ok=True) if tiles.shape[0] else None, tiles.shape[0]]
+    # the plain argument list with the prefix arrays before the work-group count
+    return args[:15] + grouped + args[15:], workspace
+
+
+def pkv_attention_decode_grouped(out, q, k_cache, v_cache, block_tables, seq_lens, max_seq_len, seq_prefix_blocks,
+                                 tiles, scale=None, work_groups=0, workspace=None, stream=None) -> None:
+    """pkv_attention_decode with shared prefixes read once per tile.
+
+    ``seq_prefix_blocks`` [B] and ``tiles`` [n][PREFIX_TILE_INTS] are int32
+    tensors (device or pinned host) as prefix_tiles returns them for the same
+    tables and lengths; f16 or bf16 caches.
+    """
+    if q.shape[0] == 0:
+        return
+    args, _ = _grouped_args(out, q, k_cache, v_cache, block_tables, seq_lens, max_seq_len, seq_prefix_blocks, tiles,
+                            scale, work_groups, workspace, stream)
+    _check(_lib.pkv_attention_decode_grouped(*args))
+
+
 class PreparedDecode:
     """A pkv_attention_decode call whose arguments are checked once.
 
@@ -508,7 +574,17 @@ class PreparedDecode:
     """
 
     def __init__(self, out, q, k_cache, v_cache, block_tables, seq_lens, max_seq_len, scale=None, work_groups=0,
-                 workspace=None, stream=None, scores=None, decay=0.995, scores_ws=None):
+                 workspace=None, stream=None, scores=None, decay=0.995, scores_ws=None, prefix=None):
+        if prefix is not None:   # grouped call: prefix = (seq_prefix_blocks, tiles)
+            if scores is not None:
+                raise InvalidArgument(PKV_ERR_INVALID, "prepared decode: scores and prefix groups do not combine")
+            self._args, ws = _grouped_args(out, q, k_cache, v_cache, block_tables, seq_lens, max_seq_len, prefix[0],
+                                           prefix[1], scale, work_groups, workspace, stream)
+            self._keep = (k_cache, v_cache, block_tables, seq_lens, ws, prefix)
+            self._shape, self._dtype = tuple(q.shape), q.dtype
+            self._fn = _lib.pkv_attention_decode_grouped
+            self._ti = 4
+            return
         self._args, ws = _decode_args(out, q, k_cache, v_cache, block_tables, seq_lens, max_seq_len, scale,
                                       work_groups, workspace, stream)
         self._keep = (k_cache, v_cache, block_tables, seq_lens, ws)
@@ -804,5 +880,7 @@ __all__ = [
     "decode_workspace", "PreparedDecode", "PreparedAppend", "version", "LIB_PATH",
     "pkv_append_quant", "pkv_attention_decode_quant", "PreparedDecodeQuant", "PreparedAppendQuant",
     "CACHE_FORMATS", "prefix_block_keys", "pkv_swap_blocks", "pkv_attention_decode_scores",
-    "pkv_attention_decode_quant_scores", "pkv_decode_scores_workspace_bytes", "scores_workspace", "pkv_append_attention_decode", "pkv_append_attention_decode_quant", "PreparedAppendDecode",
+    "pkv_attention_decode_quant_scores", "pkv_decode_scores_workspace_bytes", "scores_workspace",
+    "prefix_tiles", "pkv_attention_decode_grouped", "pkv_decode_grouped_workspace_bytes", "PREFIX_TILE_SEQS",
+    "PREFIX_TILE_INTS", "pkv_append_attention_decode", "pkv_append_attention_decode_quant", "PreparedAppendDecode",
 ]

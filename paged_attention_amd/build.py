@@ -31,7 +31,7 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", "-DPKV_BUILDING_L
 DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 HIP_SOURCES = ["kernels.hip", "kernels_q8.hip", "block_kernels.hip"]
-HOST_SOURCES = ["allocator.cpp", "status.cpp"]
+HOST_SOURCES = ["allocator.cpp", "status.cpp", "prefix_groups.cpp"]
 
 
 def _run(cmd, verbose):

@@ -221,6 +221,12 @@ struct DecodeArgs {
   int32_t logit_stride;   // max_seq_len rounded up to kLogitGroup
   int32_t score_stride;
   float decay;
+  const int32_t* prefix_blocks;  // grouped call: [batch] shared-prefix blocks per sequence (else null)
+  float* prefix_state;           // grouped call: [prefix_parts][prefix_batch][H][prefix_row] partial
+                                 // prefix states acc[D], max, sum
+  int32_t prefix_row;            // = D + 4 (rows stay 16-byte aligned)
+  int32_t prefix_parts;          // work-groups per prefix tile and head (partial states per sequence)
+  int32_t prefix_batch;          // the whole call's batch (stride of the parts)
   const int32_t* tables;
   const int32_t* lens;
   float* ws_acc;      // [partial slot][H][D]
@@ -286,6 +292,18 @@ __device__ __forceinline__ int range_owner(int64_t c, int64_t nwg, int64_t total
 template <int BS>
 __device__ __forceinline__ bool length_ok(int L, const DecodeArgs& a) {
   return L >= 0 && L <= a.max_seq_len && static_cast<int64_t>(L) <= static_cast<int64_t>(a.max_blocks) * BS;
+}
+
+// First logical position the decode kernel attends for sequence b of valid
+// length L: in a grouped call, the end of a shared prefix shorter than L
+// (the prefix itself is attended by prefix_kernel); else 0.  Compiled only
+// for formats with a grouped entry point (GROUPED): the extra state costs
+// the 8-bit kernel registers and spills.
+template <int BS, bool GROUPED>
+__device__ __forceinline__ int suffix_start(int b, int L, const DecodeArgs& a) {
+  if (!GROUPED || a.prefix_blocks == nullptr) return 0;
+  const int64_t p = a.prefix_blocks[b];
+  return p > 0 && p * BS < L ? static_cast<int>(p * BS) : 0;
 }
 
 // Scaled logits (score variant) leave the decode kernel in whole 128-byte
@@ -377,8 +395,9 @@ __global__ void __launch_bounds__(KV::kMaxWaves * 64) decode_kernel(DecodeArgs a
   // 1. chunk counts of every (head slice, sequence); bad lengths count zero.
   block_exclusive_scan(
       [&](int v) {
-        const int L = a.lens[v % a.batch];
-        return length_ok<BS>(L, a) ? (L + kChunk - 1) / kChunk : 0;
+        const int b = v % a.batch;
+        const int L = a.lens[b];
+        return length_ok<BS>(L, a) ? (L - suffix_start<BS, KV::kGrouped>(b, L, a) + kChunk - 1) / kChunk : 0;
       },
       nv, s_pref, s_waves);
   const int64_t total = s_pref[nv];
@@ -451,8 +470,9 @@ __global__ void __launch_bounds__(KV::kMaxWaves * 64) decode_kernel(DecodeArgs a
       const Elem* kp = static_cast<const Elem*>(a.k) + e0 * KB;
       const Elem* vp = static_cast<const Elem*>(a.v) + e0 * KB;
       const int L = a.lens[b];
-      const int t_begin = static_cast<int>(cur - seq0) * kChunk;
-      const int t_end = min(L, static_cast<int>(seg_end - seq0) * kChunk);
+      const int start = suffix_start<BS, KV::kGrouped>(b, L, a);
+      const int t_begin = start + static_cast<int>(cur - seq0) * kChunk;
+      const int t_end = min(L, start + static_cast<int>(seg_end - seq0) * kChunk);
       const int32_t* trow = a.tables + static_cast<int64_t>(b) * a.max_blocks;
       const typename KV::QReg qv = KV::load_q(static_cast<const Elem*>(a.q) + b * q_row_bytes + e0 * QB);
       if constexpr (APPEND) {
@@ -468,6 +488,19 @@ __global__ void __launch_bounds__(KV::kMaxWaves * 64) decode_kernel(DecodeArgs a
       float acc[EPL];
 #pragma unroll
       for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
+      if (KV::kGrouped && start > 0 && cur == seq0) {  // the first piece continues from the shared prefix's state,
+                                       // merged from its parts' partial states
+        const float* ps0 = a.prefix_state + (static_cast<int64_t>(b) * a.num_heads + hl) * a.prefix_row;
+        const int64_t part_stride = static_cast<int64_t>(a.prefix_batch) * a.num_heads * a.prefix_row;
+        for (int r = 0; r < a.prefix_parts; ++r) m = fmaxf(m, ps0[r * part_stride + D]);
+        for (int r = 0; r < a.prefix_parts; ++r) {
+          const float* ps = ps0 + r * part_stride;
+          const float w = ps[D] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ps[D] - m);
+          l = fmaf(ps[D + 1], w, l);
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) acc[e] = fmaf(ps[c * EPL + e], w, acc[e]);
+        }
+      }
       bool bad_block = false;
       float* lrow = SCORES && head_ok ? a.logits + (static_cast<int64_t>(b) * a.num_heads + h) * a.logit_stride
                                       : nullptr;
@@ -863,6 +896,11 @@ inline int prepare_decode(DecodeArgs& a, const void* q, const void* k_cache, con
   a.logit_stride = 0;
   a.score_stride = 0;
   a.decay = 0.f;
+  a.prefix_blocks = nullptr;
+  a.prefix_state = nullptr;
+  a.prefix_row = 0;
+  a.prefix_parts = 0;
+  a.prefix_batch = 0;
   a.ws_plan = reinterpret_cast<int32_t*>(base + ws.plan);
   a.ws_acc = reinterpret_cast<float*>(base + ws.acc);
   a.ws_ml = reinterpret_cast<float2*>(base + ws.ml);
@@ -905,6 +943,10 @@ int run_sliced(const DecodeArgs& base, void* out, const void* q, const int32_t* 
     }
     a.tables = block_tables + static_cast<int64_t>(b0) * max_blocks_per_seq;
     a.lens = seq_lens + b0;
+    if (base.prefix_blocks) {
+      a.prefix_blocks = base.prefix_blocks + b0;
+      a.prefix_state = base.prefix_state + static_cast<int64_t>(b0) * base.num_heads * base.prefix_row;
+    }
     launch(a, tm);
     const int st = check_launch("attention_decode");
     if (st != PKV_OK) return st;

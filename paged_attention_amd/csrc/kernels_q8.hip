@@ -126,6 +126,7 @@ struct Q8KV {
   static constexpr int KB = 1;
   static constexpr int EPL = 16;
   static constexpr int kMaxWaves = 8;
+  static constexpr bool kGrouped = false;  // no grouped entry point for 8-bit caches
   // q.k on 16-bit pairs (see qk16).
   static constexpr bool kPairQK = K == PKV_FP8_E4M3 && (Q == PKV_F16 || Q == PKV_BF16);
   struct QReg {

@@ -1,0 +1,138 @@
+"""GPU parity of grouped decode (pkv_attention_decode_grouped) through the C interface.
+
+Shared prefixes are attended once per tile of up to 16 sequences with the
+matrix cores and each sequence's own positions by the decode kernel, seeded
+with the prefix's softmax state; the output must match the oracle's attention
+within the bounds of pkv_attention_decode (2e-3 fp16; bf16 adds its output
+rounding).  Pools are NaN outside written slots, so any read of a wrong
+position shows in the output.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import paged_attention_amd as pkv
+import workloads
+from oracle import attention as oatt
+from tests import paged_case as pc
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    yield
+    torch.cuda.synchronize()
+
+
+def _log(msg):
+    print(msg, flush=True)
+
+
+def _grouped(c, work_groups=0, spb=None, tiles=None, min_sharers=2):
+    if spb is None:
+        spb, tiles = pkv.prefix_tiles(c.tables_np, c.wl.seq_lens, c.wl.block_size, min_sharers)
+    out = torch.empty_like(c.q)
+    pkv.pkv_attention_decode_grouped(out, c.q, c.k_cache, c.v_cache, c.tables, c.lens, c.wl.max_seq_len,
+                                     torch.from_numpy(np.ascontiguousarray(spb)).to(DEV),
+                                     torch.from_numpy(np.ascontiguousarray(tiles)).to(DEV), scale=c.wl.scale,
+                                     work_groups=work_groups)
+    torch.cuda.synchronize()
+    return out, spb, tiles
+
+
+LENS = [41, 60, 45, 9, 100, 77, 41, 300, 2]
+SHARERS = [0, 1, 2, 4, 5, 6, 7]
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("head_dim", [64, 128])
+@pytest.mark.parametrize("block_size", [8, 16, 32])
+def test_small_groups_match_oracle(dtype, head_dim, block_size):
+    wl = workloads.custom(LENS, num_heads=5, head_dim=head_dim, dtype=dtype, block_size=block_size,
+                          seed=head_dim + block_size, prefix_len=40, sharers=SHARERS)
+    c = pc.build(wl, DEV)
+    ref = pc.oracle_out(c)
+    for wg in (0, 3, 50):
+        out, spb, tiles = _grouped(c, wg)
+        assert len(tiles) == 1 and spb[SHARERS].min() == 40 // block_size
+        pc.compare(c, out, ref)
+
+
+def test_no_tiles_is_the_plain_call_bit_for_bit():
+    wl = workloads.custom(LENS, num_heads=5, head_dim=128, dtype="f16", block_size=16, seed=3, prefix_len=40,
+                          sharers=SHARERS)
+    c = pc.build(wl, DEV)
+    out, _, _ = _grouped(c, spb=np.zeros(wl.batch, dtype=np.int32), tiles=np.zeros((0, 18), dtype=np.int32))
+    plain = pc.run_gpu(c).clone()
+    assert torch.equal(out, plain)
+
+
+def test_group_of_forty_spans_three_tiles():
+    rng = np.random.default_rng(5)
+    lens = (200 + rng.integers(1, 300, size=44)).tolist()
+    wl = workloads.custom(lens, num_heads=8, head_dim=128, dtype="f16", block_size=16, seed=5, prefix_len=200,
+                          sharers=list(range(2, 42)))
+    c = pc.build(wl, DEV)
+    out, spb, tiles = _grouped(c)
+    assert tiles[:, 1].tolist() == [16, 16, 8] and spb[2:42].min() == 12
+    pc.compare(c, out)
+
+
+def test_prefix_cow_full_size():
+    wl = workloads.prefix_cow()
+    c = pc.build(wl, DEV)
+    out, spb, tiles = _grouped(c)
+    assert len(tiles) == 4 and spb.min() == 32
+    err = pc.compare(c, out)
+    plain = pc.run_gpu(c)
+    _log(f"prefix+CoW grouped max err {err:.2e}; grouped vs plain max diff "
+         f"{(out.float() - plain.float()).abs().max().item():.2e}")
+
+
+def test_short_member_is_attended_ungrouped_and_bad_prefix_block_gives_nan():
+    bs = 16
+    wl = workloads.custom([70, 70, 70, 70, 90], num_heads=4, head_dim=64, dtype="f16", block_size=bs, seed=8,
+                          prefix_len=64, sharers=[0, 1, 2, 3])
+    c = pc.build(wl, DEV)
+    spb, tiles = pkv.prefix_tiles(c.tables_np, wl.seq_lens, bs)
+    assert spb.tolist() == [4, 4, 4, 4, 0]
+    # member 3 attends only its first 33 positions this call: not longer than the
+    # tile's 4-block prefix, so both kernels leave it to the plain path
+    lens = np.array([70, 70, 70, 33, 90], dtype=np.int32)
+    ref = oatt.decode_attention(c.vals["q"], c.ok_pool, c.ov_pool, c.tables_np, lens, wl.dtype, wl.scale)
+    c.lens = torch.from_numpy(lens).to(DEV)
+    out, _, _ = _grouped(c, spb=spb, tiles=tiles)
+    pc.compare(c, out, ref)
+    # a prefix block id outside the pool in the row the tile reads: the tile's members are NaN
+    lead = int(tiles[0, 2])
+    bad_tables = c.tables_np.copy()
+    bad_tables[lead, 1] = wl.num_blocks + 5
+    c.tables = torch.from_numpy(bad_tables).to(DEV)
+    spb3, tiles3 = spb.copy(), tiles.copy()
+    spb3[3] = 0                                      # member 3 (33 positions) stays off the tile
+    tiles3[0, 1] = 3
+    tiles3[0, 5] = -1
+    out, _, _ = _grouped(c, spb=spb3, tiles=tiles3)
+    members = tiles3[0, 2:2 + tiles3[0, 1]].tolist()
+    assert torch.isnan(out[members].float()).all()
+    others = [b for b in range(wl.batch) if b not in members]
+    got = out[others].float().cpu().numpy()
+    assert np.all(np.abs(got - ref[others]) <= pc.tolerance(wl.dtype, ref[others]))
+
+
+def test_batch_slices_with_groups():
+    rng = np.random.default_rng(12)
+    lens = rng.integers(1, 40, size=9000)
+    lens[:300] = 33 + rng.integers(1, 20, size=300)
+    wl = workloads.custom(lens, num_heads=4, head_dim=64, dtype="bf16", block_size=8, seed=12, prefix_len=32,
+                          sharers=list(range(300)))
+    c = pc.build(wl, DEV, check_pools=False)
+    out, spb, tiles = _grouped(c, work_groups=300)
+    assert spb[:300].min() == 4 and len(tiles) == 19
+    pc.compare(c, out)
