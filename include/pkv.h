@@ -514,14 +514,16 @@ PKV_API int pkv_prefix_tiles(const int32_t* tables, int32_t max_blocks_per_seq, 
                              int32_t* tiles, int32_t max_tiles, int32_t* num_tiles);
 
 /* Workspace bytes of pkv_attention_decode_grouped: the plain decode
- * workspace plus float32 [batch][num_heads][head_dim + 4] prefix states. */
+ * workspace plus float32 prefix states [16][batch][num_heads][head_dim + 4]
+ * (up to 16 work-groups share one tile and head, each writing its part). */
 PKV_API size_t pkv_decode_grouped_workspace_bytes(int32_t batch, int32_t num_heads, int32_t head_dim,
                                                   pkv_dtype dtype, int32_t num_work_groups);
 
 /* pkv_attention_decode with shared prefixes read once per tile.
  * seq_prefix_blocks: int32 [batch] (device or pinned host), tiles: int32
  * [num_tiles][PKV_PREFIX_TILE_INTS] (device or pinned host), as written by
- * pkv_prefix_tiles from the same tables and lengths; num_tiles on the host.
+ * pkv_prefix_tiles from the same tables and lengths; num_tiles on the host,
+ * 0 to 4,194,304 (2^22; more returns PKV_ERR_INVALID).
  * dtype f16 or bf16 (a cache of another type returns PKV_ERR_INVALID).  The
  * caller guarantees that the members of a tile share their first
  * seq_prefix_blocks blocks and that every sequence with seq_prefix_blocks

@@ -111,6 +111,10 @@ constexpr int kPrefixWaves = 4;
 constexpr int kPrefixStep = 16;     // positions per step (the MFMA's M and K)
 constexpr int kPrefixIdsLds = PKV_PREFIX_MAX_BLOCKS;  // a tile's block ids, all staged in LDS
 constexpr int kPrefixPartsMax = 16;  // work-groups per (tile, head) at most
+// The prefix grid's x size is tiles × parts work-groups of 256 lanes and the
+// dispatch counts lanes in 32 bits; parts is 1 from 512 tiles on, so this cap
+// keeps every launch far inside it.
+constexpr int32_t kPrefixMaxTiles = 1 << 22;
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
@@ -447,7 +451,7 @@ int decode_grouped(void* out, const void* q, const void* k_cache, const void* v_
   const char* what = "attention_decode_grouped";
   if (batch < 0 || num_heads <= 0 || num_blocks <= 0 || max_blocks_per_seq <= 0 || max_seq_len < 0 ||
       !supported_geometry(head_dim, block_size) || (dtype != PKV_F16 && dtype != PKV_BF16) || num_tiles < 0 ||
-      num_heads > 65535)
+      num_tiles > kPrefixMaxTiles || num_heads > 65535)
     return pkv::fail(PKV_ERR_INVALID, "%s: unsupported sizes (batch %d, heads %d, head_dim %d, block %d, blocks %d, "
                                       "max_blocks %d, max_len %d, dtype %d, tiles %d)", what, batch, num_heads,
                      head_dim, block_size, num_blocks, max_blocks_per_seq, max_seq_len, static_cast<int>(dtype),

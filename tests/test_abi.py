@@ -117,6 +117,21 @@ def test_time_next_decode_takes_null_events():
     assert st == pkv.PKV_ERR_INVALID
 
 
+def test_grouped_call_rejects_bad_arguments_before_launch():
+    lib = pkv._lib
+
+    def grouped(batch=1, dtype=pkv.PKV_F16, hd=128, n_tiles=0, spb=None):
+        return lib.pkv_attention_decode_grouped(None, None, None, None, None, 4, None, 64, batch, 4, hd, 16, 8, 1.0,
+                                                dtype, spb, None, n_tiles, 0, None, 0, None)
+
+    assert grouped(dtype=pkv.PKV_F32) == pkv.PKV_ERR_INVALID   # the matrix-core path is f16 / bf16 only
+    assert grouped(hd=96) == pkv.PKV_ERR_INVALID
+    assert grouped(n_tiles=-1) == pkv.PKV_ERR_INVALID
+    assert grouped(n_tiles=(1 << 22) + 1) == pkv.PKV_ERR_INVALID  # beyond the prefix grid's cap
+    assert grouped() == pkv.PKV_ERR_INVALID                    # null prefix lengths with a non-empty batch
+    assert grouped(batch=0, n_tiles=1 << 22) == pkv.PKV_OK      # empty batch: nothing to do
+
+
 def test_workspace_queries():
     up = lambda x: -(-x // 256) * 256  # noqa: E731
     b, h, d, wg = 32, 32, 128, 512
