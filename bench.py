@@ -573,7 +573,9 @@ def main():
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
-    attn_s = float(np.mean([ev[i][layer][0].elapsed_time(ev[i][layer][1]) for i in timed for layer in range(NL)])) / 1e3
+    call_ms = np.array([ev[i][layer][0].elapsed_time(ev[i][layer][1]) for i in timed for layer in range(NL)])
+    attn_s = float(np.mean(call_ms)) / 1e3
+    call_pct = {f"p{q}": round(float(np.percentile(call_ms, q)) * 1e3, 2) for q in (10, 50, 90)}
     kv_total = float(sum(kv_bytes))
     value = kv_total / elapsed / 1e9
     unique_total = kv_total - shared_extra_tokens * tok_bytes * NL * len(kv_bytes)
@@ -657,7 +659,8 @@ def main():
                                 if prefix is not None else
                                 ("pkv_append_attention_decode" if fused else "pkv_attention_decode")
                                 + ("_quant" if kv != "dense" else "") + " (decode_kernel + decode_merge_kernel)"),
-                     "avg_call_us": round(attn_s * 1e6, 2), "algorithmic_bytes_per_call": int(algo),
+                     "avg_call_us": round(attn_s * 1e6, 2), "call_us_percentiles": call_pct,
+                     "algorithmic_bytes_per_call": int(algo),
                      "logical_kv_bytes_per_call": int(kv_per_call), "timed_calls": len(timed) * NL,
                      "timing": "kernel timestamps of the call's first and last kernel, every "
                                f"{every}-th timed step"},

@@ -32,6 +32,7 @@
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 
@@ -713,14 +714,14 @@ inline int work_groups_per_cu(pkv_dtype cache_dtype) { return is_8bit(cache_dtyp
 
 // Work-groups of the automatic choice on the current device.
 inline int32_t auto_work_groups(pkv_dtype cache_dtype) {
-  static int32_t cus_cached[64] = {0};
+  static std::atomic<int32_t> cus_cached[64];  // zero-initialised; calls from several threads may fill it
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) return pkv::fail(PKV_ERR_HIP, "no current HIP device");
-  int cus = dev < 64 ? cus_cached[dev] : 0;
+  int cus = dev < 64 ? cus_cached[dev].load(std::memory_order_relaxed) : 0;
   if (cus <= 0) {
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
       return pkv::fail(PKV_ERR_HIP, "cannot query the compute-unit count");
-    if (dev < 64) cus_cached[dev] = cus;
+    if (dev < 64) cus_cached[dev].store(cus, std::memory_order_relaxed);
   }
   return cus * work_groups_per_cu(cache_dtype);
 }
