@@ -651,37 +651,48 @@ __global__ void __launch_bounds__(kMergeWaves * 64) decode_merge_kernel(DecodeAr
 // Cumulative attention scores: one thread per (sequence, position t < L):
 //   scores[b][t] = decay * scores[b][t] + (1/H) sum_h 2^(logit[b][h][t] - M[b][h]) / S[b][h]
 // with (M, S) each head's final softmax max and sum.  A wavefront reads 64
-// consecutive positions of one head per load; a thread issues the loads of
-// kScoreHeads heads before using any, so their latencies overlap.  Sequences
-// whose length the decode kernel refused (it attended to nothing) are left
-// untouched.
-constexpr int kScoreHeads = 16;
+// consecutive positions of one head per load.  Every address is known at the
+// start, so the length, the old score, up to 64 heads' logits and their
+// (M, S) are all loaded before any of them is used: one memory round trip.
+// Lane k loads head k's (M, S) and forms 1/S; the heads' values then reach
+// every lane by v_readlane.  (Loads at one address across the wavefront
+// become scalar loads, whose waits the compiler places before the vector
+// loads.)  Threads past the longest sequence load the last position's
+// entries (inside every row) and store nothing.  Sequences whose length the
+// decode kernel refused (it attended to nothing) are left untouched.
+constexpr int kScoreHeads = 64;
+
+__device__ __forceinline__ float lane_value(float x, int k) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), k));
+}
 
 __global__ void __launch_bounds__(256) score_kernel(DecodeArgs a) {
   const int b = blockIdx.y;
   const int t = blockIdx.x * blockDim.x + threadIdx.x;
-  const int L = a.lens[b];
-  const bool ok = L >= 0 && L <= a.max_seq_len &&
-                  static_cast<int64_t>(L) <= static_cast<int64_t>(a.max_blocks) * a.block_size;
-  if (!ok || t >= L) return;
-  const float* lg = a.logits + static_cast<int64_t>(b) * a.num_heads * a.logit_stride + t;
+  const int lane = threadIdx.x & 63;
+  const int tc = min(t, a.max_seq_len - 1);  // launched only for max_seq_len >= 1
+  // The length through a per-lane load (an index the compiler cannot prove
+  // uniform, mbcnt of an empty mask = 0): a scalar load's wait would precede
+  // the vector loads below.
+  const int L = a.lens[b + static_cast<int>(__builtin_amdgcn_mbcnt_lo(0u, 0u))];
+  float* sp = a.scores + static_cast<int64_t>(b) * a.score_stride + tc;
+  const float old = *sp;
+  const float* lg = a.logits + static_cast<int64_t>(b) * a.num_heads * a.logit_stride + tc;
   const float2* ml = a.final_ml + static_cast<int64_t>(b) * a.num_heads;
   float acc = 0.f;
   for (int h0 = 0; h0 < a.num_heads; h0 += kScoreHeads) {
+    const float2 mine = ml[min(h0 + lane, a.num_heads - 1)];
     float x[kScoreHeads];
-    float2 f[kScoreHeads];
 #pragma unroll
-    for (int k = 0; k < kScoreHeads; ++k) {
-      const int h = h0 + k < a.num_heads ? h0 + k : a.num_heads - 1;
-      x[k] = lg[static_cast<int64_t>(h) * a.logit_stride];
-      f[k] = ml[h];
-    }
+    for (int k = 0; k < kScoreHeads; ++k) x[k] = lg[static_cast<int64_t>(min(h0 + k, a.num_heads - 1)) * a.logit_stride];
+    const float inv = 1.f / mine.y;
 #pragma unroll
     for (int k = 0; k < kScoreHeads; ++k)
-      if (h0 + k < a.num_heads) acc += __builtin_amdgcn_exp2f(x[k] - f[k].x) / f[k].y;
+      if (h0 + k < a.num_heads) acc += __builtin_amdgcn_exp2f(x[k] - lane_value(mine.x, k)) * lane_value(inv, k);
   }
-  float* sp = a.scores + static_cast<int64_t>(b) * a.score_stride + t;
-  *sp = a.decay * *sp + acc / static_cast<float>(a.num_heads);
+  const bool ok = L >= 0 && L <= a.max_seq_len &&
+                  static_cast<int64_t>(L) <= static_cast<int64_t>(a.max_blocks) * a.block_size;
+  if (ok && t < L) *sp = a.decay * old + acc / static_cast<float>(a.num_heads);
 }
 
 // ---- host helpers ----------------------------------------------------------
