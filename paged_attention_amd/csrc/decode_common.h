@@ -35,6 +35,7 @@
 #include <atomic>
 #include <cmath>
 #include <cstdint>
+#include <type_traits>
 
 #include "status.h"
 
@@ -217,7 +218,8 @@ struct DecodeArgs {
   const void* k_new;      // appending variant: [batch][H][D] new rows in q's dtype (else unused)
   const void* v_new;
   float* logits;          // score variant: [batch][H][logit_stride] scaled logits (log2 units), else null
-  float2* final_ml;       // score variant: [batch][H] final (max, sum) of each softmax
+  float2* final_ml;       // score variant: [batch][H] final (max, sum) of each sequence the decode kernel
+                          // attends whole (cut ones are formed from their pieces)
   float* scores;          // score variant: [batch][score_stride] cumulative scores, updated in place
   int32_t logit_stride;   // max_seq_len rounded up to kLogitGroup
   int32_t score_stride;
@@ -566,20 +568,20 @@ __global__ void __launch_bounds__(KV::kMaxWaves * 64) decode_kernel(DecodeArgs a
 // the weights reach the row holders by lane shuffles.
 constexpr int kMergeRows = 8;
 
+// Work-group (bx, v) of the merge: heads bx*kMergeWaves.. of virtual sequence v.
 template <int DT, int D>
-__global__ void __launch_bounds__(kMergeWaves * 64) decode_merge_kernel(DecodeArgs a) {
+__device__ __forceinline__ void merge_pieces(const DecodeArgs& a, int bx, int v) {
   constexpr int LPR = D / 4;     // lanes per piece row (float4 each)
   constexpr int RPW = 64 / LPR;  // rows per wavefront instruction
   constexpr int BATCH = RPW * kMergeRows;
   static_assert(BATCH <= 64, "a batch of pieces must fit one (m, l) per lane");
-  const int v = blockIdx.y;
   const int first = a.ws_plan[2 * v];
   const int count = a.ws_plan[2 * v + 1];
   if (count == 0) return;
   const int b = v % a.batch, y = v / a.batch;
   const int slice_lo = y * a.waves_per_group * a.heads_per_wave;
   const int slice_hi = min(a.num_heads, slice_lo + a.waves_per_group * a.heads_per_wave);
-  const int h = slice_lo + __builtin_amdgcn_readfirstlane(blockIdx.x * kMergeWaves + (threadIdx.x >> 6));
+  const int h = slice_lo + __builtin_amdgcn_readfirstlane(bx * kMergeWaves + (threadIdx.x >> 6));
   if (h >= slice_hi) return;
   const int lane = threadIdx.x & 63;
   const int grp = lane / LPR;
@@ -629,7 +631,6 @@ __global__ void __launch_bounds__(kMergeWaves * 64) decode_merge_kernel(DecodeAr
     o.w += __shfl_xor(o.w, off, 64);
   }
   if (grp != 0) return;
-  if (a.final_ml != nullptr && sub == 0) a.final_ml[static_cast<int64_t>(b) * a.num_heads + h] = make_float2(mx, sum);
   const float inv = 1.f / sum;
   const int64_t out_idx = (static_cast<int64_t>(b) * a.num_heads + h) * D + sub * 4;
   if constexpr (DT == PKV_F32) {
@@ -648,51 +649,126 @@ __global__ void __launch_bounds__(kMergeWaves * 64) decode_merge_kernel(DecodeAr
   }
 }
 
+template <int DT, int D>
+__global__ void __launch_bounds__(kMergeWaves * 64) decode_merge_kernel(DecodeArgs a) {
+  merge_pieces<DT, D>(a, blockIdx.x, blockIdx.y);
+}
+
 // Cumulative attention scores: one thread per (sequence, position t < L):
 //   scores[b][t] = decay * scores[b][t] + (1/H) sum_h 2^(logit[b][h][t] - M[b][h]) / S[b][h]
-// with (M, S) each head's final softmax max and sum.  A wavefront reads 64
-// consecutive positions of one head per load.  Every address is known at the
-// start, so the length, the old score, up to 64 heads' logits and their
-// (M, S) are all loaded before any of them is used: one memory round trip.
-// Lane k loads head k's (M, S) and forms 1/S; the heads' values then reach
-// every lane by v_readlane.  (Loads at one address across the wavefront
-// become scalar loads, whose waits the compiler places before the vector
-// loads.)  Threads past the longest sequence load the last position's
-// entries (inside every row) and store nothing.  Sequences whose length the
-// decode kernel refused (it attended to nothing) are left untouched.
+// with (M, S) each head's final softmax max and sum.  These work-groups run
+// in the merge kernel's launch, so they do not wait for its work-groups:
+// for a sequence the decode kernel wrote whole, (M, S) is what it stored;
+// for a cut one, (M, S) is formed here from its pieces' (m, l):
+//   M = max_i m_i,  S = sum_i l_i 2^(m_i - M).
+// Lane k works out head h0 + k's (M, S) and 1/S; the heads' values then
+// reach every lane by v_readlane.  A wavefront reads 64 consecutive
+// positions of one head per load.  The length, the old score, the logits of
+// up to 64 heads and each head's plan entry and stored (M, S) are loaded
+// before any is used (one memory round trip; a cut sequence's pieces take a
+// second).  Loads at one address across the wavefront would become scalar
+// loads, whose waits the compiler places before the vector loads, so the
+// length is read through a per-lane index.  Threads past the longest
+// sequence load the last position's entries (inside every row) and store
+// nothing.  Sequences whose length the decode kernel refused (it attended to
+// nothing) are left untouched.
 constexpr int kScoreHeads = 64;
+constexpr int kScorePieces = 16;  // pieces' (m, l) loaded per batch
 
 __device__ __forceinline__ float lane_value(float x, int k) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), k));
 }
 
-__global__ void __launch_bounds__(256) score_kernel(DecodeArgs a) {
-  const int b = blockIdx.y;
-  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+// Positions bx*256.. of sequence b.
+__device__ __forceinline__ void score_positions(const DecodeArgs& a, int bx, int b) {
+  const int t = bx * 256 + static_cast<int>(threadIdx.x);
   const int lane = threadIdx.x & 63;
   const int tc = min(t, a.max_seq_len - 1);  // launched only for max_seq_len >= 1
-  // The length through a per-lane load (an index the compiler cannot prove
-  // uniform, mbcnt of an empty mask = 0): a scalar load's wait would precede
-  // the vector loads below.
-  const int L = a.lens[b + static_cast<int>(__builtin_amdgcn_mbcnt_lo(0u, 0u))];
+  // mbcnt of an empty mask is 0 in every lane, but not provably uniform
+  const int* lp = a.lens + b + static_cast<int>(__builtin_amdgcn_mbcnt_lo(0u, 0u));
   float* sp = a.scores + static_cast<int64_t>(b) * a.score_stride + tc;
-  const float old = *sp;
+  int L = 0;
+  float old = 0.f;
   const float* lg = a.logits + static_cast<int64_t>(b) * a.num_heads * a.logit_stride + tc;
-  const float2* ml = a.final_ml + static_cast<int64_t>(b) * a.num_heads;
+  const int slice_heads = a.waves_per_group * a.heads_per_wave;
   float acc = 0.f;
-  for (int h0 = 0; h0 < a.num_heads; h0 += kScoreHeads) {
-    const float2 mine = ml[min(h0 + lane, a.num_heads - 1)];
-    float x[kScoreHeads];
+  // A batch of up to NH heads (32, or 64 when there are more than 32).  The
+  // first batch also loads the length and the old score, after its own
+  // loads: loads complete in order, so the length (host memory when the
+  // tables are pinned) must not come first.
+  auto heads = [&](int h0, auto first_batch, auto width) {
+    constexpr int NH = decltype(width)::value;
+    const int hk = min(h0 + lane, a.num_heads - 1);  // this lane's head
+    const int v = (hk / slice_heads) * a.batch + b;   // its virtual sequence
+    const int first = a.ws_plan[2 * v];
+    const int count = a.ws_plan[2 * v + 1];
+    float2 fm = a.final_ml[static_cast<int64_t>(b) * a.num_heads + hk];
+    float x[NH];
 #pragma unroll
-    for (int k = 0; k < kScoreHeads; ++k) x[k] = lg[static_cast<int64_t>(min(h0 + k, a.num_heads - 1)) * a.logit_stride];
-    const float inv = 1.f / mine.y;
+    for (int k = 0; k < NH; ++k) x[k] = lg[static_cast<int64_t>(min(h0 + k, a.num_heads - 1)) * a.logit_stride];
+    if constexpr (decltype(first_batch)::value) {
+      L = *lp;
+      old = *sp;
+    }
+    // A cut sequence combines its pieces' (m, l).  The first kScorePieces
+    // are read by every lane, at slots clamped into the sequence's range (a
+    // lane-masked load would make the compiler wait for every load in
+    // flight, the length's host read included); more pieces take a loop.
+    const float2* ml = a.ws_ml + static_cast<int64_t>(first) * a.num_heads + hk;
+    float2 p[kScorePieces];
 #pragma unroll
-    for (int k = 0; k < kScoreHeads; ++k)
-      if (h0 + k < a.num_heads) acc += __builtin_amdgcn_exp2f(x[k] - lane_value(mine.x, k)) * lane_value(inv, k);
+    for (int k = 0; k < kScorePieces; ++k)
+      p[k] = ml[static_cast<int64_t>(max(0, min(k, count - 1))) * a.num_heads];
+    float mx = -INFINITY, sum = 0.f;
+    auto fold = [&](int i0) {
+      float nmx = mx;
+#pragma unroll
+      for (int k = 0; k < kScorePieces; ++k)
+        if (i0 + k < count) nmx = fmaxf(nmx, p[k].x);
+      sum *= __builtin_amdgcn_exp2f(mx - nmx);  // 0 on the first batch
+#pragma unroll
+      for (int k = 0; k < kScorePieces; ++k)
+        if (i0 + k < count) sum = fmaf(p[k].y, __builtin_amdgcn_exp2f(p[k].x - nmx), sum);
+      mx = nmx;
+    };
+    fold(0);
+    for (int i0 = kScorePieces; i0 < count; i0 += kScorePieces) {
+#pragma unroll
+      for (int k = 0; k < kScorePieces; ++k)
+        p[k] = ml[static_cast<int64_t>(min(i0 + k, count - 1)) * a.num_heads];
+      fold(i0);
+    }
+    if (count > 0) fm = make_float2(mx, sum);
+    const float inv = 1.f / fm.y;
+#pragma unroll
+    for (int k = 0; k < NH; ++k)
+      if (h0 + k < a.num_heads) acc += __builtin_amdgcn_exp2f(x[k] - lane_value(fm.x, k)) * lane_value(inv, k);
+  };
+  // Up to 32 heads in straight-line code; more in a loop (at whose head the
+  // compiler waits for every load in flight, the length's included).
+  using Narrow = std::integral_constant<int, kScoreHeads / 2>;
+  using Wide = std::integral_constant<int, kScoreHeads>;
+  if (a.num_heads <= Narrow::value) {
+    heads(0, std::true_type{}, Narrow{});
+  } else {
+    L = *lp;
+    old = *sp;
+    for (int h0 = 0; h0 < a.num_heads; h0 += kScoreHeads) heads(h0, std::false_type{}, Wide{});
   }
   const bool ok = L >= 0 && L <= a.max_seq_len &&
                   static_cast<int64_t>(L) <= static_cast<int64_t>(a.max_blocks) * a.block_size;
   if (ok && t < L) *sp = a.decay * old + acc / static_cast<float>(a.num_heads);
+}
+
+// The score variant's second launch: work-groups (x < merge_x, v) merge the
+// pieces of virtual sequence v; work-groups (merge_x + bx, b < batch) score
+// positions bx*256.. of sequence b.  Neither waits for the other.
+template <int DT, int D>
+__global__ void __launch_bounds__(kMergeWaves * 64) merge_score_kernel(DecodeArgs a, int merge_x) {
+  static_assert(kMergeWaves * 64 == 256, "merge and score work-groups share the launch's shape");
+  const int x = blockIdx.x;
+  if (x < merge_x) merge_pieces<DT, D>(a, x, blockIdx.y);
+  else if (static_cast<int>(blockIdx.y) < a.batch) score_positions(a, x - merge_x, blockIdx.y);
 }
 
 // ---- host helpers ----------------------------------------------------------
@@ -783,9 +859,10 @@ inline Layout workspace_layout(int32_t batch, int32_t num_heads, int32_t head_di
   return w;
 }
 
-// Kernels of one launch_decode: the decode kernel, the merge kernel and, for
-// a score request, the score kernel.  `tm.start` goes with the first of them
-// and `tm.stop` with the last (kernel timestamps, no extra queue packets).
+// Kernels of one launch_decode: the decode kernel, then the merge kernel (for
+// a score request, the merge and score kernel).  `tm.start` goes with the
+// first and `tm.stop` with the second (kernel timestamps, no extra queue
+// packets).
 template <class KV, int D, int BS, int MODE>
 void launch_decode(const DecodeArgs& a, int wg, hipStream_t stream, const pkv::CallEvents& tm) {
   const size_t lds = 2 * (static_cast<size_t>(a.batch) * a.groups_y + 1) * sizeof(int32_t);
@@ -793,12 +870,14 @@ void launch_decode(const DecodeArgs& a, int wg, hipStream_t stream, const pkv::C
   hipExtLaunchKernelGGL((decode_kernel<KV, D, BS, MODE>), dim3(wg), dim3(a.waves_per_group * 64), lds, stream,
                         tm.start, nullptr, 0, a);
   const int slice_heads = a.waves_per_group * a.heads_per_wave;
-  dim3 mgrid(ceil_div(slice_heads, kMergeWaves), a.batch * a.groups_y);
-  hipExtLaunchKernelGGL((decode_merge_kernel<KV::QT, D>), mgrid, dim3(kMergeWaves * 64), 0, stream, nullptr,
-                        scores ? nullptr : tm.stop, 0, a);
+  const int merge_x = ceil_div(slice_heads, kMergeWaves);
   if (scores)
-    hipExtLaunchKernelGGL(score_kernel, dim3(ceil_div(a.max_seq_len, 256), a.batch), dim3(256), 0, stream, nullptr,
-                          tm.stop, 0, a);
+    hipExtLaunchKernelGGL((merge_score_kernel<KV::QT, D>),
+                          dim3(merge_x + ceil_div(a.max_seq_len, 256), a.batch * a.groups_y), dim3(kMergeWaves * 64),
+                          0, stream, nullptr, tm.stop, 0, a, merge_x);
+  else
+    hipExtLaunchKernelGGL((decode_merge_kernel<KV::QT, D>), dim3(merge_x, a.batch * a.groups_y),
+                          dim3(kMergeWaves * 64), 0, stream, nullptr, tm.stop, 0, a);
 }
 
 template <class KV, int D, int MODE>
