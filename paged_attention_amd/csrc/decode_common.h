@@ -566,7 +566,7 @@ __global__ void __launch_bounds__(KV::kMaxWaves * 64) decode_kernel(DecodeArgs a
 // float4, kMergeRows rows per group.  Every load of a batch of pieces is
 // issued before any of them is used, so a batch costs one memory round trip;
 // the weights reach the row holders by lane shuffles.
-constexpr int kMergeRows = 16;
+constexpr int kMergeRows = 8;
 
 // Work-group (bx, v) of the merge: heads bx*kMergeWaves.. of virtual sequence v.
 template <int DT, int D>
