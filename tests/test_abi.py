@@ -40,6 +40,39 @@ def test_library_exports_every_declared_symbol():
         getattr(lib, n)
 
 
+def _c_kind(decl: str):
+    """Kind of a C parameter or return type: ptr, i32, i64, size, f32 or void."""
+    d = " ".join(decl.replace("const ", "").split())
+    if "*" in d or d.split()[0] in ("hipStream_t", "hipEvent_t"):
+        return "ptr"
+    t = d.split()[0]
+    return {"int32_t": "i32", "int": "i32", "pkv_dtype": "i32", "int64_t": "i64", "size_t": "size",
+            "float": "f32", "void": "void"}[t]
+
+
+def _ctypes_kind(t):
+    if t is None:
+        return "void"
+    if t in (ctypes.c_void_p, ctypes.c_char_p) or (isinstance(t, type) and issubclass(t, ctypes._Pointer)):
+        return "ptr"
+    return {ctypes.c_int32: "i32", ctypes.c_int64: "i64", ctypes.c_size_t: "size", ctypes.c_float: "f32"}[t]
+
+
+def test_binding_signatures_match_the_header():
+    with open(os.path.join(ROOT, "include", "pkv.h")) as f:
+        text = re.sub(r"/\*.*?\*/", "", f.read(), flags=re.S)
+    decls = re.findall(r"PKV_API\s+([^;(]*?)\b(pkv_\w+)\s*\(([^)]*)\)\s*;", text, flags=re.S)
+    assert len(decls) == len(_declared())
+    for ret, name, params in decls:
+        params = [q for q in (x.strip() for x in params.split(",")) if q and q != "void"]
+        fn = getattr(pkv._lib, name)
+        assert fn.argtypes is not None, name
+        want = [_c_kind(q.rsplit(" ", 1)[0] if "*" not in q.rsplit(" ", 1)[-1] else q) for q in params]
+        got = [_ctypes_kind(t) for t in fn.argtypes]
+        assert got == want, (name, got, want)
+        assert _ctypes_kind(fn.restype) == _c_kind(ret.strip()), (name, fn.restype, ret)
+
+
 def test_status_strings_and_version():
     lib = pkv._lib
     assert pkv.version() >= 100
