@@ -438,8 +438,10 @@ PKV_API int pkv_append_attention_decode_quant(void* out, const void* q, const vo
  * the decode output is averaged with).  Positions >= L and sequences with an
  * invalid length are untouched; a row starts from zero when its sequence
  * starts (the caller zeroes it).  The decode launch stores each position's
- * scaled logit and each head's final softmax (max, sum) in
- * `scores_workspace`; a third kernel on the stream folds them into `scores`.
+ * scaled logit, and each head's final softmax (max, sum) for sequences it
+ * attends in one piece, in `scores_workspace`; the second launch on the
+ * stream merges split sequences and folds the logits into `scores` (for a
+ * split sequence it forms each head's (max, sum) from the pieces).
  * ------------------------------------------------------------------------- */
 
 /* Bytes of the score workspace: float32 logits [batch][num_heads][S] with S =
