@@ -307,16 +307,16 @@ def run_swap(args):
 
 def main():
     args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (how the path would shard "
+              f"across GPUs is described in the design notes)", file=sys.stderr)
+        sys.exit(2)
     if args.component == "prefix_cache":
         run_prefix_cache(args)
         return
     if args.component == "swap":
         run_swap(args)
         return
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported by this single-GPU build "
-              f"(how the path would shard is described in the design notes)", file=sys.stderr)
-        sys.exit(2)
     import torch
 
     import paged_attention_amd as pkv
