@@ -156,6 +156,18 @@ _i32p = _ptr
 _i64p = _ptr
 
 
+def _host_array(arr, dtype, name, ndim=None, size=None, size_at_least=None) -> None:
+    """Checks a host array handed to the library as a raw pointer."""
+    if not isinstance(arr, np.ndarray) or arr.dtype != dtype or not arr.flags.c_contiguous:
+        raise ValueError(f"{name} must be a C-contiguous numpy array of {np.dtype(dtype).name}")
+    if ndim is not None and arr.ndim != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions, not {arr.ndim}")
+    if size is not None and arr.size != size:
+        raise ValueError(f"{name} must hold {size} elements, not {arr.size}")
+    if size_at_least is not None and arr.size < size_at_least:
+        raise ValueError(f"{name} must hold at least {size_at_least} elements, not {arr.size}")
+
+
 class BlockAllocator:
     """Host block allocator (FIFO free queue + reference counts), backed by libpkv."""
 
@@ -243,8 +255,8 @@ class BlockAllocator:
         ``n_blocks`` (int32 [B]) is updated in place.  Returns (slots int64
         [sum n_new], pairs int32 [k][2]).
         """
-        assert tables.dtype == np.int32 and tables.flags.c_contiguous and tables.ndim == 2
-        assert n_blocks.dtype == np.int32 and n_blocks.flags.c_contiguous
+        _host_array(tables, np.int32, "tables", ndim=2)
+        _host_array(n_blocks, np.int32, "n_blocks", size=tables.shape[0])
         lens = np.ascontiguousarray(cur_lens, dtype=np.int32)
         new = np.ascontiguousarray(n_new, dtype=np.int32)
         batch = tables.shape[0]
@@ -261,6 +273,14 @@ class BlockAllocator:
         """As :meth:`reserve_batch`, writing into caller arrays (e.g. pinned staging
         memory); every array must already be C-contiguous of the right dtype
         (int32, slots int64).  Returns the number of copy pairs written."""
+        batch = tables.shape[0] if isinstance(tables, np.ndarray) else 0
+        _host_array(tables, np.int32, "tables", ndim=2)
+        for arr, name in ((n_blocks, "n_blocks"), (cur_lens, "cur_lens"), (n_new, "n_new")):
+            _host_array(arr, np.int32, name, size=batch)
+        _host_array(slots_out, np.int64, "slots_out", size_at_least=int(np.asarray(n_new).sum()))
+        _host_array(pairs_out, np.int32, "pairs_out", ndim=2)
+        if pairs_out.shape[1] != 2:
+            raise ValueError("pairs_out must have shape [k][2]")
         ncow = ctypes.c_int32(0)
         _check(_lib.pkv_seq_reserve_batch(self._h, _i32p(tables), tables.shape[1], _i32p(n_blocks), _i32p(cur_lens),
                                           _i32p(n_new), tables.shape[0], _i64p(slots_out), _i32p(pairs_out),

@@ -323,3 +323,31 @@ def test_allocator_under_sanitizers(tmp_path):
                              env={**os.environ, "ASAN_OPTIONS": "detect_leaks=1"})
         assert res.returncode == 0, res.stderr
         assert res.stdout.split("\n")[:-1] == want, f"trial {trial}"
+
+
+def test_batch_reservation_refuses_wrong_host_arrays():
+    a = pkv.BlockAllocator(64, 16)
+    B = 3
+    tables = np.zeros((B, 8), np.int32)
+    nblk = np.zeros(B, np.int32)
+    cur = np.zeros(B, np.int32)
+    new = np.ones(B, np.int32)
+    slots = np.zeros(B, np.int64)
+    pairs = np.zeros((B, 2), np.int32)
+    assert a.reserve_batch_into(tables, nblk, cur, new, slots, pairs) == 0
+    bad = [
+        (tables.astype(np.int64), nblk, cur, new, slots, pairs),          # table dtype
+        (tables[:, ::2], nblk, cur, new, slots, pairs),                     # not contiguous
+        (tables, nblk[:2], cur, new, slots, pairs),                         # short n_blocks
+        (tables, nblk, cur.astype(np.int64), new, slots, pairs),            # lengths dtype
+        (tables, nblk, cur, new, slots.astype(np.int32), pairs),            # slots dtype
+        (tables, nblk, cur, new * 2, slots, pairs),                         # slots too short for the new tokens
+        (tables, nblk, cur, new, slots, np.zeros((B, 3), np.int32)),        # pairs shape
+    ]
+    for args in bad:
+        with pytest.raises(ValueError):
+            a.reserve_batch_into(*args)
+    with pytest.raises(ValueError):
+        a.reserve_batch(tables.astype(np.int64), nblk, [0] * B, [1] * B)
+    # nothing was reserved by the refused calls
+    assert a.num_free() == 64 - B
