@@ -592,8 +592,9 @@ def main():
     if fused:   # the launch also reads the new rows and writes them (8-bit: codes and scales) into the pools
         algo += 2 * B * H * D * esz + B * tok_bytes
     achieved = algo / attn_s / 1e9
+    # one record per distinct call (format, fused append, scores, grouping, layer rotation)
     traffic = recorded_traffic(args.workload + ("" if kv == "dense" else f"/{kv}") + ("/fused" if fused else "")
-                               + ("/grouped" if prefix is not None else "")
+                               + ("/scores" if args.scores else "") + ("/grouped" if prefix is not None else "")
                                + (f"/layers{args.layers}" if args.layers > 0 else ""))
 
     extra = {}
@@ -657,6 +658,8 @@ def main():
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "kernel": ("pkv_attention_decode_grouped (prefix_kernel + decode_kernel + decode_merge_kernel)"
                                 if prefix is not None else
+                                "pkv_attention_decode_scores (decode_kernel + merge_score_kernel)"
+                                if args.scores else
                                 ("pkv_append_attention_decode" if fused else "pkv_attention_decode")
                                 + ("_quant" if kv != "dense" else "") + " (decode_kernel + decode_merge_kernel)"),
                      "avg_call_us": round(attn_s * 1e6, 2), "call_us_percentiles": call_pct,
