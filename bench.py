@@ -593,7 +593,9 @@ def main():
         algo += 2 * B * H * D * esz + B * tok_bytes
     achieved = algo / attn_s / 1e9
     # one record per distinct call (format, fused append, scores, grouping, layer rotation)
-    traffic = recorded_traffic(args.workload + ("" if kv == "dense" else f"/{kv}") + ("/fused" if fused else "")
+    traffic = recorded_traffic(args.workload + (f"/bs{args.block_size}" if args.workload == "long13b"
+                                                and args.block_size != 16 else "")
+                               + ("" if kv == "dense" else f"/{kv}") + ("/fused" if fused else "")
                                + ("/scores" if args.scores else "") + ("/grouped" if prefix is not None else "")
                                + (f"/layers{args.layers}" if args.layers > 0 else ""))
 
