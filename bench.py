@@ -75,8 +75,9 @@ def parse():
                         "single-layer workloads N > 1 keeps one call's K rows from still being cached at the next")
     p.add_argument("--work-groups", type=int, default=0, help="decode work-groups (0 = library choice)")
     p.add_argument("--ring", type=int, default=4, help="host staging buffers (how many steps the host may run ahead)")
-    p.add_argument("--metadata", choices=["pinned", "device"], default="pinned",
-                   help="where kernels read step metadata: pinned host memory in place, or a device copy")
+    p.add_argument("--metadata", choices=["pinned", "device", "staged"], default="pinned",
+                   help="where kernels read step metadata: pinned host memory in place, a device copy on the "
+                        "compute stream, or a device copy per ring slot made on a second stream")
     p.add_argument("--kv-dtype", choices=["auto", "i8", "fp8"], default="auto",
                    help="K/V cache storage: the workload's dtype (auto) or an 8-bit format")
     p.add_argument("--scores", action="store_true",
@@ -454,9 +455,19 @@ def main():
     stream = torch.cuda.current_stream()
     # Calls checked once; each step only swaps the per-step row pointers.  In
     # pinned mode every ring slot has its own set of calls pointing into it.
+    copy_stream, d_slots = None, None
     if mode == "device":
         d_meta = torch.empty(nbytes, dtype=torch.uint8, device=dev)
         metas = [split(d_meta)] * ring
+    elif mode == "staged":
+        # one device copy per ring slot, made on a second stream (default
+        # priority) so that it runs beside the previous step's kernels
+        d_meta = None
+        d_slots = [torch.empty(nbytes, dtype=torch.uint8, device=dev) for _ in range(ring)]
+        metas = [split(dm) for dm in d_slots]
+        copy_stream = torch.cuda.Stream(device=dev)
+        copied = [torch.cuda.Event() for _ in range(ring)]
+        slot_read = [None] * ring          # event after the kernels that last read device slot r
     else:
         d_meta = None
         metas = [split(hm) for hm in h_meta]
@@ -537,6 +548,13 @@ def main():
         tab_v[:] = tables
         if d_meta is not None:
             d_meta.copy_(h_meta[r], non_blocking=True)                 # 2. stage metadata (one copy)
+        if d_slots is not None:                                        # 2. stage on the copy stream
+            if slot_read[r] is not None:
+                copy_stream.wait_event(slot_read[r])
+            with torch.cuda.stream(copy_stream):
+                d_slots[r].copy_(h_meta[r], non_blocking=True)
+            copied[r].record(copy_stream)
+            stream.wait_event(copied[r])
         if npairs:                                                     # 3. copy-on-write
             d_pairs[:npairs].copy_(h_pairs[r][:npairs], non_blocking=True)
             pkv.pkv_copy_blocks(k_caches, v_caches, d_pairs[:npairs])
@@ -556,8 +574,10 @@ def main():
                 if i in ev:
                     pkv.pkv_time_next_decode(*ev[i][layer])
                 decodes[layer].launch(q_all[i, layer])                     # 5. decode attention
-        if d_meta is None:                                             # read in place until here
-            released[r].record(stream)
+        if d_meta is None:                                             # read (in place, or the device
+            released[r].record(stream)                                 # slot) until here; the copy-on-
+        if d_slots is not None:                                        # write pairs too
+            slot_read[r] = released[r]
         h_done[r] = released[r]
         kv_bytes.append(int(cur.astype(np.int64).sum()) * tok_bytes * NL)
         table_entries.append(int(((cur.astype(np.int64) + bs - 1) // bs).sum()))
