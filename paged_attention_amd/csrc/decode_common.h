@@ -663,12 +663,13 @@ __global__ void __launch_bounds__(kMergeWaves * 64) decode_merge_kernel(DecodeAr
 //   M = max_i m_i,  S = sum_i l_i 2^(m_i - M).
 // Lane k works out head h0 + k's (M, S) and 1/S; the heads' values then
 // reach every lane by v_readlane.  A wavefront reads 64 consecutive
-// positions of one head per load.  The length, the old score, the logits of
-// up to 64 heads and each head's plan entry and stored (M, S) are loaded
-// before any is used (one memory round trip; a cut sequence's pieces take a
-// second).  Loads at one address across the wavefront would become scalar
-// loads, whose waits the compiler places before the vector loads, so the
-// length is read through a per-lane index.  Threads past the longest
+// positions of one head per load.  Two memory round trips: each head's plan
+// entry, then together the logits of up to 32 (or 64) heads, the stored
+// (M, S), a cut sequence's first pieces' (m, l), the old score and, last,
+// the length (loads complete in order, and the length may be a host read).
+// Loads at one address across the wavefront would become scalar loads,
+// whose waits the compiler places before the vector loads, so the length is
+// read through a per-lane index.  Threads past the longest
 // sequence load the last position's entries (inside every row) and store
 // nothing.  Sequences whose length the decode kernel refused (it attended to
 // nothing) are left untouched.

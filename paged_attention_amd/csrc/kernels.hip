@@ -184,7 +184,6 @@ __global__ void __launch_bounds__(kPrefixWaves * 64) prefix_kernel(DecodeArgs a,
   const int lane = threadIdx.x & 63;
   const int col = lane & 15, grp = lane >> 4;
   const int prefix_tokens = P * BS;
-  const int64_t row_elems = static_cast<int64_t>(a.num_heads) * D;
   const uint16_t* kpool = static_cast<const uint16_t*>(a.k);
   const uint16_t* vpool = static_cast<const uint16_t*>(a.v);
   const int32_t* trow = a.tables + static_cast<int64_t>(lead) * a.max_blocks;
