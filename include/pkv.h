@@ -39,6 +39,13 @@
  *     f32, f16 or bf16.  Anything else returns PKV_ERR_INVALID.
  *   - The allocator is not thread-safe; callers serialise access to one
  *     allocator.  Device operations are reentrant.
+ *   - Device-side indices are always range-checked, in every build: a block
+ *     id outside [0, num_blocks) or a slot outside the pool is never used to
+ *     form an address.  Decode calls turn such a sequence's output into NaN
+ *     rows; scatter and block copies skip the row or pair.  (The page this
+ *     follows checks its indices with asserts in debug builds only,
+ *     m.lqnn.cn/news/240480 §5.2 tip 3; here the check is one compare per
+ *     64 block ids and stays on, and there is no build that traps.)
  */
 #ifndef PKV_H_
 #define PKV_H_
@@ -117,6 +124,12 @@ PKV_API void pkv_allocator_destroy(pkv_allocator* a);
  * 1.  PKV_ERR_NO_BLOCKS when nothing is available — the pool is full and the
  * caller queues the request (hnwysp.cn/news/103996 §4.4 alloc_block). */
 PKV_API int pkv_block_alloc(pkv_allocator* a, int32_t* block_out);
+/* Take n blocks at once, each as pkv_block_alloc would in turn, into
+ * blocks_out[0 .. n).  All or nothing: PKV_ERR_NO_BLOCKS takes nothing when
+ * fewer than n are available (the page pool's allocate_pages(n), which
+ * checks the free count before taking pages from the front,
+ * m.lqnn.cn/news/240480 §4.2).  Release them with pkv_seq_release. */
+PKV_API int pkv_blocks_alloc(pkv_allocator* a, int32_t n, int32_t* blocks_out);
 /* Share a block: count + 1.  PKV_ERR_REFCOUNT if the block is free
  * (hnwysp.cn/news/103996 §3.3: a prefix hit raises the count). */
 PKV_API int pkv_block_incref(pkv_allocator* a, int32_t block);

@@ -79,6 +79,7 @@ def _load():
         "pkv_allocator_create": (ctypes.c_int, [i32, i32, p32, ctypes.POINTER(vp)]),
         "pkv_allocator_destroy": (None, [vp]),
         "pkv_block_alloc": (ctypes.c_int, [vp, p32]),
+        "pkv_blocks_alloc": (ctypes.c_int, [vp, i32, p32]),
         "pkv_block_incref": (ctypes.c_int, [vp, i32]),
         "pkv_block_decref": (ctypes.c_int, [vp, i32]),
         "pkv_block_refcount": (ctypes.c_int, [vp, i32]),
@@ -203,6 +204,14 @@ class BlockAllocator:
         out = ctypes.c_int32()
         _check(_lib.pkv_block_alloc(self._h, ctypes.byref(out)))
         return out.value
+
+    def alloc_n(self, n: int, out: np.ndarray | None = None) -> np.ndarray:
+        """Take ``n`` blocks at once (all or nothing); returns their ids (int32), in ``out`` if given."""
+        if out is None:
+            out = np.zeros(max(1, n), dtype=np.int32)
+        _host_array(out, np.int32, "out", size_at_least=n)
+        _check(_lib.pkv_blocks_alloc(self._h, n, _i32p(out)))
+        return out[:n]
 
     def incref(self, block: int) -> None:
         _check(_lib.pkv_block_incref(self._h, block))
@@ -476,14 +485,28 @@ def pkv_decode_workspace_bytes(batch, num_heads, head_dim, dtype, work_groups=0)
 _DT_NAMES = {PKV_F32: "f32", PKV_F16: "f16", PKV_BF16: "bf16", PKV_I8: "i8", PKV_FP8_E4M3: "fp8"}
 
 
-def decode_workspace(batch, num_heads, head_dim, dtype, work_groups=0, device="cuda"):
-    """Allocate a workspace for these decode sizes (a uint8 tensor)."""
+def _bytes_on(nbytes, device, stream):
+    """A uint8 tensor allocated for use on ``stream`` (the current stream when None).
+
+    torch's caching allocator hands a freed block back only to later work on
+    the stream it was allocated on, so a workspace the wrappers drop right
+    after enqueueing a call on ``stream`` cannot be reused by work on another
+    stream while that call's kernels still write it.
+    """
     torch = _torch()
+    if stream is None:
+        return torch.empty(nbytes, dtype=torch.uint8, device=device)
+    with torch.cuda.stream(stream):
+        return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def decode_workspace(batch, num_heads, head_dim, dtype, work_groups=0, device="cuda", stream=None):
+    """Allocate a workspace for these decode sizes (a uint8 tensor) for use on ``stream``."""
     need = pkv_decode_workspace_bytes(batch, num_heads, head_dim, dtype, work_groups)
     if need == 0:
         detail = _lib.pkv_last_error().decode()
         raise InvalidArgument(PKV_ERR_INVALID, f"decode_workspace: unsupported sizes ({detail})")
-    return torch.empty(need, dtype=torch.uint8, device=device)
+    return _bytes_on(need, device, stream)
 
 
 def _decode_args(out, q, k_cache, v_cache, block_tables, seq_lens, max_seq_len, scale, work_groups, workspace,
@@ -501,7 +524,7 @@ def _decode_args(out, q, k_cache, v_cache, block_tables, seq_lens, max_seq_len, 
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if workspace is None:
-        workspace = decode_workspace(max(batch, 1), h, d, _DT_NAMES[code], work_groups, q.device)
+        workspace = decode_workspace(max(batch, 1), h, d, _DT_NAMES[code], work_groups, q.device, stream)
     args = [_dev(out, "out"), _dev(q, "q"), _dev(k_cache, "k_cache", ndim=4), _dev(v_cache, "v_cache", ndim=4),
             _dev(block_tables, "block_tables", torch.int32, pinned_ok=True), block_tables.shape[1],
             _dev(seq_lens, "seq_lens", torch.int32, pinned_ok=True), int(max_seq_len), batch, h, d, bs, nb,
@@ -557,7 +580,7 @@ def _grouped_args(out, q, k_cache, v_cache, block_tables, seq_lens, max_seq_len,
         need = pkv_decode_grouped_workspace_bytes(max(batch, 1), h, d, _DT_NAMES[_dtype_code(q)], work_groups)
         if need == 0:
             raise InvalidArgument(PKV_ERR_INVALID, "attention_decode_grouped: unsupported sizes")
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = _bytes_on(need, q.device, stream)
     args, _ = _decode_args(out, q, k_cache, v_cache, block_tables, seq_lens, max_seq_len, scale, work_groups,
                            workspace, stream)
     if seq_prefix_blocks.shape != (batch,) or tiles.dim() != 2 or tiles.shape[1] != PREFIX_TILE_INTS:
@@ -611,7 +634,7 @@ class PreparedDecode:
         self._shape, self._dtype = tuple(q.shape), q.dtype
         self._fn = _lib.pkv_attention_decode
         if scores is not None:   # also update cumulative attention scores
-            extra, sws = _score_args(scores, q, max_seq_len, decay, scores_ws)
+            extra, sws = _score_args(scores, q, max_seq_len, decay, scores_ws, stream)
             self._args = self._args[:-1] + extra + self._args[-1:]
             self._keep = self._keep + (scores, sws)
             self._fn = _lib.pkv_attention_decode_scores
@@ -722,7 +745,7 @@ def _decode_quant_args(out, q, k_cache, v_cache, k_scales, v_scales, block_table
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if workspace is None:
-        workspace = decode_workspace(max(batch, 1), h, d, cache_dtype, work_groups, q.device)
+        workspace = decode_workspace(max(batch, 1), h, d, cache_dtype, work_groups, q.device, stream)
     args = [_dev(out, "out"), _dev(q, "q"), *pools,
             _dev(block_tables, "block_tables", torch.int32, pinned_ok=True), block_tables.shape[1],
             _dev(seq_lens, "seq_lens", torch.int32, pinned_ok=True), int(max_seq_len), batch, h, d, bs, nb,
@@ -782,20 +805,19 @@ def pkv_decode_scores_workspace_bytes(batch, num_heads, max_seq_len) -> int:
     return int(_lib.pkv_decode_scores_workspace_bytes(batch, num_heads, max_seq_len))
 
 
-def scores_workspace(batch, num_heads, max_seq_len, device="cuda"):
-    """Allocate the workspace a score-updating decode call needs (a uint8 tensor)."""
-    torch = _torch()
+def scores_workspace(batch, num_heads, max_seq_len, device="cuda", stream=None):
+    """Allocate the workspace a score-updating decode call needs (a uint8 tensor) for use on ``stream``."""
     need = pkv_decode_scores_workspace_bytes(batch, num_heads, max_seq_len)
-    return torch.empty(max(need, 1), dtype=torch.uint8, device=device)
+    return _bytes_on(max(need, 1), device, stream)
 
 
-def _score_args(scores, q, max_seq_len, decay, scores_ws):
+def _score_args(scores, q, max_seq_len, decay, scores_ws, stream):
     torch = _torch()
     batch = q.shape[0]
     if scores.dim() != 2 or scores.shape[0] != batch or scores.shape[1] < max_seq_len:
         raise InvalidArgument(PKV_ERR_INVALID, "scores must be float32 [batch][>= max_seq_len]")
     if scores_ws is None:
-        scores_ws = scores_workspace(batch, q.shape[1], int(max_seq_len), q.device)
+        scores_ws = scores_workspace(batch, q.shape[1], int(max_seq_len), q.device, stream)
     return [_dev(scores, "scores", torch.float32), scores.shape[1], float(decay), _dev(scores_ws, "scores_ws"),
             scores_ws.numel() * scores_ws.element_size()], scores_ws
 
@@ -807,7 +829,7 @@ def pkv_attention_decode_scores(out, q, k_cache, v_cache, block_tables, seq_lens
         return
     args, _ = _decode_args(out, q, k_cache, v_cache, block_tables, seq_lens, max_seq_len, scale, work_groups,
                            workspace, stream)
-    extra, _ = _score_args(scores, q, max_seq_len, decay, scores_ws)
+    extra, _ = _score_args(scores, q, max_seq_len, decay, scores_ws, stream)
     _check(_lib.pkv_attention_decode_scores(*(args[:-1] + extra + args[-1:])))
 
 
@@ -819,7 +841,7 @@ def pkv_attention_decode_quant_scores(out, q, k_cache, v_cache, k_scales, v_scal
         return
     args, _ = _decode_quant_args(out, q, k_cache, v_cache, k_scales, v_scales, block_tables, seq_lens, max_seq_len,
                                  cache_dtype, scale, work_groups, workspace, stream)
-    extra, _ = _score_args(scores, q, max_seq_len, decay, scores_ws)
+    extra, _ = _score_args(scores, q, max_seq_len, decay, scores_ws, stream)
     _check(_lib.pkv_attention_decode_quant_scores(*(args[:-1] + extra + args[-1:])))
 
 

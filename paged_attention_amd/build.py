@@ -44,18 +44,17 @@ def _run(cmd, verbose):
     return res
 
 
-def build(verbose: bool = False, debug: bool = False) -> str:
+def build(verbose: bool = False) -> str:
     """Compile all sources and link libpkv.so; returns the library path."""
     os.makedirs(BUILD, exist_ok=True)
-    extra = ["-DPKV_DEBUG", "-g"] if debug else []
     jobs = []
     for src in HIP_SOURCES:
         obj = os.path.join(BUILD, src + ".o")
-        jobs.append([HIPCC, *COMMON, *DEVICE, *extra, "-c", os.path.join(CSRC, src), "-o", obj])
+        jobs.append([HIPCC, *COMMON, *DEVICE, "-c", os.path.join(CSRC, src), "-o", obj])
     for src in HOST_SOURCES:
         obj = os.path.join(BUILD, src + ".o")
         # Host-only C++ (no device code): compiled by hipcc's clang as plain C++.
-        jobs.append([HIPCC, *COMMON, *extra, f"-I{ROCM}/include", "-D__HIP_PLATFORM_AMD__", "-x", "c++", "-c",
+        jobs.append([HIPCC, *COMMON, f"-I{ROCM}/include", "-D__HIP_PLATFORM_AMD__", "-x", "c++", "-c",
                      os.path.join(CSRC, src), "-o", obj])
     with ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:
         list(ex.map(lambda c: _run(c, verbose), jobs))
@@ -67,4 +66,4 @@ def build(verbose: bool = False, debug: bool = False) -> str:
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv, debug="--debug" in sys.argv))
+    print(build(verbose="-v" in sys.argv))

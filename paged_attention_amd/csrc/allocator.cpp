@@ -70,6 +70,12 @@ struct pkv_allocator {
   // list (doubly linked through lru_prev / lru_next) instead of the free
   // queue, and stays matchable until the free queue is empty and it is the
   // least recently released.
+  // Duplicate detection for rows handed to release and fork: stamp[b] ==
+  // epoch marks an id already seen in the row being checked (one linear
+  // pass; a new epoch per check, the stamps cleared when it wraps).
+  mutable std::vector<uint32_t> stamp;
+  mutable uint32_t epoch = 0;
+
   bool cache_on = false;
   std::vector<Key> key_of;
   std::vector<uint8_t> cached;
@@ -143,6 +149,16 @@ int check_row(const pkv_allocator* a, const int32_t* row, int32_t n, const char*
     if (a->ref[b] < 1) return pkv::fail(PKV_ERR_REFCOUNT, "%s: block %d is free", what, b);
   }
   if (!count_duplicates || n < 2) return PKV_OK;
+  if (++a->epoch == 0) {
+    std::fill(a->stamp.begin(), a->stamp.end(), 0u);
+    a->epoch = 1;
+  }
+  bool repeats = false;
+  for (int32_t j = 0; j < n && !repeats; ++j) {
+    repeats = a->stamp[row[j]] == a->epoch;
+    a->stamp[row[j]] = a->epoch;
+  }
+  if (!repeats) return PKV_OK;  // each id once: referenced ids cannot underflow
   std::vector<int32_t> sorted(row, row + n);
   std::sort(sorted.begin(), sorted.end());
   for (int32_t j = 0; j < n;) {
@@ -229,6 +245,7 @@ PKV_API int pkv_allocator_create(int32_t num_blocks, int32_t block_size, const i
   try {
     a->ring.resize(num_blocks);
     a->ref.assign(num_blocks, 0);
+    a->stamp.assign(num_blocks, 0u);
   } catch (...) {
     delete a;
     return pkv::fail(PKV_ERR_INVALID, "allocator_create: out of host memory");
@@ -261,6 +278,15 @@ PKV_API int pkv_block_alloc(pkv_allocator* a, int32_t* block_out) {
   if (a == nullptr || block_out == nullptr) return pkv::fail(PKV_ERR_INVALID, "block_alloc: null argument");
   if (a->available() == 0) return pkv::fail(PKV_ERR_NO_BLOCKS, "block_alloc: pool of %d blocks is full", a->num_blocks);
   *block_out = a->pop();
+  return PKV_OK;
+}
+
+PKV_API int pkv_blocks_alloc(pkv_allocator* a, int32_t n, int32_t* blocks_out) {
+  if (a == nullptr || n < 0 || (blocks_out == nullptr && n > 0))
+    return pkv::fail(PKV_ERR_INVALID, "blocks_alloc: null argument or negative count");
+  if (n > a->available())
+    return pkv::fail(PKV_ERR_NO_BLOCKS, "blocks_alloc: %d blocks asked, %d available", n, a->available());
+  for (int32_t i = 0; i < n; ++i) blocks_out[i] = a->pop();
   return PKV_OK;
 }
 

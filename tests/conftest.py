@@ -1,3 +1,4 @@
+import json
 import os
 import sys
 
@@ -18,3 +19,16 @@ def pytest_configure(config):
 @pytest.fixture(scope="session")
 def golden_dir():
     return GOLDEN
+
+
+def pytest_sessionfinish(session, exitstatus):
+    """Writes the largest error of every recorded parity case (GPU runs) to
+    gpurun_out/parity_max_err.json, so the margins survive a quiet run."""
+    mod = sys.modules.get("tests.paged_case")
+    errors = getattr(mod, "ERRORS", None)
+    if not errors:
+        return
+    out_dir = os.path.join(ROOT, "gpurun_out")
+    os.makedirs(out_dir, exist_ok=True)
+    with open(os.path.join(out_dir, "parity_max_err.json"), "w") as f:
+        json.dump(dict(sorted(errors.items())), f, indent=1)

@@ -213,19 +213,22 @@ def run_gpu(c: Case, work_groups=0, out=None):
 
 
 def tolerance(dtype: str, ref: np.ndarray) -> np.ndarray:
-    """Per-element bound: 1e-5 for fp32 and 2e-3 for fp16.  For bf16 the bound
-    is 2e-3 plus the output's own rounding (half a unit in the last place of
-    the stored result), which alone exceeds 2e-3 once |out| >= 1."""
+    """Per-element bound: 1e-5 for fp32, 2e-3 for fp16 and for bf16 results
+    below 0.5 in magnitude.  A bf16 result of magnitude 0.5 or more is allowed
+    2e-3 plus its own rounding (half a unit in the last place of the stored
+    value: 2^-9 at 0.5, 2^-8 at 1), which alone exceeds 2e-3 once |out| >= 1."""
     if dtype == "f32":
         return np.full(ref.shape, 1e-5)
     if dtype == "f16":
         return np.full(ref.shape, 2e-3)
     mag = np.maximum(np.abs(ref), 2.0 ** -126)
     half_ulp = 2.0 ** (np.floor(np.log2(mag)) - 8)
-    return 2e-3 + half_ulp
+    return np.where(np.abs(ref) < 0.5, 2e-3, 2e-3 + half_ulp)
 
 
-def compare(c: Case, got, ref=None, heads=None):
+def compare(c: Case, got, ref=None, heads=None, record=None):
+    """Element-wise check against the oracle; returns the largest |error|.
+    ``record`` names the case in the run's table of largest errors."""
     ref = oracle_out(c, heads=heads) if ref is None else ref
     g = got.detach().float().cpu().numpy().astype(np.float64)
     if heads is not None:
@@ -235,4 +238,18 @@ def compare(c: Case, got, ref=None, heads=None):
     bad = ~(err <= tol)
     assert not bad.any(), (f"max err {np.nanmax(err):.3e} at {np.unravel_index(np.nanargmax(err), err.shape)}, "
                            f"{int(bad.sum())} elements over tolerance")
-    return float(np.max(err)) if err.size else 0.0
+    worst = float(np.max(err)) if err.size else 0.0
+    if record is not None:
+        record_error(record, worst, c.wl.dtype, float(np.max(np.abs(ref))) if ref.size else 0.0)
+    return worst
+
+
+# Largest error per named case, written out at the end of the session (see
+# tests/conftest.py) so that a quiet run still leaves the achieved margins.
+ERRORS: dict = {}
+
+
+def record_error(name: str, err: float, dtype: str, max_abs_out: float | None = None) -> None:
+    prev = ERRORS.get(name)
+    if prev is None or err > prev["max_abs_err"]:
+        ERRORS[name] = {"max_abs_err": err, "dtype": dtype, "max_abs_out": max_abs_out}

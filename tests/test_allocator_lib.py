@@ -351,3 +351,27 @@ def test_batch_reservation_refuses_wrong_host_arrays():
         a.reserve_batch(tables.astype(np.int64), nblk, [0] * B, [1] * B)
     # nothing was reserved by the refused calls
     assert a.num_free() == 64 - B
+
+
+def test_blocks_alloc_takes_n_like_n_single_allocations():
+    # allocate_pages(n) of m.lqnn.cn/news/240480 §4.2: n blocks from the front
+    # of the queue, or nothing at all when fewer are free.
+    order = np.random.default_rng(3).permutation(20).astype(np.int32)
+    a = pkv.BlockAllocator(20, 16, order)
+    o = oa.OracleAllocator(20, 16, order.tolist())
+    got = a.alloc_n(7).tolist()
+    assert got == [o.alloc() for _ in range(7)] == order[:7].tolist()
+    a.release(got[2:5])
+    o.release(got[2:5], 3)
+    assert a.free_list() == o.free_list()
+    before = a.free_list()
+    with pytest.raises(pkv.OutOfBlocks):
+        a.alloc_n(17)
+    assert a.free_list() == before and a.num_free() == 16
+    got = a.alloc_n(16).tolist()
+    assert got == [o.alloc() for _ in range(16)]
+    assert a.alloc_n(0).tolist() == [] and a.num_free() == 0
+    for b in range(20):
+        assert a.refcount(b) == o.refcount(b) == 1
+    with pytest.raises(pkv.InvalidArgument):
+        a.alloc_n(-1)

@@ -109,7 +109,7 @@ def test_fused_full_7b_layer(kv):
     _poison_newest(c)
     out = _run_fused(c)
     _assert_pools(c)
-    pc.compare(c, out, ref)
+    pc.compare(c, out, ref, record=f"config 2 7B layer fused append ({kv} cache)")
 
 
 def test_fused_head_slices_and_batch_slices():

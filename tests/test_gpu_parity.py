@@ -38,7 +38,7 @@ def test_tiny_fp32():
     wl = workloads.tiny()
     c = pc.build(wl, DEV)
     _log(f"tiny: lens {wl.seq_lens.tolist()}")
-    err = pc.compare(c, pc.run_gpu(c))
+    err = pc.compare(c, pc.run_gpu(c), record="config 1 tiny f32")
     assert err < 1e-5
     # One token: the output is that token's value row (exactly, in fp32).
     out = pc.run_gpu(c)
@@ -83,10 +83,14 @@ def test_llama7b_layer_full_size():
     wl = workloads.llama7b_layer()
     _log(f"7B layer: batch {wl.batch}, sum len {int(wl.seq_lens.sum())}, pool {wl.num_blocks}")
     c = pc.build(wl, DEV)
-    err = pc.compare(c, pc.run_gpu(c))
+    err = pc.compare(c, pc.run_gpu(c), record="config 2 7B layer f16")
     _log(f"7B layer max err {err:.2e}")
-    assert sizes.fragmentation_tokens(wl.seq_lens, 16) == sum(
-        -(-int(x) // 16) * 16 - int(x) for x in wl.seq_lens)
+    # The slots the library's allocator holds beyond the tokens written are
+    # the fragmentation the oracle's closed form gives.
+    used = wl.num_blocks - c.palloc.num_free()
+    frag = sizes.fragmentation_tokens(wl.seq_lens, 16)
+    assert used * 16 - int(wl.seq_lens.sum()) == frag
+    pc.record_error("config 2 fragmentation tokens (not an error)", float(frag), "int")
 
 
 def test_prefix_cow_full_size():
@@ -99,7 +103,7 @@ def test_prefix_cow_full_size():
     assert used == 32 + sum(-(-int(x) // 16) - 32 for x in wl.seq_lens)
     ref = pc.oracle_out(c)
     got = pc.run_gpu(c).clone()
-    err = pc.compare(c, got, ref)
+    err = pc.compare(c, got, ref, record="config 3 prefix+CoW f16")
     _log(f"prefix+CoW max err {err:.2e}, unique/logical bytes "
          f"{sizes.unique_kv_bytes(c.tables_np, wl.seq_lens, 16, 32, 128, 2) / sizes.logical_kv_bytes(wl.seq_lens, 32, 128, 2):.3f}")
     # Sharing changes nothing: give every sequence private copies of the
@@ -126,8 +130,11 @@ def test_long13b_full_size(block_size):
     wl = workloads.long13b(block_size)
     assert sizes.fragmentation_tokens(wl.seq_lens, block_size) == 0
     c = pc.build(wl, DEV)
-    err = pc.compare(c, pc.run_gpu(c))
+    err = pc.compare(c, pc.run_gpu(c), record=f"config 4 13B long bf16 block {block_size}")
     _log(f"13B long bs {block_size} max err {err:.2e}")
+    # outputs here are averages over 4096 rows (|out| well below 0.5): the
+    # plain bound holds with no allowance for the output's own rounding
+    assert err <= 2e-3
 
 
 def test_physical_permutation_changes_nothing():
@@ -313,3 +320,29 @@ def test_metadata_in_pinned_host_memory():
     opool.copy_blocks([okp], [ovp], pairs)
     assert np.array_equal(pc.to_bits(kc), pc.storage_bits(okp))
     assert np.array_equal(pc.to_bits(vc), pc.storage_bits(ovp))
+
+
+def test_implicit_workspace_on_a_side_stream():
+    # A call enqueued on another stream with no workspace given: the binding
+    # allocates the workspace for that stream, so memory that work on the
+    # current stream allocates and fills meanwhile cannot be the workspace
+    # the delayed kernels still write.
+    wl = workloads.custom([700, 65, 1, 300, 1500], num_heads=32, head_dim=128, dtype="f16", block_size=16, seed=61)
+    c = pc.build(wl, DEV)
+    ref = pc.oracle_out(c)
+    need = pkv.pkv_decode_workspace_bytes(wl.batch, 32, 128, "f16")
+    side = torch.cuda.Stream()
+    a = torch.randn((4096, 4096), device=DEV, dtype=torch.float16)
+    for _ in range(3):
+        out = torch.full_like(c.q, float("nan"))
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for _ in range(20):          # keep the side stream busy before the decode call
+                a = (a @ a).clamp_(-1, 1)
+        pkv.pkv_attention_decode(out, c.q, c.k_cache, c.v_cache, c.tables, c.lens, wl.max_seq_len, scale=wl.scale,
+                                 stream=side)
+        junk = torch.empty(need, dtype=torch.uint8, device=DEV)
+        junk.fill_(0x7F)
+        torch.cuda.synchronize()
+        pc.compare(c, out, ref)
+        del junk
