@@ -6,30 +6,36 @@ One step = the whole decode path for one batch:
      place from pinned host memory, with no copy on the queue (``--metadata
      device`` stages them with one asynchronous copy per step instead),
   3. copy-on-write block copies (pkv_copy_blocks) when a reservation produced any,
-  4. scatter of the new K/V rows (pkv_append) and
-  5. decode attention over the paged cache (pkv_attention_decode); with
-     ``--fused`` both in one launch per layer (pkv_append_attention_decode),
-with 4-5 repeated per layer for multi-layer workloads.  Inputs are resident in
-HBM before timing; sequences grow by one token per step.
+  4. scatter of the new K/V rows and
+  5. decode attention over the paged cache, 4 and 5 in one launch per layer
+     (pkv_append_attention_decode; ``--separate``: pkv_append, then
+     pkv_attention_decode),
+with 4-5 repeated per layer.  Every layer has its own cache; the single-layer
+workloads read the caches of 4 layers in turn by default, so that no call
+finds the previous call's rows in the 256 MB Infinity Cache (a model's next
+decode of a layer comes 31 layers later).  Inputs are resident in HBM before
+timing; sequences grow by one token per step.
 
 Default workload: one layer of a 7B-shaped model (32 heads x 128, fp16, block
 16, batch 32, lengths uniform on [128, 2048], blocks scattered through a pool
 of 1.3x the blocks needed).  ``--workload full7b_step`` runs the 32-layer step
 (batch 256, lognormal lengths, 30 % sharing a 256-token prefix, pool = 85 % of
-free HBM); ``--workload long13b`` the 40-head bf16 4096-token case.
+free HBM); ``--workload long13b`` the 40-head bf16 4096-token case;
+``--workload tiny`` the 4-sequence fp32 case (launch-bound).
 
 ``--kv-dtype i8|fp8`` stores K/V as 8-bit codes plus one float32 scale per
-(token, head) (pkv_append_quant / pkv_attention_decode_quant); queries and
-outputs stay in the workload's dtype.
+(token, head); queries and outputs stay in the workload's dtype.
 
 Prints one JSON line.  ``value`` is KV GB/s over the whole timed step (K+V
 bytes attention reads / step time).  ``roofline`` reports the decode-attention
-call (decode kernel + merge kernel) timed with HIP events that the call itself
-records at its first kernel's start and its last kernel's end
-(pkv_time_next_decode), and
-the HBM traffic rocprofv3 counted for it when the recorded counters belong to
-the current kernel source.  ``cpu_baseline`` times the oracle on a bounded
-sample of the same workload on the host cores.
+call (decode kernel + merge kernel), each call of a separate pass timed with
+HIP events that the call itself records at its first kernel's start and its
+last kernel's end (pkv_time_next_decode), and the HBM traffic rocprofv3
+counted for the same call, as its ratio to the algorithmic bytes, when the
+recorded counters belong to the current kernel source.  ``cpu_baseline``
+times the oracle on a bounded sample of the same workload on the host cores.
+``host_side`` carries the host figures of the path: allocator ns per block,
+reservation us per step, fragmentation, the Tiny call's us and the host CPU.
 """
 
 from __future__ import annotations
@@ -64,15 +70,17 @@ def parse():
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="llama7b_layer",
-                   choices=["llama7b_layer", "prefix_cow", "long13b", "full7b_step"])
-    p.add_argument("--component", default="decode", choices=["decode", "prefix_cache", "swap"],
+                   choices=["tiny", "llama7b_layer", "prefix_cow", "long13b", "full7b_step"])
+    p.add_argument("--component", default="decode", choices=["decode", "prefix_cache", "swap", "allocator"],
                    help="decode: the decode step (default, the headline line); prefix_cache: host prefix-cache "
                         "operations on a shared-system-prompt request stream; swap: preemption swap of a "
-                        "request's blocks to pinned host memory and back")
+                        "request's blocks to pinned host memory and back; allocator: host block allocation and "
+                        "release, ns per block")
     p.add_argument("--block-size", type=int, default=16, help="block size of the long13b workload")
     p.add_argument("--layers", type=int, default=0,
-                   help="layers per step (0 = the workload's own); each layer has its own cache, so with the "
-                        "single-layer workloads N > 1 keeps one call's K rows from still being cached at the next")
+                   help="layers per step, each with its own cache read in turn (0 = the workload's default: 4 for "
+                        "the single-layer 7B and prefix workloads, so that no call finds the previous call's rows "
+                        "in the Infinity Cache; 1 for long13b and tiny; 32 for full7b_step)")
     p.add_argument("--work-groups", type=int, default=0, help="decode work-groups (0 = library choice)")
     p.add_argument("--ring", type=int, default=4, help="host staging buffers (how many steps the host may run ahead)")
     p.add_argument("--metadata", choices=["pinned", "device", "staged"], default="pinned",
@@ -81,15 +89,19 @@ def parse():
     p.add_argument("--kv-dtype", choices=["auto", "i8", "fp8"], default="auto",
                    help="K/V cache storage: the workload's dtype (auto) or an 8-bit format")
     p.add_argument("--scores", action="store_true",
-                   help="also update cumulative attention scores per cached token (16/32-bit caches)")
+                   help="also update cumulative attention scores per cached token (16/32-bit caches; two launches "
+                        "per layer)")
     p.add_argument("--grouped", action="store_true",
-                   help="decode with pkv_attention_decode_grouped: shared prefixes read once per tile of sequences")
-    p.add_argument("--fused", action="store_true",
-                   help="scatter and attend in one launch per layer (pkv_append_attention_decode)")
-    p.add_argument("--time-every", type=int, default=8,
-                   help="time the attention call on every N-th timed step (timing a call costs the step ~6 us)")
+                   help="decode with pkv_attention_decode_grouped: shared prefixes read once per tile of sequences "
+                        "(two launches per layer)")
+    p.add_argument("--separate", action="store_true",
+                   help="scatter and attend in two launches per layer (pkv_append, pkv_attention_decode) instead "
+                        "of one (pkv_append_attention_decode)")
+    p.add_argument("--timed-calls", type=int, default=64,
+                   help="decode calls timed one by one, in a pass after the wall-clock steps (at least 50)")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target length of the oracle timing sample")
     p.add_argument("--no-cpu", action="store_true", help="skip the cpu_baseline leg")
+    p.add_argument("--no-host-side", action="store_true", help="skip the host_side figures")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run a plain 1 GiB device-to-device copy (reference for HBM byte counters)")
     return p.parse_args()
@@ -103,17 +115,62 @@ def source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def recorded_traffic(workload: str):
-    """HBM bytes per decode-attention call from committed rocprofv3 counters, if still current."""
+def recorded_traffic(key: str):
+    """(counted / algorithmic bytes) of one decode-attention call from committed
+    rocprofv3 counters of the same call, if they belong to the current kernel
+    sources; else None."""
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    entry = rec.get(workload)
+    entry = rec.get(key)
     if not entry or entry.get("kernel_source_sha256_16") != source_hash():
         return None
-    return entry.get("bytes_per_call")
+    counted, algo = entry.get("counted_bytes_per_call"), entry.get("algorithmic_bytes_per_call")
+    if not counted or not algo:
+        return None
+    return counted / algo
+
+
+def host_info() -> dict:
+    """The host CPU as lscpu reports it, and the CPUs this process may use."""
+    info = {"logical_cpus": os.cpu_count()}
+    try:
+        info["usable_cpus"] = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        pass
+    try:
+        import subprocess
+
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        fields = dict(line.split(":", 1) for line in out.splitlines() if ":" in line)
+        for key, name in (("Model name", "cpu_model"), ("Socket(s)", "sockets"),
+                          ("Core(s) per socket", "cores_per_socket"), ("Thread(s) per core", "threads_per_core")):
+            if key in fields:
+                v = fields[key].strip()
+                info[name] = int(v) if v.isdigit() else v
+    except (OSError, ValueError):
+        pass
+    if "cpu_model" not in info:
+        try:
+            with open("/proc/cpuinfo") as f:
+                for line in f:
+                    if line.startswith("model name"):
+                        info["cpu_model"] = line.split(":", 1)[1].strip()
+                        break
+        except OSError:
+            pass
+    return info
+
+
+def blas_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+
+        return max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # no threadpoolctl: numpy's BLAS threads unknown, report one
+        return 1
 
 
 def cpu_baseline(wl, sample_rows, target_s, kv):
@@ -121,12 +178,7 @@ def cpu_baseline(wl, sample_rows, target_s, kv):
     from oracle import attention as oatt
     from oracle import quant as oquant
 
-    try:
-        from threadpoolctl import threadpool_info
-
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:  # no threadpoolctl: numpy's BLAS threads unknown, report one
-        cores = 1
+    cores = blas_threads()
     h, d = wl.num_heads, wl.head_dim
     order = np.random.default_rng(99).permutation(wl.batch)
     done_bytes, spent, seqs, tokens = 0, 0.0, 0, 0
@@ -153,7 +205,139 @@ def cpu_baseline(wl, sample_rows, target_s, kv):
         tokens += L
     return {"value": round(done_bytes / spent / 1e9, 4), "unit": "GB/s", "cores": int(cores), "kind": "oracle",
             "sample": f"numpy float64 oracle, {seqs} sequence decodes of this workload ({tokens} tokens x {h} heads, "
-                      f"one layer), {spent:.1f} s of oracle time"}
+                      f"one layer), {spent:.1f} s of oracle time",
+            "host": host_info()}
+
+
+# The pages' allocation latencies (context, not targets: other systems,
+# hardware unstated).
+PAGE_ALLOC_FIGURES = [
+    "fixed-size page pool: 0.18 ms -> 0.003 ms per allocation once the free list replaces a scan "
+    "(m.lqnn.cn/news/240480 §5.2 tip 1)",
+    "variable-size pool: 15 ms -> 0.5 ms per allocation (l189.com/news/1438543 §2.3)",
+]
+
+
+def allocator_figures(n_blocks: int = 4096, seconds: float = 0.5) -> dict:
+    """ns per block of one allocation plus one release: the library (a batch of
+    n_blocks taken by pkv_blocks_alloc and returned by pkv_seq_release, so
+    that the Python call costs nothing per block) and the oracle allocator
+    (one Python call per block)."""
+    import paged_attention_amd as pkv
+    from oracle import allocator as oalloc
+
+    order = np.random.default_rng(13).permutation(n_blocks).astype(np.int32)
+    a = pkv.BlockAllocator(n_blocks, 16, order)
+    ids = np.zeros(n_blocks, dtype=np.int32)
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        a.alloc_n(n_blocks, ids)
+        a.release(ids)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el > seconds:
+            break
+    lib_ns = el / (reps * n_blocks) * 1e9
+    o = oalloc.OracleAllocator(n_blocks, 16, order.tolist())
+    oreps, t0 = 0, time.perf_counter()
+    while True:
+        got = [o.alloc() for _ in range(n_blocks)]
+        for b in got:
+            o.decref(b)
+        oreps += 1
+        oel = time.perf_counter() - t0
+        if oel > seconds:
+            break
+    return {"library_ns_per_block": round(lib_ns, 2), "oracle_ns_per_block": round(oel / (oreps * n_blocks) * 1e9, 1),
+            "what": f"one allocation + one release per block, pool of {n_blocks} blocks (library: batches of "
+                    f"{n_blocks} through pkv_blocks_alloc / pkv_seq_release; oracle: Python calls)",
+            "pages": PAGE_ALLOC_FIGURES}
+
+
+def full7b_reservation(num_blocks: int, steps: int = 100) -> dict:
+    """Host reservation of the full 7B step (256 sequences, one token each)
+    after its history is in place, us per step; and its fragmentation."""
+    import paged_attention_amd as pkv
+    import workloads
+    from oracle import sizes
+
+    wl = workloads.full7b_step(num_blocks)
+    B, bs = wl.batch, wl.block_size
+    lens = wl.seq_lens.astype(np.int64)
+    maxb = -(-(int(lens.max()) + steps) // bs) + 1
+    alloc = pkv.BlockAllocator(wl.num_blocks, bs, wl.free_order)
+    tables = np.zeros((B, maxb), dtype=np.int32)
+    nblk = np.zeros(B, dtype=np.int32)
+    done = np.zeros(B, dtype=np.int64)
+    sharers = [int(x) for x in wl.sharers]
+    s0 = sharers[0]
+    alloc.reserve_batch(tables[s0:s0 + 1], nblk[s0:s0 + 1], [0], [wl.prefix_len])
+    done[s0] = wl.prefix_len
+    for x in sharers[1:]:
+        row = alloc.fork(tables[s0, : nblk[s0]])
+        tables[x, : len(row)] = row
+        nblk[x] = len(row)
+        done[x] = wl.prefix_len
+    alloc.reserve_batch(tables, nblk, done, lens - 1 - done)
+    cur = (lens - 1).astype(np.int32)
+    ones = np.ones(B, dtype=np.int32)
+    slots = np.zeros(B, dtype=np.int64)
+    pairs = np.zeros((B, 2), dtype=np.int32)
+    frag = sizes.fragmentation_tokens(lens, bs)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        alloc.reserve_batch_into(tables, nblk, cur, ones, slots, pairs)
+        cur += 1
+    el = time.perf_counter() - t0
+    return {"us_per_step": round(el / steps * 1e6, 2), "sequences": B, "pool_blocks": int(wl.num_blocks),
+            "fragmentation_tokens": int(frag), "fragmentation_of_tokens": round(frag / int(lens.sum()), 5)}
+
+
+def tiny_call_us(dev, calls: int = 200) -> dict:
+    """The Tiny workload's decode call (4 sequences, 4 heads x 64, fp32): us
+    per call from its kernel timestamps, and back to back on the stream."""
+    import torch
+
+    import paged_attention_amd as pkv
+    import workloads
+
+    wl = workloads.tiny()
+    bs, H, D = wl.block_size, wl.num_heads, wl.head_dim
+    vals = wl.draw_values()
+    alloc = pkv.BlockAllocator(wl.num_blocks, bs, wl.free_order)
+    tables = np.zeros((wl.batch, wl.max_blocks_per_seq()), dtype=np.int32)
+    nblk = np.zeros(wl.batch, dtype=np.int32)
+    lens = wl.seq_lens.astype(np.int32)
+    slots, _ = alloc.reserve_batch(tables, nblk, np.zeros(wl.batch), lens)
+    kc = torch.zeros((wl.num_blocks, bs, H, D), dtype=torch.float32, device=dev)
+    vc = torch.zeros_like(kc)
+    pkv.pkv_append(torch.from_numpy(np.concatenate(vals["k_seq"])).to(dev),
+                   torch.from_numpy(np.concatenate(vals["v_seq"])).to(dev), torch.from_numpy(slots).to(dev), kc, vc)
+    q = torch.from_numpy(vals["q"]).to(dev)
+    out = torch.empty_like(q)
+    call = pkv.PreparedDecode(out, q, kc, vc, torch.from_numpy(tables).to(dev), torch.from_numpy(lens).to(dev),
+                              int(lens.max()), scale=wl.scale)
+    stream = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(calls)]
+    for e0, e1 in evs:
+        e0.record(stream)
+        e1.record(stream)
+    for _ in range(20):
+        call.launch()
+    torch.cuda.synchronize()
+    for e0, e1 in evs:
+        pkv.pkv_time_next_decode(e0, e1)
+        call.launch()
+    torch.cuda.synchronize()
+    kern = np.array([e0.elapsed_time(e1) * 1e3 for e0, e1 in evs])
+    t0 = time.perf_counter()
+    for _ in range(calls):
+        call.launch()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / calls * 1e6
+    return {"call_us_p50": round(float(np.median(kern)), 2), "call_us_p10": round(float(np.percentile(kern, 10)), 2),
+            "call_us_p90": round(float(np.percentile(kern, 90)), 2), "back_to_back_us_per_call": round(wall, 2),
+            "workload": wl.title, "bound": "launch latency (no roofline claim)"}
 
 
 def run_prefix_cache(args):
@@ -306,6 +490,24 @@ def run_swap(args):
     print(json.dumps(rec), flush=True)
 
 
+def run_allocator(args):
+    """Host block allocation and release, ns per block, beside the oracle's
+    and the pages' figures (no GPU)."""
+    fig = allocator_figures(seconds=2.0)
+    rec = {
+        "metric": "host block allocation + release, ns per block",
+        "value": fig["library_ns_per_block"], "unit": "ns/block", "n_gpus": 0, "steps": 0, "warmup": 0,
+        "ms_per_step": None, "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
+        "dtype": "int32 block ids", "data": "synthetic (seeded free-list order)",
+        "config": {"workload": fig["what"]},
+        "cpu_baseline": {"value": fig["oracle_ns_per_block"], "unit": "ns/block", "cores": 1, "kind": "oracle",
+                         "sample": "the oracle allocator (Python deque and list) on the same operations",
+                         "host": host_info()},
+        "pages": fig["pages"],
+    }
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -318,38 +520,57 @@ def main():
     if args.component == "swap":
         run_swap(args)
         return
+    if args.component == "allocator":
+        run_allocator(args)
+        return
     import torch
 
     import paged_attention_amd as pkv
     import workloads
+    from oracle import sizes
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    total_steps = args.warmup + args.steps
-    if args.workload == "llama7b_layer":
+    full7b_blocks = None
+    if args.workload == "tiny":
+        wl = workloads.tiny()
+    elif args.workload == "llama7b_layer":
         wl = workloads.llama7b_layer()
     elif args.workload == "long13b":
         wl = workloads.long13b(args.block_size)
     elif args.workload == "prefix_cow":
         wl = workloads.prefix_cow()
-    else:
+    if args.workload == "full7b_step" or not args.no_host_side:
         # 32 layers; the pool takes 85 % of the free device memory.
         free, _ = torch.cuda.mem_get_info()
         per_block = 32 * 2 * 16 * 32 * 128 * 2
-        wl = workloads.full7b_step(int(0.85 * free) // per_block)
-    if args.layers > 0:
-        wl = dataclasses.replace(wl, num_layers=args.layers, title=f"{wl.title}; {args.layers} layers")
+        full7b_blocks = int(0.85 * free) // per_block
+    if args.workload == "full7b_step":
+        wl = workloads.full7b_step(full7b_blocks)
+    layers = args.layers or {"llama7b_layer": 4, "prefix_cow": 4}.get(args.workload, wl.num_layers)
+    if layers != wl.num_layers:
+        wl = dataclasses.replace(wl, num_layers=layers,
+                                 title=f"{wl.title}; the caches of {layers} layers read in turn")
     B, H, D, bs, NL = wl.batch, wl.num_heads, wl.head_dim, wl.block_size, wl.num_layers
     tdt = {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32}[wl.dtype]
     esz = wl.dtype_bytes
     kv = "dense" if args.kv_dtype == "auto" else args.kv_dtype
+    if args.scores and kv != "dense":
+        print("--scores runs with a 16/32-bit cache", file=sys.stderr)
+        sys.exit(2)
+    if args.grouped and (kv != "dense" or args.scores or wl.dtype not in ("f16", "bf16")):
+        print("--grouped runs with an fp16/bf16 cache and no scores", file=sys.stderr)
+        sys.exit(2)
+    fused = not (args.separate or args.scores or args.grouped)
+    timed_steps = -(-max(50, args.timed_calls) // NL)
+    total_steps = args.warmup + args.steps + timed_steps
     # K/V bytes one token adds to one layer's cache (codes and scales for 8-bit)
     tok_bytes = 2 * H * D * esz if kv == "dense" else 2 * H * (D + 4)
     lens0 = wl.seq_lens.astype(np.int64)
     max_len = int(lens0.max()) + total_steps
     maxb = -(-max_len // bs)
-    print(f"[bench] {wl.title}; pool {wl.num_blocks} blocks; steps {args.steps} warmup {args.warmup}",
-          file=sys.stderr, flush=True)
+    print(f"[bench] {wl.title}; pool {wl.num_blocks} blocks; steps {args.steps} warmup {args.warmup} "
+          f"+ {timed_steps} timed", file=sys.stderr, flush=True)
 
     # --- set-up (not timed): allocator, pools, history ---------------------
     alloc = pkv.BlockAllocator(wl.num_blocks, bs, wl.free_order)
@@ -411,18 +632,18 @@ def main():
         k_caches.append(kc)
         v_caches.append(vc)
     del slots_hist
+    # Queries and new rows: a few steps' worth, used in turn (their values do
+    # not change the work).
+    nq = min(total_steps, 8)
     gen.manual_seed(7)
-    q_all = torch.randn((total_steps, NL, B, H, D), generator=gen, device=dev, dtype=torch.float32).to(tdt)
-    k_new = torch.randn((total_steps, NL, B, H, D), generator=gen, device=dev, dtype=torch.float32).to(tdt)
-    v_new = torch.randn((total_steps, NL, B, H, D), generator=gen, device=dev, dtype=torch.float32).to(tdt)
+    q_all = torch.randn((nq, NL, B, H, D), generator=gen, device=dev, dtype=torch.float32).to(tdt)
+    k_new = torch.randn((nq, NL, B, H, D), generator=gen, device=dev, dtype=torch.float32).to(tdt)
+    v_new = torch.randn((nq, NL, B, H, D), generator=gen, device=dev, dtype=torch.float32).to(tdt)
     out = torch.empty((B, H, D), dtype=tdt, device=dev)
     wgs = args.work_groups or pkv.pkv_decode_work_groups(wl.dtype if kv == "dense" else kv)
     workspace = pkv.decode_workspace(B, H, D, wl.dtype if kv == "dense" else kv, wgs, device=dev)
     prefix = None
     if args.grouped:
-        if kv != "dense" or args.fused or args.scores or wl.dtype not in ("f16", "bf16"):
-            print("--grouped runs with an fp16/bf16 cache, separate launches and no scores", file=sys.stderr)
-            sys.exit(2)
         # Groups from the tables and the first step's lengths.  New tokens land
         # in private blocks, so the shared prefixes (capped by each length) stay
         # valid for every later step.
@@ -473,10 +694,6 @@ def main():
         metas = [split(hm) for hm in h_meta]
     per_slot = {}
     score_bufs = []
-    if args.scores and (kv != "dense" or args.fused):
-        print("--scores runs with a 16/32-bit cache and separate launches", file=sys.stderr)
-        sys.exit(2)
-    fused = args.fused
     for r in range(ring):
         key = metas[r][0].data_ptr()
         if key not in per_slot:
@@ -518,34 +735,22 @@ def main():
     torch.cuda.synchronize()
 
     ones = np.ones(B, dtype=np.int32)
-    # The decode call's own first-kernel start and last-kernel end
-    # (pkv_time_next_decode): an event recorded between the append and the
-    # decode kernel would delay the decode kernel's start by about 4 us and
-    # count that delay as attention time.  Timing a call still costs its step
-    # about 6 us of queue time, so only every time_every-th timed step is
-    # timed (all layers of it).  Each event is recorded once here so that its
-    # HIP event exists.
-    every = max(1, args.time_every)
-    timed = [i for i in range(args.warmup, total_steps) if (i - args.warmup) % every == 0]
-    ev = {i: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(NL)]
-          for i in timed}
-    for pairs in ev.values():
-        for e0, e1 in pairs:
-            e0.record(stream)
-            e1.record(stream)
     released = [torch.cuda.Event() for _ in range(ring)]
-    kv_bytes, table_entries, n_pairs = [], [], [0]
+    kv_bytes, table_entries, n_pairs, host_s = [], [], [0], []
 
-    def step(i):
+    def step(i, timing=None):
         r = i % ring
+        j = i % nq
         if h_done[r] is not None:                                      # ring slot r free again:
             while not h_done[r].query():                               # poll; a blocking wait sleeps and
                 pass                                                   # wakes up late
         slots_v, lens_v, tab_v = h_views[r]
+        t_host = time.perf_counter()
         npairs = alloc.reserve_batch_into(tables, nblk, cur, ones, slots_v, h_pairs[r].numpy())  # 1. reserve
         cur[:] += 1
         lens_v[:] = cur
         tab_v[:] = tables
+        host_s.append(time.perf_counter() - t_host)
         if d_meta is not None:
             d_meta.copy_(h_meta[r], non_blocking=True)                 # 2. stage metadata (one copy)
         if d_slots is not None:                                        # 2. stage on the copy stream
@@ -566,14 +771,14 @@ def main():
         appends, decodes = calls[r]
         for layer in range(NL):
             if fused:                                                  # 4 + 5 in one launch
-                if i in ev:
-                    pkv.pkv_time_next_decode(*ev[i][layer])
-                decodes[layer].launch(q_all[i, layer], k_new[i, layer], v_new[i, layer])
+                if timing is not None:
+                    pkv.pkv_time_next_decode(*timing[layer])
+                decodes[layer].launch(q_all[j, layer], k_new[j, layer], v_new[j, layer])
             else:
-                appends[layer].launch(k_new[i, layer], v_new[i, layer])    # 4. scatter new rows
-                if i in ev:
-                    pkv.pkv_time_next_decode(*ev[i][layer])
-                decodes[layer].launch(q_all[i, layer])                     # 5. decode attention
+                appends[layer].launch(k_new[j, layer], v_new[j, layer])    # 4. scatter new rows
+                if timing is not None:
+                    pkv.pkv_time_next_decode(*timing[layer])
+                decodes[layer].launch(q_all[j, layer])                     # 5. decode attention
         if d_meta is None:                                             # read (in place, or the device
             released[r].record(stream)                                 # slot) until here; the copy-on-
         if d_slots is not None:                                        # write pairs too
@@ -587,37 +792,56 @@ def main():
     torch.cuda.synchronize()
     kv_bytes.clear()
     table_entries.clear()
+    host_s.clear()
     t0 = time.perf_counter()
-    for i in range(args.warmup, total_steps):
+    for i in range(args.warmup, args.warmup + args.steps):
         step(i)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-
-    call_ms = np.array([ev[i][layer][0].elapsed_time(ev[i][layer][1]) for i in timed for layer in range(NL)])
-    attn_s = float(np.mean(call_ms)) / 1e3
-    call_pct = {f"p{q}": round(float(np.percentile(call_ms, q)) * 1e3, 2) for q in (10, 50, 90)}
     kv_total = float(sum(kv_bytes))
+    host_us = float(np.mean(host_s)) * 1e6
+    frag_tokens = int(sizes.fragmentation_tokens(cur, bs))
+    n_wall = len(kv_bytes)
+
+    # A separate pass: every decode call timed by its own kernel timestamps
+    # (timing a call costs its step queue time, so the wall-clock steps above
+    # carry none).  Each event is recorded once first so that its HIP event
+    # exists.
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(NL)]
+          for _ in range(timed_steps)]
+    for pairs in ev:
+        for e0, e1 in pairs:
+            e0.record(stream)
+            e1.record(stream)
+    torch.cuda.synchronize()
+    first_timed = args.warmup + args.steps
+    for k in range(timed_steps):
+        step(first_timed + k, ev[k])
+    torch.cuda.synchronize()
+    call_us = np.array([e0.elapsed_time(e1) * 1e3 for pairs in ev for e0, e1 in pairs])
+    attn_s = float(np.mean(call_us)) / 1e6
+    call_pct = {f"p{q}": round(float(np.percentile(call_us, q)), 2) for q in (10, 50, 90)}
+
     value = kv_total / elapsed / 1e9
-    unique_total = kv_total - shared_extra_tokens * tok_bytes * NL * len(kv_bytes)
+    unique_total = kv_total - shared_extra_tokens * tok_bytes * NL * n_wall
     unique_gbs = unique_total / elapsed / 1e9
-    # Algorithmic bytes of one decode-attention call (mean over the steps whose
-    # calls were timed, one layer): K+V rows read (8-bit: codes and scales) +
-    # q in + out + block-table entries + lengths.
-    sampled = [i - args.warmup for i in timed]
-    kv_per_call = float(np.mean([kv_bytes[s] for s in sampled])) / NL
-    # With shared blocks only the unique bytes must leave HBM (the rest are
-    # cache hits), so the roofline counts unique K/V bytes.
+    # Algorithmic bytes of one decode-attention call (mean over the timed
+    # pass, one layer): K+V rows read (8-bit: codes and scales) + q in + out
+    # + block-table entries + lengths.  With shared blocks only the unique
+    # bytes must leave HBM (the rest are cache hits), so the roofline counts
+    # unique K/V bytes.
+    kv_per_call = float(np.mean(kv_bytes[n_wall:])) / NL
     unique_kv_per_call = kv_per_call - shared_extra_tokens * tok_bytes
-    algo = unique_kv_per_call + 2 * B * H * D * esz + 4 * float(np.mean([table_entries[s] for s in sampled])) + 4 * B
+    algo = unique_kv_per_call + 2 * B * H * D * esz + 4 * float(np.mean(table_entries[n_wall:])) + 4 * B
     if fused:   # the launch also reads the new rows and writes them (8-bit: codes and scales) into the pools
         algo += 2 * B * H * D * esz + B * tok_bytes
     achieved = algo / attn_s / 1e9
-    # one record per distinct call (format, fused append, scores, grouping, layer rotation)
-    traffic = recorded_traffic(args.workload + (f"/bs{args.block_size}" if args.workload == "long13b"
-                                                and args.block_size != 16 else "")
-                               + ("" if kv == "dense" else f"/{kv}") + ("/fused" if fused else "")
-                               + ("/scores" if args.scores else "") + ("/grouped" if prefix is not None else "")
-                               + (f"/layers{args.layers}" if args.layers > 0 else ""))
+    # one record per distinct call (workload, format, launches, scores, grouping)
+    key = (args.workload + (f"/bs{args.block_size}" if args.workload == "long13b" and args.block_size != 16 else "")
+           + ("" if kv == "dense" else f"/{kv}") + ("/fused" if fused else "") + ("/scores" if args.scores else "")
+           + ("/grouped" if prefix is not None else ""))
+    ratio = recorded_traffic(key)
+    traffic = None if ratio is None else int(round(ratio * algo))
 
     extra = {}
     if args.copy_calibration:
@@ -626,6 +850,18 @@ def main():
         bcopy.copy_(a)
         torch.cuda.synchronize()
         extra["copy_calibration_bytes"] = 1 << 30
+
+    host_side = None
+    if not args.no_host_side:
+        host_side = {
+            "reservation_us_per_step": {"this workload": round(host_us, 2),
+                                        "full 7B step (256 sequences)": full7b_reservation(full7b_blocks)},
+            "fragmentation_tokens": {"this workload": frag_tokens,
+                                     "this workload, fraction of tokens": round(frag_tokens / int(cur.sum()), 5)},
+            "allocator": allocator_figures(),
+            "tiny_decode_call": tiny_call_us(dev),
+            "host": host_info(),
+        }
 
     cpu = None
     if not args.no_cpu:
@@ -636,7 +872,7 @@ def main():
             idx = np.arange(L)
             blocks = tables[b, idx // bs].astype(np.int64)
             flat = torch.from_numpy(blocks * bs + idx % bs).to(dev)
-            qq = q_all[total_steps - 1, 0, b].cpu()
+            qq = q_all[(total_steps - 1) % nq, 0, b].cpu()
             if tdt == torch.bfloat16:
                 qq = qq.view(torch.int16).numpy().view(np.uint16)
             else:
@@ -654,6 +890,11 @@ def main():
         cpu = cpu_baseline(wl, rows, args.cpu_seconds, kv)
 
     ms_per_step = elapsed / args.steps * 1e3
+    call_name = ("pkv_attention_decode_grouped (prefix_kernel + decode_kernel + decode_merge_kernel)"
+                 if prefix is not None else
+                 "pkv_attention_decode_scores (decode_kernel + merge_score_kernel)" if args.scores else
+                 ("pkv_append_attention_decode" if fused else "pkv_attention_decode")
+                 + ("_quant" if kv != "dense" else "") + " (decode_kernel + decode_merge_kernel)")
     rec = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -668,27 +909,29 @@ def main():
         "dtype": wl.dtype if kv == "dense" else {"i8": "i8", "fp8": "fp8_e4m3"}[kv],
         "data": "synthetic (seeded; Q/K/V ~ N(0,1) cast to the storage dtype)",
         "config": {"workload": wl.title + ("" if kv == "dense" else f"; K/V cache {kv} + f32 scale per (token, head)"),
-                   "kv_cache": wl.dtype if kv == "dense" else kv, "q_dtype": wl.dtype, "layers": NL, "batch": B, "heads": H, "head_dim": D, "block_size": bs,
-                   "pool_blocks": wl.num_blocks, "work_groups": wgs, "metadata": mode,
-                   "launches_per_layer": 1 if fused else 2, "cumulative_scores": bool(args.scores),
+                   "kv_cache": wl.dtype if kv == "dense" else kv, "q_dtype": wl.dtype, "layers": NL, "batch": B,
+                   "heads": H, "head_dim": D, "block_size": bs, "pool_blocks": wl.num_blocks, "work_groups": wgs,
+                   "metadata": mode, "launches_per_layer": 1 if fused else 2,
+                   "cumulative_scores": bool(args.scores),
                    "grouped_prefix_tiles": None if prefix is None else int(prefix[1].shape[0]),
-                   "mean_seq_len": round(kv_per_call / tok_bytes / B, 1), "cow_pairs": n_pairs[0]},
+                   "mean_seq_len": round(float(np.mean(kv_bytes[:n_wall])) / NL / tok_bytes / B, 1),
+                   "cow_pairs": n_pairs[0]},
         "hbm_peak_frac": round(unique_gbs / HBM_PEAK_GBS, 4),
         "unique_kv_gbs": round(unique_gbs, 2),
         "token_steps_per_s": round(B * args.steps / elapsed, 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "kernel": ("pkv_attention_decode_grouped (prefix_kernel + decode_kernel + decode_merge_kernel)"
-                                if prefix is not None else
-                                "pkv_attention_decode_scores (decode_kernel + merge_score_kernel)"
-                                if args.scores else
-                                ("pkv_append_attention_decode" if fused else "pkv_attention_decode")
-                                + ("_quant" if kv != "dense" else "") + " (decode_kernel + decode_merge_kernel)"),
+                     "traffic_ratio": None if ratio is None else round(ratio, 4),
+                     "kernel": call_name,
                      "avg_call_us": round(attn_s * 1e6, 2), "call_us_percentiles": call_pct,
                      "algorithmic_bytes_per_call": int(algo),
-                     "logical_kv_bytes_per_call": int(kv_per_call), "timed_calls": len(timed) * NL,
-                     "timing": "kernel timestamps of the call's first and last kernel, every "
-                               f"{every}-th timed step"},
+                     "logical_kv_bytes_per_call": int(kv_per_call), "timed_calls": int(call_us.size),
+                     "timing": f"kernel timestamps of each call's first and last kernel, {call_us.size} calls "
+                               f"({timed_steps} steps x {NL} layers) in a pass after the wall-clock steps",
+                     "traffic_source": "rocprofv3 FETCH_SIZE + WRITE_SIZE of the same call, as a ratio to its "
+                                       "algorithmic bytes (profiles/decode_traffic.json), times this run's "
+                                       "algorithmic bytes"},
+        "host_side": host_side,
         "cpu_baseline": cpu,
     }
     rec.update(extra)

@@ -306,7 +306,7 @@ PKV_API int32_t pkv_decode_work_groups(pkv_dtype cache_dtype);
  * automatic count for that cache type).  `dtype` is the cache element type:
  * F32/F16/BF16 for pkv_attention_decode, I8/FP8_E4M3 for
  * pkv_attention_decode_quant.  It holds a per-sequence plan (2 int32 per sequence and head
- * slice, at most 8190 per launch) and float32 partial softmax states for
+ * slice, at most 5460 per launch) and float32 partial softmax states for
  * 2 * num_work_groups pieces of num_heads * (head_dim + 2) floats, each
  * region 256-byte aligned.  It does not depend on sequence lengths.
  * Returns 0 for an invalid shape. */

@@ -204,7 +204,7 @@ __device__ __forceinline__ float wave_sum(float x) {
 // small merge kernel combines the pieces.  Cut points depend only on logical
 // positions, so the result does not depend on where blocks sit physically.
 
-constexpr int kMaxVirtual = 8190;   // sequences x head slices per launch (two LDS prefix arrays <= 64 KiB)
+constexpr int kMaxVirtual = 5460;   // sequences x head slices per launch (the LDS arrays: 3 x (5460 + 1) int32 <= 64 KiB)
 constexpr int kTableWindow = 64;    // block ids held in registers at a time (one per lane)
 constexpr int kMergeWaves = 4;      // heads per merge work-group
 
@@ -393,13 +393,16 @@ __global__ void __launch_bounds__(KV::kMaxWaves * 64) decode_kernel(DecodeArgs a
   const int nv = a.batch * a.groups_y;
   int32_t* s_pref = s_dyn;           // [nv + 1]: first chunk of each virtual sequence
   int32_t* s_part = s_dyn + nv + 1;  // [nv + 1]: first partial slot of each virtual sequence
+  int32_t* s_len = s_part + nv + 1;  // [batch]: the lengths, read once (they may be host memory)
   const int g = blockIdx.x;
 
   // 1. chunk counts of every (head slice, sequence); bad lengths count zero.
+  for (int b = threadIdx.x; b < a.batch; b += blockDim.x) s_len[b] = a.lens[b];
+  __syncthreads();
   block_exclusive_scan(
       [&](int v) {
         const int b = v % a.batch;
-        const int L = a.lens[b];
+        const int L = s_len[b];
         return length_ok<BS>(L, a) ? (L - suffix_start<BS, KV::kGrouped>(b, L, a) + kChunk - 1) / kChunk : 0;
       },
       nv, s_pref, s_waves);
@@ -435,7 +438,7 @@ __global__ void __launch_bounds__(KV::kMaxWaves * 64) decode_kernel(DecodeArgs a
     const int b = v % a.batch, y = v / a.batch;
     const int h = (y * a.waves_per_group + wave) * HPW + r;
     if ((y * a.waves_per_group + wave) * HPW >= a.num_heads || h >= a.num_heads) continue;
-    const float fill = a.lens[b] == 0 ? 0.f : __builtin_nanf("");
+    const float fill = s_len[b] == 0 ? 0.f : __builtin_nanf("");
     float f[EPL];
 #pragma unroll
     for (int e = 0; e < EPL; ++e) f[e] = fill;
@@ -472,7 +475,7 @@ __global__ void __launch_bounds__(KV::kMaxWaves * 64) decode_kernel(DecodeArgs a
       const int e0 = hl * D + c * EPL;                // this lane's first element of the row
       const Elem* kp = static_cast<const Elem*>(a.k) + e0 * KB;
       const Elem* vp = static_cast<const Elem*>(a.v) + e0 * KB;
-      const int L = a.lens[b];
+      const int L = s_len[b];
       const int start = suffix_start<BS, KV::kGrouped>(b, L, a);
       const int t_begin = start + static_cast<int>(cur - seq0) * kChunk;
       const int t_end = min(L, start + static_cast<int>(seg_end - seq0) * kChunk);
@@ -866,7 +869,7 @@ inline Layout workspace_layout(int32_t batch, int32_t num_heads, int32_t head_di
 // packets).
 template <class KV, int D, int BS, int MODE>
 void launch_decode(const DecodeArgs& a, int wg, hipStream_t stream, const pkv::CallEvents& tm) {
-  const size_t lds = 2 * (static_cast<size_t>(a.batch) * a.groups_y + 1) * sizeof(int32_t);
+  const size_t lds = (2 * (static_cast<size_t>(a.batch) * a.groups_y + 1) + a.batch) * sizeof(int32_t);
   const bool scores = MODE == kScores && a.max_seq_len > 0;
   hipExtLaunchKernelGGL((decode_kernel<KV, D, BS, MODE>), dim3(wg), dim3(a.waves_per_group * 64), lds, stream,
                         tm.start, nullptr, 0, a);

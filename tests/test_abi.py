@@ -174,9 +174,9 @@ def test_workspace_queries():
     # 160 heads at fp16 x 128: 40 wavefronts -> 3 head slices of <= 16 wavefronts
     want = up(b * 3 * 8) + up(2 * wg * 160 * d * 4) + up(2 * wg * 160 * 8)
     assert pkv.pkv_decode_workspace_bytes(b, 160, d, "bf16", wg) == want
-    # The plan holds at most one launch's worth of sequences (8190 per head slice).
+    # The plan holds at most one launch's worth of sequences (5460 per head slice).
     big = pkv.pkv_decode_workspace_bytes(20000, 4, 64, "f32", 8)
-    assert big == up(8190 * 8) + up(2 * 8 * 4 * 64 * 4) + up(2 * 8 * 4 * 8)
+    assert big == up(5460 * 8) + up(2 * 8 * 4 * 64 * 4) + up(2 * 8 * 4 * 8)
     assert pkv.pkv_decode_workspace_bytes(b, h, 96, "f16", wg) == 0
     # 8-bit caches: 16 elements per lane -> 8 heads per wavefront at 128, at
     # most 8 wavefronts per work-group.

@@ -15,7 +15,7 @@ def _bench(*args, timeout=300):
 
 
 def test_more_than_one_gpu_is_refused_for_every_component():
-    for extra in ([], ["--component", "swap"], ["--component", "prefix_cache"]):
+    for extra in ([], ["--component", "swap"], ["--component", "prefix_cache"], ["--component", "allocator"]):
         r = _bench("--gpus", "2", *extra)
         assert r.returncode == 2, (extra, r.stdout, r.stderr)
         assert "measures one GPU" in r.stderr
@@ -34,3 +34,14 @@ def test_prefix_cache_component_prints_one_json_line():
     assert rec["value"] > 0 and rec["higher_is_better"] is True and "workload" in rec["config"]
     # every request but the first finds the shared prompt's full blocks cached
     assert 0.5 < rec["prefill_tokens_saved_frac"] < 1.0
+
+
+def test_allocator_component_prints_one_json_line():
+    r = _bench("--component", "allocator")
+    assert r.returncode == 0, r.stderr
+    lines = [ln for ln in r.stdout.splitlines() if ln.startswith("{")]
+    assert len(lines) == 1
+    rec = json.loads(lines[0])
+    assert rec["unit"] == "ns/block" and rec["value"] > 0 and rec["higher_is_better"] is False
+    assert rec["cpu_baseline"]["kind"] == "oracle" and rec["cpu_baseline"]["value"] > rec["value"]
+    assert "cpu_model" in rec["cpu_baseline"]["host"] and len(rec["pages"]) == 2
