@@ -350,6 +350,29 @@ PKV_API int pkv_attention_decode(void* out, const void* q, const void* k_cache, 
                                  int32_t num_work_groups, void* workspace, size_t workspace_bytes,
                                  hipStream_t stream);
 
+/* Size of the device scratch array pkv_attention_decode_scratch uses on each
+ * device (32 MiB). */
+#define PKV_DECODE_SCRATCH_BYTES ((size_t)32 << 20)
+
+/* pkv_attention_decode for callers that cannot allocate device memory (code
+ * captured into a HIP graph, tight serving loops, harnesses that forbid
+ * hipMalloc): the workspace is a 32 MiB array the library holds on each
+ * device, so the call takes no workspace argument and allocates nothing.
+ * Every argument and result is that of pkv_attention_decode (same kernels,
+ * same work split: bit-identical output for the same num_work_groups).
+ * Sizes whose workspace (pkv_decode_workspace_bytes) would exceed
+ * PKV_DECODE_SCRATCH_BYTES return PKV_ERR_INVALID and launch nothing (the
+ * 7B shape, 32 heads x 128 at the automatic 256 work-groups, needs about 8.6
+ * MB).  The array is shared by every call on its device and keeps the last
+ * call's contents (nothing in it needs clearing): calls that may overlap on
+ * one device must go through one stream, in order.  The first call on a
+ * device looks up the array's device address (PKV_ERR_HIP if that fails). */
+PKV_API int pkv_attention_decode_scratch(void* out, const void* q, const void* k_cache, const void* v_cache,
+                                         const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                         const int32_t* seq_lens, int32_t max_seq_len, int32_t batch,
+                                         int32_t num_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                         float scale, pkv_dtype dtype, int32_t num_work_groups, hipStream_t stream);
+
 /* Scatter and decode attention in one launch: for every sequence b with
  * L = seq_lens[b] >= 1, the new rows k_new[b], v_new[b] (device
  * [batch][num_heads][head_dim] of `dtype`) are stored at logical position

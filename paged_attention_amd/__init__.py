@@ -102,6 +102,8 @@ def _load():
         "pkv_decode_work_groups": (i32, [ctypes.c_int]),
         "pkv_swap_blocks": (ctypes.c_int, [ctypes.POINTER(vp), ctypes.POINTER(vp), i32, vp, i32, i32, i32, sz, vp]),
         "pkv_decode_workspace_bytes": (sz, [i32, i32, i32, ctypes.c_int, i32]),
+        "pkv_attention_decode_scratch": (ctypes.c_int, [vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, i32, i32,
+                                                        ctypes.c_float, ctypes.c_int, i32, vp]),
         "pkv_attention_decode": (ctypes.c_int, [vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, i32, i32,
                                                 ctypes.c_float, ctypes.c_int, i32, vp, sz, vp]),
         "pkv_append_quant": (ctypes.c_int, [vp, vp, i32, vp, vp, vp, vp, vp, i32, i32, i32, i32, ctypes.c_int,
@@ -544,6 +546,33 @@ def pkv_attention_decode(out, q, k_cache, v_cache, block_tables, seq_lens, max_s
     _check(_lib.pkv_attention_decode(*args))
 
 
+DECODE_SCRATCH_BYTES = 32 << 20   # PKV_DECODE_SCRATCH_BYTES
+
+
+def pkv_attention_decode_scratch(out, q, k_cache, v_cache, block_tables, seq_lens, max_seq_len, scale=None,
+                                 work_groups=0, stream=None) -> None:
+    """pkv_attention_decode with the library's own device scratch as workspace: allocates nothing.
+
+    Calls on one device share that scratch; they must not overlap (one stream, in order).
+    """
+    torch = _torch()
+    nb, bs, h, d = k_cache.shape
+    batch = q.shape[0]
+    if q.shape != (batch, h, d) or out.shape != q.shape or v_cache.shape != k_cache.shape:
+        raise InvalidArgument(PKV_ERR_INVALID, "attention_decode_scratch: shape mismatch")
+    if not (q.dtype == out.dtype == k_cache.dtype == v_cache.dtype):
+        raise InvalidArgument(PKV_ERR_INVALID, "attention_decode_scratch: dtype mismatch")
+    if block_tables.dim() != 2 or block_tables.shape[0] != batch or seq_lens.shape != (batch,):
+        raise InvalidArgument(PKV_ERR_INVALID, "attention_decode_scratch: tables must be [B][max_blocks], lens [B]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    _check(_lib.pkv_attention_decode_scratch(
+        _dev(out, "out"), _dev(q, "q"), _dev(k_cache, "k_cache", ndim=4), _dev(v_cache, "v_cache", ndim=4),
+        _dev(block_tables, "block_tables", torch.int32, pinned_ok=True), block_tables.shape[1],
+        _dev(seq_lens, "seq_lens", torch.int32, pinned_ok=True), int(max_seq_len), batch, h, d, bs, nb,
+        float(scale), _dtype_code(q), int(work_groups), _stream(stream)))
+
+
 PREFIX_TILE_SEQS, PREFIX_TILE_INTS, PREFIX_MAX_BLOCKS = 16, 18, 1024
 
 
@@ -919,6 +948,7 @@ class PreparedAppendDecode(PreparedDecode):
 __all__ = [
     "BlockAllocator", "PkvError", "OutOfBlocks", "InvalidArgument", "pkv_append", "pkv_copy_blocks",
     "pkv_attention_decode", "pkv_decode_workspace_bytes", "pkv_decode_work_groups",
+    "pkv_attention_decode_scratch", "DECODE_SCRATCH_BYTES",
     "decode_workspace", "PreparedDecode", "PreparedAppend", "version", "LIB_PATH",
     "pkv_append_quant", "pkv_attention_decode_quant", "PreparedDecodeQuant", "PreparedAppendQuant",
     "CACHE_FORMATS", "prefix_block_keys", "pkv_swap_blocks", "pkv_attention_decode_scores",

@@ -510,7 +510,84 @@ int decode_grouped(void* out, const void* q, const void* k_cache, const void* v_
 
 }  // namespace
 
+// ---- decode with the library's own device scratch ----------------------------
+//
+// pkv_attention_decode_scratch runs pkv_attention_decode with its workspace
+// (the per-sequence plan and the split pieces' partial states) in this
+// file-scope array instead of caller memory, for callers that cannot
+// allocate.  Each device holds its own copy from module load until the
+// process ends.  In host code `scratch` names a host-side stand-in, never the
+// device memory: its device address is looked up once per device, with that
+// device current, and only that address is handed to kernels.  Every call on
+// a device shares the device's copy, so calls that overlap on one device
+// (several streams or threads) race.  Nothing in it has to start at zero: the
+// decode kernel writes the plan and the pieces before any of them is read.
+constexpr size_t kScratchBytes = PKV_DECODE_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+
+constexpr int kScratchDevices = 64;
+
+// Device address of `scratch` on the current device (looked up on the first
+// call per device), or nullptr after recording the error.
+void* scratch_on_current_device() {
+  static std::atomic<void*> addr[kScratchDevices];  // zero-initialised; racing look-ups store the same value
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kScratchDevices) {
+    pkv::fail(PKV_ERR_HIP, "attention_decode_scratch: no usable current HIP device (%d)", dev);
+    return nullptr;
+  }
+  void* p = addr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr) {
+      pkv::fail(PKV_ERR_HIP, "attention_decode_scratch: device address of the scratch array on device %d: %s", dev,
+                hipGetErrorString(e));
+      return nullptr;
+    }
+    addr[dev].store(p, std::memory_order_release);
+  }
+  return p;
+}
+
+}  // namespace
+
 extern "C" {
+
+PKV_API int pkv_attention_decode_scratch(void* out, const void* q, const void* k_cache, const void* v_cache,
+                                         const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                         const int32_t* seq_lens, int32_t max_seq_len, int32_t batch,
+                                         int32_t num_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                         float scale, pkv_dtype dtype, int32_t num_work_groups, hipStream_t stream) {
+  if (batch > 0 && num_heads > 0 && num_work_groups >= 0 && num_work_groups <= (1 << 20) &&
+      supported(head_dim, block_size, dtype)) {
+    const int32_t wg = num_work_groups > 0 ? num_work_groups : auto_work_groups(dtype);
+    if (wg <= 0) {
+      pkv::take_call_events();  // a pending timing request belongs to this call
+      return wg;
+    }
+    const size_t need = workspace_layout(batch, num_heads, head_dim, dtype, wg).total;
+    if (need > kScratchBytes) {
+      pkv::take_call_events();
+      return pkv::fail(PKV_ERR_INVALID, "attention_decode_scratch: these sizes need %zu bytes of scratch, the library "
+                                        "holds %zu (fewer work-groups or heads, or pkv_attention_decode with a "
+                                        "workspace)", need, kScratchBytes);
+    }
+    void* ws = scratch_on_current_device();
+    if (ws == nullptr) {
+      pkv::take_call_events();
+      return PKV_ERR_HIP;
+    }
+    return decode_dense(out, q, nullptr, nullptr, k_cache, v_cache, block_tables, max_blocks_per_seq, seq_lens,
+                        max_seq_len, batch, num_heads, head_dim, block_size, num_blocks, scale, dtype, wg, ws,
+                        kScratchBytes, stream, "attention_decode_scratch");
+  }
+  // invalid or empty requests: decode_dense reports them exactly as pkv_attention_decode does
+  return decode_dense(out, q, nullptr, nullptr, k_cache, v_cache, block_tables, max_blocks_per_seq, seq_lens,
+                      max_seq_len, batch, num_heads, head_dim, block_size, num_blocks, scale, dtype, num_work_groups,
+                      nullptr, 0, stream, "attention_decode_scratch");
+}
 
 PKV_API size_t pkv_decode_grouped_workspace_bytes(int32_t batch, int32_t num_heads, int32_t head_dim, pkv_dtype dtype,
                                                   int32_t num_work_groups) {
