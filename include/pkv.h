@@ -522,8 +522,9 @@ PKV_API int pkv_attention_decode_quant_scores(void* out, const void* q, const vo
  * and head, with the tile's queries against the prefix as two small matrix
  * products on the matrix cores (scores = K Q^T, weighted values = V^T P^T,
  * with P split into two 16-bit parts so that the weights keep float32
- * precision), and seeds each sequence's online softmax over its own
- * positions with the prefix's (max, sum, weighted values).  The result
+ * precision); each sequence's own positions are attended by the decode
+ * kernel, and the merge kernel combines the prefix's partial (max, sum,
+ * weighted values) with those of the sequence's own positions.  The result
  * equals pkv_attention_decode.
  * ------------------------------------------------------------------------- */
 
@@ -552,8 +553,10 @@ PKV_API int pkv_prefix_tiles(const int32_t* tables, int32_t max_blocks_per_seq, 
                              int32_t* tiles, int32_t max_tiles, int32_t* num_tiles);
 
 /* Workspace bytes of pkv_attention_decode_grouped: the plain decode
- * workspace plus float32 prefix states [16][batch][num_heads][head_dim + 4]
- * (up to 16 work-groups share one tile and head, each writing its part). */
+ * workspace with room for one more partial state per sequence and head
+ * slice (a sequence with a shared prefix always leaves one), plus float32
+ * prefix states [16][batch][num_heads][head_dim + 4] (up to 16 work-groups
+ * share one tile and head, each writing its part). */
 PKV_API size_t pkv_decode_grouped_workspace_bytes(int32_t batch, int32_t num_heads, int32_t head_dim,
                                                   pkv_dtype dtype, int32_t num_work_groups);
 

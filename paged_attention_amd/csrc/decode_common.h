@@ -207,6 +207,9 @@ __device__ __forceinline__ float wave_sum(float x) {
 constexpr int kMaxVirtual = 5460;   // sequences x head slices per launch (the LDS arrays: 3 x (5460 + 1) int32 <= 64 KiB)
 constexpr int kTableWindow = 64;    // block ids held in registers at a time (one per lane)
 constexpr int kMergeWaves = 4;      // heads per merge work-group
+constexpr int32_t kPlanPrefix = 1 << 30;  // plan flag: the sequence has a shared prefix's partial states
+constexpr int32_t kPlanCount = kPlanPrefix - 1;
+constexpr int kPrefixPartsMax = 16;  // work-groups per (prefix tile, head) at most: partial states per sequence
 
 struct DecodeArgs {
   void* out;
@@ -299,9 +302,9 @@ __device__ __forceinline__ bool length_ok(int L, const DecodeArgs& a) {
 
 // First logical position the decode kernel attends for sequence b of valid
 // length L: in a grouped call, the end of a shared prefix shorter than L
-// (the prefix itself is attended by prefix_kernel); else 0.  Compiled only
-// for formats with a grouped entry point (GROUPED): the extra state costs
-// the 8-bit kernel registers and spills.
+// (the prefix itself is attended by prefix_kernel, whose partial states the
+// merge kernel folds in); else 0.  Compiled only for formats with a grouped
+// entry point (GROUPED).
 template <int BS, bool GROUPED>
 __device__ __forceinline__ int suffix_start(int b, int L, const DecodeArgs& a) {
   if (!GROUPED || a.prefix_blocks == nullptr) return 0;
@@ -373,7 +376,7 @@ enum DecodeMode { kPlain = 0, kAppend = 1, kScores = 2 };
 // work-group whose range holds a sequence's last chunk is the only one that
 // reads position L - 1, and it stores the row itself, lane by lane, before
 // reading it back with the same lanes: no other work-group is involved.
-template <class KV, int D, int BS, int MODE>
+template <class KV, int D, int BS, int MODE, bool GROUPED>
 __global__ void __launch_bounds__(KV::kMaxWaves * 64) decode_kernel(DecodeArgs a) {
   constexpr bool APPEND = MODE == kAppend;
   constexpr bool SCORES = MODE == kScores;
@@ -403,24 +406,31 @@ __global__ void __launch_bounds__(KV::kMaxWaves * 64) decode_kernel(DecodeArgs a
       [&](int v) {
         const int b = v % a.batch;
         const int L = s_len[b];
-        return length_ok<BS>(L, a) ? (L - suffix_start<BS, KV::kGrouped>(b, L, a) + kChunk - 1) / kChunk : 0;
+        return length_ok<BS>(L, a) ? (L - suffix_start<BS, GROUPED>(b, L, a) + kChunk - 1) / kChunk : 0;
       },
       nv, s_pref, s_waves);
   const int64_t total = s_pref[nv];
   // Ranges are dealt over min(grid, chunks) work-groups so none is empty.
   const int64_t nwg = total < gridDim.x ? total : static_cast<int64_t>(gridDim.x);
   // 2. pieces of every sequence the ranges cut; slots for their partials.
+  // A sequence with a shared prefix (grouped call) always leaves pieces: the
+  // merge kernel folds the prefix's partial states in with them.
+  auto prefixed = [&](int v) -> bool {
+    const int b = v % a.batch;
+    const int L = s_len[b];
+    return length_ok<BS>(L, a) && suffix_start<BS, GROUPED>(b, L, a) > 0;
+  };
   auto pieces = [&](int v) -> int32_t {
     const int64_t c0 = s_pref[v], c1 = s_pref[v + 1];
     if (c1 == c0) return 0;
     const int k = range_owner(c1 - 1, nwg, total) - range_owner(c0, nwg, total) + 1;
-    return k > 1 ? k : 0;
+    return k > 1 || prefixed(v) ? k : 0;
   };
   block_exclusive_scan(pieces, nv, s_part, s_waves);
   if (g == 0) {
     for (int v = threadIdx.x; v < nv; v += blockDim.x) {
       a.ws_plan[2 * v] = s_part[v];
-      a.ws_plan[2 * v + 1] = s_part[v + 1] - s_part[v];
+      a.ws_plan[2 * v + 1] = (s_part[v + 1] - s_part[v]) | (prefixed(v) ? kPlanPrefix : 0);
     }
   }
 
@@ -468,7 +478,6 @@ __global__ void __launch_bounds__(KV::kMaxWaves * 64) decode_kernel(DecodeArgs a
     const int b = v % a.batch, y = v / a.batch;
     const int hg = y * a.waves_per_group + wave;
     const int h = hg * HPW + r;
-    const bool whole = cur == seq0 && seg_end == seq1;
     if (hg * HPW < a.num_heads) {
       const bool head_ok = h < a.num_heads;
       const int hl = head_ok ? h : a.num_heads - 1;  // clamped head for loads
@@ -476,7 +485,7 @@ __global__ void __launch_bounds__(KV::kMaxWaves * 64) decode_kernel(DecodeArgs a
       const Elem* kp = static_cast<const Elem*>(a.k) + e0 * KB;
       const Elem* vp = static_cast<const Elem*>(a.v) + e0 * KB;
       const int L = s_len[b];
-      const int start = suffix_start<BS, KV::kGrouped>(b, L, a);
+      const int start = suffix_start<BS, GROUPED>(b, L, a);
       const int t_begin = start + static_cast<int>(cur - seq0) * kChunk;
       const int t_end = min(L, start + static_cast<int>(seg_end - seq0) * kChunk);
       const int32_t* trow = a.tables + static_cast<int64_t>(b) * a.max_blocks;
@@ -490,23 +499,13 @@ __global__ void __launch_bounds__(KV::kMaxWaves * 64) decode_kernel(DecodeArgs a
         }
       }
 
+      // a piece of a sequence with a shared prefix never writes the output:
+      // the merge kernel adds the prefix's partial states
+      const bool whole = cur == seq0 && seg_end == seq1 && start == 0;
       float m = -INFINITY, l = 0.f;
       float acc[EPL];
 #pragma unroll
       for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
-      if (KV::kGrouped && start > 0 && cur == seq0) {  // the first piece continues from the shared prefix's state,
-                                       // merged from its parts' partial states
-        const float* ps0 = a.prefix_state + (static_cast<int64_t>(b) * a.num_heads + hl) * a.prefix_row;
-        const int64_t part_stride = static_cast<int64_t>(a.prefix_batch) * a.num_heads * a.prefix_row;
-        for (int r = 0; r < a.prefix_parts; ++r) m = fmaxf(m, ps0[r * part_stride + D]);
-        for (int r = 0; r < a.prefix_parts; ++r) {
-          const float* ps = ps0 + r * part_stride;
-          const float w = ps[D] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ps[D] - m);
-          l = fmaf(ps[D + 1], w, l);
-#pragma unroll
-          for (int e = 0; e < EPL; ++e) acc[e] = fmaf(ps[c * EPL + e], w, acc[e]);
-        }
-      }
       bool bad_block = false;
       float* lrow = SCORES && head_ok ? a.logits + (static_cast<int64_t>(b) * a.num_heads + h) * a.logit_stride
                                       : nullptr;
@@ -562,8 +561,10 @@ __global__ void __launch_bounds__(KV::kMaxWaves * 64) decode_kernel(DecodeArgs a
   }
 }
 
-// Merges the pieces of every cut sequence:
-//   M = max_i m_i,  S = sum_i l_i 2^(m_i - M),  out = sum_i acc_i 2^(m_i - M) / S.
+// Merges the pieces of every cut sequence, after the partial states of its
+// shared prefix when it has one (grouped call):
+//   M = max_i m_i,  S = sum_i l_i 2^(m_i - M),  out = sum_i acc_i 2^(m_i - M) / S,
+// over the prefix's parts and then the pieces, in that order.
 // One wavefront per (sequence, head).  Lane i holds piece i's (m, l); the
 // lanes also split into groups of D/4 lanes that hold whole piece rows as
 // float4, kMergeRows rows per group.  Every load of a batch of pieces is
@@ -572,15 +573,18 @@ __global__ void __launch_bounds__(KV::kMaxWaves * 64) decode_kernel(DecodeArgs a
 constexpr int kMergeRows = 8;
 
 // Work-group (bx, v) of the merge: heads bx*kMergeWaves.. of virtual sequence v.
-template <int DT, int D>
+template <int DT, int D, bool GROUPED>
 __device__ __forceinline__ void merge_pieces(const DecodeArgs& a, int bx, int v) {
   constexpr int LPR = D / 4;     // lanes per piece row (float4 each)
   constexpr int RPW = 64 / LPR;  // rows per wavefront instruction
   constexpr int BATCH = RPW * kMergeRows;
   static_assert(BATCH <= 64, "a batch of pieces must fit one (m, l) per lane");
+  static_assert(BATCH >= kPrefixPartsMax, "a shared prefix's parts fit one batch");
   const int first = a.ws_plan[2 * v];
-  const int count = a.ws_plan[2 * v + 1];
-  if (count == 0) return;
+  const int word = a.ws_plan[2 * v + 1];
+  const int count = word & kPlanCount;
+  const bool pre = GROUPED && (word & kPlanPrefix) != 0;
+  if (count == 0 && !pre) return;
   const int b = v % a.batch, y = v / a.batch;
   const int slice_lo = y * a.waves_per_group * a.heads_per_wave;
   const int slice_hi = min(a.num_heads, slice_lo + a.waves_per_group * a.heads_per_wave);
@@ -589,23 +593,20 @@ __device__ __forceinline__ void merge_pieces(const DecodeArgs& a, int bx, int v)
   const int lane = threadIdx.x & 63;
   const int grp = lane / LPR;
   const int sub = lane % LPR;
-  const float2* ml = a.ws_ml + static_cast<int64_t>(first) * a.num_heads + h;  // stride num_heads
-  const float* accp = a.ws_acc + (static_cast<int64_t>(first) * a.num_heads + h) * D + sub * 4;
-  const int64_t row_stride = static_cast<int64_t>(a.num_heads) * D;
 
   float mx = -INFINITY;   // running max over batches (wave-uniform)
   float sum = 0.f;        // running sum, scaled to mx
   float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int i0 = 0; i0 < count; i0 += BATCH) {
-    const int n = min(BATCH, count - i0);
+  // Folds states 0 .. n-1 (n <= BATCH): ml_at(i) = (m, l), row_at(i) = this
+  // lane's float4 of the weighted values.
+  auto fold = [&](int n, auto ml_at, auto row_at) {
     // issue every load of the batch first
-    const float2 mine = lane < n ? ml[static_cast<int64_t>(i0 + lane) * a.num_heads] : make_float2(-INFINITY, 0.f);
+    const float2 mine = lane < n ? ml_at(lane) : make_float2(-INFINITY, 0.f);
     float4 rows[kMergeRows];
 #pragma unroll
     for (int k = 0; k < kMergeRows; ++k) {
       const int i = grp + k * RPW;
-      rows[k] = i < n ? *reinterpret_cast<const float4*>(accp + static_cast<int64_t>(i0 + i) * row_stride)
-                      : make_float4(0.f, 0.f, 0.f, 0.f);
+      rows[k] = i < n ? row_at(i) : make_float4(0.f, 0.f, 0.f, 0.f);
     }
     const float bmx = wave_max(mine.x);
     const float nmx = fmaxf(mx, bmx);
@@ -625,7 +626,25 @@ __device__ __forceinline__ void merge_pieces(const DecodeArgs& a, int bx, int v)
       o.w = fmaf(rows[k].w, wk, o.w);
     }
     mx = nmx;
+  };
+  if (GROUPED && pre) {  // the shared prefix's parts: [part][prefix_batch][H][prefix_row] = acc[D], max, sum
+    const float* ps = a.prefix_state + (static_cast<int64_t>(b) * a.num_heads + h) * a.prefix_row;
+    const int64_t part_stride = static_cast<int64_t>(a.prefix_batch) * a.num_heads * a.prefix_row;
+    fold(
+        a.prefix_parts,
+        [&](int i) {
+          const float* p = ps + i * part_stride + D;
+          return make_float2(p[0], p[1]);
+        },
+        [&](int i) { return *reinterpret_cast<const float4*>(ps + i * part_stride + sub * 4); });
   }
+  const float2* ml = a.ws_ml + static_cast<int64_t>(first) * a.num_heads + h;  // stride num_heads
+  const float* accp = a.ws_acc + (static_cast<int64_t>(first) * a.num_heads + h) * D + sub * 4;
+  const int64_t row_stride = static_cast<int64_t>(a.num_heads) * D;
+  for (int i0 = 0; i0 < count; i0 += BATCH)
+    fold(
+        min(BATCH, count - i0), [&](int i) { return ml[static_cast<int64_t>(i0 + i) * a.num_heads]; },
+        [&](int i) { return *reinterpret_cast<const float4*>(accp + static_cast<int64_t>(i0 + i) * row_stride); });
 #pragma unroll
   for (int off = LPR; off < 64; off <<= 1) {
     o.x += __shfl_xor(o.x, off, 64);
@@ -652,9 +671,9 @@ __device__ __forceinline__ void merge_pieces(const DecodeArgs& a, int bx, int v)
   }
 }
 
-template <int DT, int D>
+template <int DT, int D, bool GROUPED>
 __global__ void __launch_bounds__(kMergeWaves * 64) decode_merge_kernel(DecodeArgs a) {
-  merge_pieces<DT, D>(a, blockIdx.x, blockIdx.y);
+  merge_pieces<DT, D, GROUPED>(a, blockIdx.x, blockIdx.y);
 }
 
 // Cumulative attention scores: one thread per (sequence, position t < L):
@@ -705,7 +724,7 @@ __device__ __forceinline__ void score_positions(const DecodeArgs& a, int bx, int
     const int hk = min(h0 + lane, a.num_heads - 1);  // this lane's head
     const int v = (hk / slice_heads) * a.batch + b;   // its virtual sequence
     const int first = a.ws_plan[2 * v];
-    const int count = a.ws_plan[2 * v + 1];
+    const int count = a.ws_plan[2 * v + 1] & kPlanCount;
     float2 fm = a.final_ml[static_cast<int64_t>(b) * a.num_heads + hk];
     float x[NH];
 #pragma unroll
@@ -771,7 +790,7 @@ template <int DT, int D>
 __global__ void __launch_bounds__(kMergeWaves * 64) merge_score_kernel(DecodeArgs a, int merge_x) {
   static_assert(kMergeWaves * 64 == 256, "merge and score work-groups share the launch's shape");
   const int x = blockIdx.x;
-  if (x < merge_x) merge_pieces<DT, D>(a, x, blockIdx.y);
+  if (x < merge_x) merge_pieces<DT, D, false>(a, x, blockIdx.y);
   else if (static_cast<int>(blockIdx.y) < a.batch) score_positions(a, x - merge_x, blockIdx.y);
 }
 
@@ -841,20 +860,23 @@ inline Shape decode_shape(int32_t num_heads, int32_t head_dim, pkv_dtype cache_d
   return sh;
 }
 
-// Workspace: [plan: virtual sequences x 2 int32][acc: 2G slots x H x D f32][(m, l): 2G slots x H]
-// (a cut at each of the G-1 range boundaries adds at most one piece and one
-// cut sequence, so the pieces of all cut sequences number at most 2(G-1)).
+// Workspace: [plan: virtual sequences x 2 int32][acc: P slots x H x D f32][(m, l): P slots x H].
+// A cut at each of the G-1 range boundaries adds at most one piece and one
+// cut sequence, so the pieces of all cut sequences number at most 2(G-1);
+// in a grouped call a sequence with a shared prefix leaves a piece even
+// when it is not cut, at most one more per virtual sequence.  P = 2G, plus
+// the virtual sequences of a launch for a grouped call.
 struct Layout {
   size_t plan, acc, ml, total;
 };
 
 inline Layout workspace_layout(int32_t batch, int32_t num_heads, int32_t head_dim, pkv_dtype cache_dtype,
-                               int32_t wg) {
+                               int32_t wg, bool grouped = false) {
   auto up = [](size_t x) { return (x + 255) / 256 * 256; };
   const Shape sh = decode_shape(num_heads, head_dim, cache_dtype);
   const int64_t per_launch = kMaxVirtual / sh.groups_y;
   const size_t nv = static_cast<size_t>(batch < per_launch ? batch : per_launch) * sh.groups_y;
-  const size_t slots = 2 * static_cast<size_t>(wg) * num_heads;
+  const size_t slots = (2 * static_cast<size_t>(wg) + (grouped ? nv : 0)) * num_heads;
   Layout w{};
   w.plan = 0;
   w.acc = up(nv * 2 * sizeof(int32_t));
@@ -867,12 +889,13 @@ inline Layout workspace_layout(int32_t batch, int32_t num_heads, int32_t head_di
 // a score request, the merge and score kernel).  `tm.start` goes with the
 // first and `tm.stop` with the second (kernel timestamps, no extra queue
 // packets).
-template <class KV, int D, int BS, int MODE>
-void launch_decode(const DecodeArgs& a, int wg, hipStream_t stream, const pkv::CallEvents& tm) {
+// GROUPED: a grouped call (shared prefixes attended by the prefix kernel).
+template <class KV, int D, int BS, int MODE, bool GROUPED>
+void launch_decode_g(const DecodeArgs& a, int wg, hipStream_t stream, const pkv::CallEvents& tm) {
   const size_t lds = (2 * (static_cast<size_t>(a.batch) * a.groups_y + 1) + a.batch) * sizeof(int32_t);
   const bool scores = MODE == kScores && a.max_seq_len > 0;
-  hipExtLaunchKernelGGL((decode_kernel<KV, D, BS, MODE>), dim3(wg), dim3(a.waves_per_group * 64), lds, stream,
-                        tm.start, nullptr, 0, a);
+  hipExtLaunchKernelGGL((decode_kernel<KV, D, BS, MODE, GROUPED>), dim3(wg), dim3(a.waves_per_group * 64), lds,
+                        stream, tm.start, nullptr, 0, a);
   const int slice_heads = a.waves_per_group * a.heads_per_wave;
   const int merge_x = ceil_div(slice_heads, kMergeWaves);
   if (scores)
@@ -880,8 +903,19 @@ void launch_decode(const DecodeArgs& a, int wg, hipStream_t stream, const pkv::C
                           dim3(merge_x + ceil_div(a.max_seq_len, 256), a.batch * a.groups_y), dim3(kMergeWaves * 64),
                           0, stream, nullptr, tm.stop, 0, a, merge_x);
   else
-    hipExtLaunchKernelGGL((decode_merge_kernel<KV::QT, D>), dim3(merge_x, a.batch * a.groups_y),
+    hipExtLaunchKernelGGL((decode_merge_kernel<KV::QT, D, GROUPED>), dim3(merge_x, a.batch * a.groups_y),
                           dim3(kMergeWaves * 64), 0, stream, nullptr, tm.stop, 0, a);
+}
+
+template <class KV, int D, int BS, int MODE>
+void launch_decode(const DecodeArgs& a, int wg, hipStream_t stream, const pkv::CallEvents& tm) {
+  if constexpr (MODE == kPlain && KV::kGrouped) {
+    if (a.prefix_blocks != nullptr) {
+      launch_decode_g<KV, D, BS, MODE, true>(a, wg, stream, tm);
+      return;
+    }
+  }
+  launch_decode_g<KV, D, BS, MODE, false>(a, wg, stream, tm);
 }
 
 template <class KV, int D, int MODE>
@@ -968,12 +1002,12 @@ inline int prepare_decode(DecodeArgs& a, const void* q, const void* k_cache, con
                           const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* seq_lens,
                           int32_t max_seq_len, int32_t batch, int32_t num_heads, int32_t head_dim, int32_t block_size,
                           int32_t num_blocks, float scale, pkv_dtype cache_dtype, int32_t num_work_groups,
-                          void* workspace, size_t workspace_bytes, const void* out) {
+                          void* workspace, size_t workspace_bytes, const void* out, bool grouped = false) {
   if (!out || !q || !k_cache || !v_cache || !block_tables || !seq_lens)
     return pkv::fail(PKV_ERR_INVALID, "attention_decode: null pointer");
   const int32_t wg = num_work_groups > 0 ? num_work_groups : auto_work_groups(cache_dtype);
   if (wg <= 0) return wg;
-  const Layout ws = workspace_layout(batch, num_heads, head_dim, cache_dtype, wg);
+  const Layout ws = workspace_layout(batch, num_heads, head_dim, cache_dtype, wg, grouped);
   if (workspace == nullptr || workspace_bytes < ws.total)
     return pkv::fail(PKV_ERR_INVALID, "attention_decode: workspace of %zu bytes needed, %zu given", ws.total,
                      workspace_bytes);

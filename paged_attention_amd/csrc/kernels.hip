@@ -110,7 +110,6 @@ struct DenseKV {
 constexpr int kPrefixWaves = 4;
 constexpr int kPrefixStep = 16;     // positions per step (the MFMA's M and K)
 constexpr int kPrefixIdsLds = PKV_PREFIX_MAX_BLOCKS;  // a tile's block ids, all staged in LDS
-constexpr int kPrefixPartsMax = 16;  // work-groups per (tile, head) at most
 // The prefix grid's x size is tiles × parts work-groups of 256 lanes and the
 // dispatch counts lanes in 32 bits; parts is 1 from 512 tiles on, so this cap
 // keeps every launch far inside it.
@@ -425,7 +424,7 @@ int decode_dense(void* out, const void* q, const void* k_new, const void* v_new,
 // states of up to kPrefixPartsMax parts.
 inline size_t grouped_workspace_bytes(int32_t batch, int32_t num_heads, int32_t head_dim, pkv_dtype dtype,
                                       int32_t wg) {
-  const size_t base = workspace_layout(batch, num_heads, head_dim, dtype, wg).total;
+  const size_t base = workspace_layout(batch, num_heads, head_dim, dtype, wg, true).total;
   return base + (static_cast<size_t>(kPrefixPartsMax) * batch * num_heads * (head_dim + 4) * sizeof(float) + 255) /
                     256 * 256;
 }
@@ -463,14 +462,14 @@ int decode_grouped(void* out, const void* q, const void* k_cache, const void* v_
   DecodeArgs a;
   const int wg = prepare_decode(a, q, k_cache, v_cache, block_tables, max_blocks_per_seq, seq_lens, max_seq_len,
                                 batch, num_heads, head_dim, block_size, num_blocks, scale, dtype, num_work_groups,
-                                workspace, workspace_bytes, out);
+                                workspace, workspace_bytes, out, /*grouped=*/true);
   if (wg <= 0) return wg;
   const size_t need = grouped_workspace_bytes(batch, num_heads, head_dim, dtype, wg);
   if (workspace_bytes < need)
     return pkv::fail(PKV_ERR_INVALID, "%s: workspace of %zu bytes needed, %zu given", what, need, workspace_bytes);
   a.prefix_blocks = seq_prefix_blocks;
   a.prefix_state = reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                            workspace_layout(batch, num_heads, head_dim, dtype, wg).total);
+                                            workspace_layout(batch, num_heads, head_dim, dtype, wg, true).total);
   a.prefix_row = head_dim + 4;
   a.prefix_batch = batch;
   // Parts per (tile, head): enough work-groups for two per compute unit.

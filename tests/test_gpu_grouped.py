@@ -1,8 +1,9 @@
 """GPU parity of grouped decode (pkv_attention_decode_grouped) through the C interface.
 
 Shared prefixes are attended once per tile of up to 16 sequences with the
-matrix cores and each sequence's own positions by the decode kernel, seeded
-with the prefix's softmax state; the output must match the oracle's attention
+matrix cores and each sequence's own positions by the decode kernel; the
+merge kernel combines the prefix's partial softmax states with the
+sequence's pieces.  The output must match the oracle's attention
 within the bounds of pkv_attention_decode (2e-3 fp16; bf16 adds its output
 rounding).  Pools are NaN outside written slots, so any read of a wrong
 position shows in the output.
