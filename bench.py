@@ -92,8 +92,8 @@ def parse():
                    help="also update cumulative attention scores per cached token (16/32-bit caches; two launches "
                         "per layer)")
     p.add_argument("--grouped", action="store_true",
-                   help="decode with pkv_attention_decode_grouped: shared prefixes read once per tile of sequences "
-                        "(two launches per layer)")
+                   help="decode with pkv_attention_decode_grouped[_quant]: shared prefixes read once per tile of "
+                        "sequences (three launches per layer)")
     p.add_argument("--separate", action="store_true",
                    help="scatter and attend in two launches per layer (pkv_append, pkv_attention_decode) instead "
                         "of one (pkv_append_attention_decode)")
@@ -558,8 +558,8 @@ def main():
     if args.scores and kv != "dense":
         print("--scores runs with a 16/32-bit cache", file=sys.stderr)
         sys.exit(2)
-    if args.grouped and (kv != "dense" or args.scores or wl.dtype not in ("f16", "bf16")):
-        print("--grouped runs with an fp16/bf16 cache and no scores", file=sys.stderr)
+    if args.grouped and (args.scores or wl.dtype not in ("f16", "bf16")):
+        print("--grouped runs with fp16/bf16 queries and no scores", file=sys.stderr)
         sys.exit(2)
     fused = not (args.separate or args.scores or args.grouped)
     timed_steps = -(-max(50, args.timed_calls) // NL)
@@ -649,7 +649,8 @@ def main():
         # valid for every later step.
         spb, tiles = pkv.prefix_tiles(tables, (cur + 1).astype(np.int32), bs)
         prefix = (torch.from_numpy(spb).to(dev), torch.from_numpy(tiles).to(dev))
-        workspace = torch.empty(pkv.pkv_decode_grouped_workspace_bytes(B, H, D, wl.dtype, wgs), dtype=torch.uint8,
+        workspace = torch.empty(pkv.pkv_decode_grouped_workspace_bytes(B, H, D, wl.dtype if kv == "dense" else kv,
+                                                                       wgs), dtype=torch.uint8,
                                 device=dev)
     # Step metadata is one packed buffer: slots (int64), lengths and block
     # tables (int32).  Host side: a ring of pinned buffers, so the host can
@@ -730,7 +731,7 @@ def main():
                                              k_scales[l], v_scales[l], kv) for l in range(NL)],
                     [pkv.PreparedDecodeQuant(out, q_all[0, l], k_caches[l], v_caches[l], k_scales[l], v_scales[l],
                                              tb_t, ln_t, max_len, kv, scale=wl.scale, work_groups=wgs,
-                                             workspace=workspace) for l in range(NL)])
+                                             workspace=workspace, prefix=prefix) for l in range(NL)])
     calls = [per_slot[metas[r][0].data_ptr()] for r in range(ring)]
     torch.cuda.synchronize()
 
@@ -890,7 +891,8 @@ def main():
         cpu = cpu_baseline(wl, rows, args.cpu_seconds, kv)
 
     ms_per_step = elapsed / args.steps * 1e3
-    call_name = ("pkv_attention_decode_grouped (prefix_kernel + decode_kernel + decode_merge_kernel)"
+    call_name = ("pkv_attention_decode_grouped" + ("_quant" if kv != "dense" else "")
+                 + " (prefix_kernel + decode_kernel + decode_merge_kernel)"
                  if prefix is not None else
                  "pkv_attention_decode_scores (decode_kernel + merge_score_kernel)" if args.scores else
                  ("pkv_append_attention_decode" if fused else "pkv_attention_decode")

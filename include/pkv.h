@@ -552,11 +552,12 @@ PKV_API int pkv_prefix_tiles(const int32_t* tables, int32_t max_blocks_per_seq, 
                              int32_t batch, int32_t block_size, int32_t min_sharers, int32_t* seq_prefix_blocks,
                              int32_t* tiles, int32_t max_tiles, int32_t* num_tiles);
 
-/* Workspace bytes of pkv_attention_decode_grouped: the plain decode
- * workspace with room for one more partial state per sequence and head
- * slice (a sequence with a shared prefix always leaves one), plus float32
- * prefix states [16][batch][num_heads][head_dim + 4] (up to 16 work-groups
- * share one tile and head, each writing its part). */
+/* Workspace bytes of pkv_attention_decode_grouped (dtype F16/BF16) and
+ * pkv_attention_decode_grouped_quant (dtype = the cache's, I8/FP8_E4M3): the
+ * plain decode workspace with room for one more partial state per sequence
+ * and head slice (a sequence with a shared prefix always leaves one), plus
+ * float32 prefix states [16][batch][num_heads][head_dim + 4] (up to 16
+ * work-groups share one tile and head, each writing its part). */
 PKV_API size_t pkv_decode_grouped_workspace_bytes(int32_t batch, int32_t num_heads, int32_t head_dim,
                                                   pkv_dtype dtype, int32_t num_work_groups);
 
@@ -584,6 +585,30 @@ PKV_API int pkv_attention_decode_grouped(void* out, const void* q, const void* k
                                          float scale, pkv_dtype dtype, const int32_t* seq_prefix_blocks,
                                          const int32_t* tiles, int32_t num_tiles, int32_t num_work_groups,
                                          void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* pkv_attention_decode_grouped for an 8-bit cache (int8 or OCP FP8 E4M3
+ * codes with per-(token, head) scales, the format of
+ * pkv_attention_decode_quant): the result equals pkv_attention_decode_quant.
+ * Shared prefixes are quantised caches too: their codes enter the matrix
+ * cores as the query's type (every E4M3 value, and every int8 value in
+ * [-127, 127], is exact in f16 and in bf16), each position's K scale
+ * multiplies its scores and its V scale its softmax weight
+ * (icman.com.cn/news/78786 §1.3 and §3.4: quantised caches and shared
+ * prefixes together).  q_dtype F16 or BF16 (else PKV_ERR_INVALID);
+ * cache_dtype I8 or FP8_E4M3; k_scales, v_scales as for
+ * pkv_attention_decode_quant; seq_prefix_blocks, tiles, num_tiles as for
+ * pkv_attention_decode_grouped; workspace:
+ * pkv_decode_grouped_workspace_bytes with dtype = cache_dtype.  Every other
+ * argument is that of pkv_attention_decode_quant. */
+PKV_API int pkv_attention_decode_grouped_quant(void* out, const void* q, const void* k_cache, const void* v_cache,
+                                               const float* k_scales, const float* v_scales,
+                                               const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                               const int32_t* seq_lens, int32_t max_seq_len, int32_t batch,
+                                               int32_t num_heads, int32_t head_dim, int32_t block_size,
+                                               int32_t num_blocks, float scale, pkv_dtype q_dtype,
+                                               pkv_dtype cache_dtype, const int32_t* seq_prefix_blocks,
+                                               const int32_t* tiles, int32_t num_tiles, int32_t num_work_groups,
+                                               void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

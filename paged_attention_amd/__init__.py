@@ -76,6 +76,9 @@ def _load():
         "pkv_decode_grouped_workspace_bytes": (sz, [i32, i32, i32, ctypes.c_int, i32]),
         "pkv_attention_decode_grouped": (ctypes.c_int, [vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, i32, i32,
                                                         ctypes.c_float, ctypes.c_int, vp, vp, i32, i32, vp, sz, vp]),
+        "pkv_attention_decode_grouped_quant": (ctypes.c_int, [vp, vp, vp, vp, vp, vp, vp, i32, vp, i32, i32, i32,
+                                                              i32, i32, i32, ctypes.c_float, ctypes.c_int,
+                                                              ctypes.c_int, vp, vp, i32, i32, vp, sz, vp]),
         "pkv_allocator_create": (ctypes.c_int, [i32, i32, p32, ctypes.POINTER(vp)]),
         "pkv_allocator_destroy": (None, [vp]),
         "pkv_block_alloc": (ctypes.c_int, [vp, p32]),
@@ -793,16 +796,58 @@ def pkv_attention_decode_quant(out, q, k_cache, v_cache, k_scales, v_scales, blo
     _check(_lib.pkv_attention_decode_quant(*args))
 
 
+def _grouped_quant_args(out, q, k_cache, v_cache, k_scales, v_scales, block_tables, seq_lens, max_seq_len,
+                        seq_prefix_blocks, tiles, cache_dtype, scale, work_groups, workspace, stream):
+    torch = _torch()
+    batch, h, d = q.shape
+    if workspace is None:
+        need = pkv_decode_grouped_workspace_bytes(max(batch, 1), h, d, cache_dtype, work_groups)
+        if need == 0:
+            raise InvalidArgument(PKV_ERR_INVALID, "attention_decode_grouped_quant: unsupported sizes")
+        workspace = _bytes_on(need, q.device, stream)
+    args, _ = _decode_quant_args(out, q, k_cache, v_cache, k_scales, v_scales, block_tables, seq_lens, max_seq_len,
+                                 cache_dtype, scale, work_groups, workspace, stream)
+    if seq_prefix_blocks.shape != (batch,) or tiles.dim() != 2 or tiles.shape[1] != PREFIX_TILE_INTS:
+        raise InvalidArgument(PKV_ERR_INVALID, "attention_decode_grouped_quant: seq_prefix_blocks [B], tiles [n][18]")
+    grouped = [_dev(seq_prefix_blocks, "seq_prefix_blocks", torch.int32, pinned_ok=True),
+               _dev(tiles, "tiles", torch.int32, pinned_ok=True) if tiles.shape[0] else None, tiles.shape[0]]
+    # the quant argument list with the prefix arrays before the work-group count
+    return args[:18] + grouped + args[18:], workspace
+
+
+def pkv_attention_decode_grouped_quant(out, q, k_cache, v_cache, k_scales, v_scales, block_tables, seq_lens,
+                                       max_seq_len, seq_prefix_blocks, tiles, cache_dtype, scale=None,
+                                       work_groups=0, workspace=None, stream=None) -> None:
+    """pkv_attention_decode_quant with shared prefixes read once per tile (f16 or bf16 queries)."""
+    if q.shape[0] == 0:
+        return
+    args, _ = _grouped_quant_args(out, q, k_cache, v_cache, k_scales, v_scales, block_tables, seq_lens,
+                                  max_seq_len, seq_prefix_blocks, tiles, cache_dtype, scale, work_groups, workspace,
+                                  stream)
+    _check(_lib.pkv_attention_decode_grouped_quant(*args))
+
+
 class PreparedDecodeQuant(PreparedDecode):
-    """A pkv_attention_decode_quant call checked once; ``launch(q, out)`` swaps q/out."""
+    """A pkv_attention_decode_quant call checked once; ``launch(q, out)`` swaps q/out.
+
+    With ``prefix = (seq_prefix_blocks, tiles)`` the call is
+    pkv_attention_decode_grouped_quant.
+    """
 
     def __init__(self, out, q, k_cache, v_cache, k_scales, v_scales, block_tables, seq_lens, max_seq_len,
-                 cache_dtype, scale=None, work_groups=0, workspace=None, stream=None):  # noqa: D107
-        self._args, ws = _decode_quant_args(out, q, k_cache, v_cache, k_scales, v_scales, block_tables, seq_lens,
-                                            max_seq_len, cache_dtype, scale, work_groups, workspace, stream)
-        self._keep = (k_cache, v_cache, k_scales, v_scales, block_tables, seq_lens, ws)
+                 cache_dtype, scale=None, work_groups=0, workspace=None, stream=None, prefix=None):  # noqa: D107
+        if prefix is not None:
+            self._args, ws = _grouped_quant_args(out, q, k_cache, v_cache, k_scales, v_scales, block_tables,
+                                                 seq_lens, max_seq_len, prefix[0], prefix[1], cache_dtype, scale,
+                                                 work_groups, workspace, stream)
+            self._fn = _lib.pkv_attention_decode_grouped_quant
+        else:
+            self._args, ws = _decode_quant_args(out, q, k_cache, v_cache, k_scales, v_scales, block_tables,
+                                                seq_lens, max_seq_len, cache_dtype, scale, work_groups, workspace,
+                                                stream)
+            self._fn = _lib.pkv_attention_decode_quant
+        self._keep = (k_cache, v_cache, k_scales, v_scales, block_tables, seq_lens, ws, prefix)
         self._shape, self._dtype = tuple(q.shape), q.dtype
-        self._fn = _lib.pkv_attention_decode_quant
         self._ti = 6
 
 
@@ -954,5 +999,6 @@ __all__ = [
     "CACHE_FORMATS", "prefix_block_keys", "pkv_swap_blocks", "pkv_attention_decode_scores",
     "pkv_attention_decode_quant_scores", "pkv_decode_scores_workspace_bytes", "scores_workspace",
     "prefix_tiles", "pkv_attention_decode_grouped", "pkv_decode_grouped_workspace_bytes", "PREFIX_TILE_SEQS",
+    "pkv_attention_decode_grouped_quant",
     "PREFIX_TILE_INTS", "pkv_append_attention_decode", "pkv_append_attention_decode_quant", "PreparedAppendDecode",
 ]

@@ -25,6 +25,7 @@
 // pairs in dot2 instructions; otherwise the codes become floats
 // (v_cvt_pk_f32_fp8 for E4M3, signed byte conversion for int8).
 #include "decode_common.h"
+#include "prefix_common.h"
 
 namespace {
 
@@ -126,7 +127,7 @@ struct Q8KV {
   static constexpr int KB = 1;
   static constexpr int EPL = 16;
   static constexpr int kMaxWaves = 8;
-  static constexpr bool kGrouped = false;  // no grouped entry point for 8-bit caches
+  static constexpr bool kGrouped = true;   // pkv_attention_decode_grouped_quant uses this policy
   // q.k on 16-bit pairs (see qk16).
   static constexpr bool kPairQK = K == PKV_FP8_E4M3 && (Q == PKV_F16 || Q == PKV_BF16);
   struct QReg {
@@ -295,6 +296,42 @@ struct Q8KV {
   }
 };
 
+// Prefix-kernel load policy of 8-bit caches with f16 or bf16 queries: the
+// codes enter the matrix cores as the query's type (every E4M3 value and
+// every int8 value in [-127, 127] is exact in f16 and in bf16), the scales
+// act on scores and weights.
+template <int Q, int K>
+struct PrefixQ8 {
+  static_assert(Q == PKV_F16 || Q == PKV_BF16, "matrix-core input types");
+  static constexpr int MT = Q;
+  static constexpr int KB = 1;
+  static constexpr bool kScaled = true;
+  __device__ static uint32_t bits16(float x) { return Q == PKV_F16 ? f16_bits(x) : bf16_rne(x); }
+  template <int N>
+  __device__ static void widen(const uint32_t* raw, uint32_t* w) {
+#pragma unroll
+    for (int i = 0; i < N / 4; ++i) {
+      if constexpr (K == PKV_FP8_E4M3) {
+        if constexpr (Q == PKV_F16) {
+          w[2 * i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(raw[i], 1.f, false));
+          w[2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(raw[i], 1.f, true));
+        } else {
+          w[2 * i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw[i], 1.f, false));
+          w[2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw[i], 1.f, true));
+        }
+      } else {
+        float c[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) c[j] = static_cast<float>(static_cast<int8_t>(raw[i] >> (8 * j)));
+        w[2 * i] = bits16(c[0]) | (bits16(c[1]) << 16);
+        w[2 * i + 1] = bits16(c[2]) | (bits16(c[3]) << 16);
+      }
+    }
+  }
+  __device__ static const float* k_scales(const DecodeArgs& a) { return a.k_scales; }
+  __device__ static const float* v_scales(const DecodeArgs& a) { return a.v_scales; }
+};
+
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 template <int ST, int KT>
@@ -365,9 +402,87 @@ int decode_q8(void* out, const void* q, const void* k_new, const void* v_new, co
                     });
 }
 
+template <int Q, int K>
+void launch_prefix_q8(const DecodeArgs& pa, int32_t bs, int32_t d, const int32_t* tiles, int32_t num_tiles,
+                      hipStream_t stream, hipEvent_t start) {
+  if (d == 64) launch_prefix<PrefixQ8<Q, K>, 64>(pa, bs, tiles, num_tiles, stream, start);
+  else launch_prefix<PrefixQ8<Q, K>, 128>(pa, bs, tiles, num_tiles, stream, start);
+}
+
+int decode_grouped_q8(void* out, const void* q, const void* k_cache, const void* v_cache, const float* k_scales,
+                      const float* v_scales, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                      const int32_t* seq_lens, int32_t max_seq_len, int32_t batch, int32_t num_heads,
+                      int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale, pkv_dtype q_dtype,
+                      pkv_dtype cache_dtype, const int32_t* seq_prefix_blocks, const int32_t* tiles,
+                      int32_t num_tiles, int32_t num_work_groups, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream) {
+  const pkv::CallEvents timing = pkv::take_call_events();  // consumed by this call, whatever its outcome
+  const char* what = "attention_decode_grouped_quant";
+  const int sz = check_grouped_sizes(what, batch, num_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
+                                     max_seq_len, num_tiles);
+  if (sz != PKV_OK) return sz;
+  if ((q_dtype != PKV_F16 && q_dtype != PKV_BF16) || !is_8bit(cache_dtype))
+    return pkv::fail(PKV_ERR_INVALID, "%s: queries must be f16 or bf16 and the cache 8-bit (q dtype %d, cache %d)",
+                     what, static_cast<int>(q_dtype), static_cast<int>(cache_dtype));
+  const int st = check_decode_scalars(scale, num_work_groups);
+  if (st != PKV_OK) return st;
+  if (batch == 0) return PKV_OK;
+  if (!seq_prefix_blocks || (num_tiles > 0 && !tiles))
+    return pkv::fail(PKV_ERR_INVALID, "%s: null prefix arrays", what);
+  if (!k_scales || !v_scales) return pkv::fail(PKV_ERR_INVALID, "%s: null scale pool", what);
+  if (!aligned16(q) || !aligned16(out) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(k_scales) ||
+      !aligned16(v_scales))
+    return pkv::fail(PKV_ERR_INVALID, "%s: q, out, pools and scales must be 16-byte aligned", what);
+  DecodeArgs a;
+  const int wg = prepare_decode(a, q, k_cache, v_cache, block_tables, max_blocks_per_seq, seq_lens, max_seq_len,
+                                batch, num_heads, head_dim, block_size, num_blocks, scale, cache_dtype,
+                                num_work_groups, workspace, workspace_bytes, out, /*grouped=*/true);
+  if (wg <= 0) return wg;
+  a.k_scales = const_cast<float*>(k_scales);
+  a.v_scales = const_cast<float*>(v_scales);
+  const int64_t row = static_cast<int64_t>(num_heads) * head_dim * dtype_bytes(q_dtype);
+  const bool fp8 = cache_dtype == PKV_FP8_E4M3;
+  return run_grouped(
+      a, wg, out, q, block_tables, max_blocks_per_seq, seq_lens, batch, num_heads, head_dim, cache_dtype, row,
+      seq_prefix_blocks, num_tiles, workspace, workspace_bytes, timing, what,
+      [&](const DecodeArgs& pa, hipEvent_t start) {
+        if (q_dtype == PKV_F16) {
+          if (fp8) launch_prefix_q8<PKV_F16, PKV_FP8_E4M3>(pa, block_size, head_dim, tiles, num_tiles, stream, start);
+          else launch_prefix_q8<PKV_F16, PKV_I8>(pa, block_size, head_dim, tiles, num_tiles, stream, start);
+        } else {
+          if (fp8) launch_prefix_q8<PKV_BF16, PKV_FP8_E4M3>(pa, block_size, head_dim, tiles, num_tiles, stream, start);
+          else launch_prefix_q8<PKV_BF16, PKV_I8>(pa, block_size, head_dim, tiles, num_tiles, stream, start);
+        }
+      },
+      [&](const DecodeArgs& s, const pkv::CallEvents& tm) {
+        if (q_dtype == PKV_F16) {
+          if (fp8) launch_decode_m<Q8KV<PKV_F16, PKV_FP8_E4M3>, kPlain>(s, wg, block_size, head_dim, stream, tm);
+          else launch_decode_m<Q8KV<PKV_F16, PKV_I8>, kPlain>(s, wg, block_size, head_dim, stream, tm);
+        } else {
+          if (fp8) launch_decode_m<Q8KV<PKV_BF16, PKV_FP8_E4M3>, kPlain>(s, wg, block_size, head_dim, stream, tm);
+          else launch_decode_m<Q8KV<PKV_BF16, PKV_I8>, kPlain>(s, wg, block_size, head_dim, stream, tm);
+        }
+      });
+}
+
 }  // namespace
 
 extern "C" {
+
+PKV_API int pkv_attention_decode_grouped_quant(void* out, const void* q, const void* k_cache, const void* v_cache,
+                                               const float* k_scales, const float* v_scales,
+                                               const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                               const int32_t* seq_lens, int32_t max_seq_len, int32_t batch,
+                                               int32_t num_heads, int32_t head_dim, int32_t block_size,
+                                               int32_t num_blocks, float scale, pkv_dtype q_dtype,
+                                               pkv_dtype cache_dtype, const int32_t* seq_prefix_blocks,
+                                               const int32_t* tiles, int32_t num_tiles, int32_t num_work_groups,
+                                               void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return decode_grouped_q8(out, q, k_cache, v_cache, k_scales, v_scales, block_tables, max_blocks_per_seq, seq_lens,
+                           max_seq_len, batch, num_heads, head_dim, block_size, num_blocks, scale, q_dtype,
+                           cache_dtype, seq_prefix_blocks, tiles, num_tiles, num_work_groups, workspace,
+                           workspace_bytes, stream);
+}
 
 PKV_API int pkv_append_quant(const void* k_new, const void* v_new, int32_t num_tokens, const int64_t* slot_mapping,
                              void* k_cache, void* v_cache, float* k_scales, float* v_scales, int32_t num_blocks,

@@ -187,6 +187,11 @@ def test_workspace_queries():
     assert pkv.pkv_decode_workspace_bytes(b, 256, 64, "i8", wg) == (
         up(b * 2 * 8) + up(2 * wg * 256 * 64 * 4) + up(2 * wg * 256 * 8))
     assert pkv.pkv_decode_workspace_bytes(b, h, d, "f16", -1) == 0
+    # grouped: one more piece slot per sequence, then 16 parts of prefix states
+    for dt in ("f16", "bf16", "fp8", "i8"):
+        want = up(b * 8) + up((2 * wg + b) * h * d * 4) + up((2 * wg + b) * h * 8) + up(16 * b * h * (d + 4) * 4)
+        assert pkv.pkv_decode_grouped_workspace_bytes(b, h, d, dt, wg) == want
+    assert pkv.pkv_decode_grouped_workspace_bytes(b, h, d, "f32", wg) == 0
 
 
 def test_one_hip_runtime_per_process():

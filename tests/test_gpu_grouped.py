@@ -137,3 +137,79 @@ def test_batch_slices_with_groups():
     out, spb, tiles = _grouped(c, work_groups=300)
     assert spb[:300].min() == 4 and len(tiles) == 19
     pc.compare(c, out)
+
+
+# ---- 8-bit caches (pkv_attention_decode_grouped_quant) -----------------------
+
+def _grouped_quant(c, work_groups=0, spb=None, tiles=None, min_sharers=2):
+    if spb is None:
+        spb, tiles = pkv.prefix_tiles(c.tables_np, c.wl.seq_lens, c.wl.block_size, min_sharers)
+    out = torch.empty_like(c.q)
+    pkv.pkv_attention_decode_grouped_quant(out, c.q, c.k_cache, c.v_cache, c.k_scales, c.v_scales, c.tables, c.lens,
+                                           c.wl.max_seq_len, torch.from_numpy(np.ascontiguousarray(spb)).to(DEV),
+                                           torch.from_numpy(np.ascontiguousarray(tiles)).to(DEV), c.kv,
+                                           scale=c.wl.scale, work_groups=work_groups)
+    torch.cuda.synchronize()
+    return out, spb, tiles
+
+
+@pytest.mark.parametrize("fmt", ["i8", "fp8"])
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("head_dim,block_size", [(64, 8), (128, 16), (64, 32), (128, 8)])
+def test_small_groups_quant_match_oracle(fmt, dtype, head_dim, block_size):
+    # The oracle attends over the exactly dequantised rows; the grouped call
+    # meets the same bound as pkv_attention_decode_quant.
+    wl = workloads.custom(LENS, num_heads=5, head_dim=head_dim, dtype=dtype, block_size=block_size,
+                          seed=head_dim + block_size + 1, prefix_len=40, sharers=SHARERS)
+    c = pc.build(wl, DEV, kv=fmt)
+    ref = pc.oracle_out(c)
+    for wg in (0, 3, 50):
+        out, spb, tiles = _grouped_quant(c, wg)
+        assert len(tiles) == 1 and spb[SHARERS].min() == 40 // block_size
+        pc.compare(c, out, ref)
+
+
+def test_quant_no_tiles_is_the_plain_call_bit_for_bit():
+    wl = workloads.custom(LENS, num_heads=5, head_dim=128, dtype="f16", block_size=16, seed=4, prefix_len=40,
+                          sharers=SHARERS)
+    c = pc.build(wl, DEV, kv="fp8")
+    out, _, _ = _grouped_quant(c, spb=np.zeros(wl.batch, dtype=np.int32), tiles=np.zeros((0, 18), dtype=np.int32))
+    plain = pc.run_gpu(c).clone()
+    assert torch.equal(out, plain)
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "i8"])
+def test_prefix_cow_full_size_grouped_quant(fmt):
+    wl = workloads.prefix_cow()
+    c = pc.build(wl, DEV, kv=fmt)
+    out, spb, tiles = _grouped_quant(c)
+    assert len(tiles) == 4 and spb.min() == 32
+    err = pc.compare(c, out, record=f"config 3 prefix+CoW {fmt} cache grouped")
+    _log(f"prefix+CoW {fmt} grouped max err {err:.2e}")
+
+
+def test_quant_bad_prefix_block_gives_nan_and_refuses_f32_queries():
+    bs = 16
+    wl = workloads.custom([70, 70, 70, 90], num_heads=4, head_dim=64, dtype="f16", block_size=bs, seed=18,
+                          prefix_len=64, sharers=[0, 1, 2])
+    c = pc.build(wl, DEV, kv="i8")
+    ref = pc.oracle_out(c)
+    spb, tiles = pkv.prefix_tiles(c.tables_np, wl.seq_lens, bs)
+    assert spb.tolist() == [4, 4, 4, 0]
+    out, _, _ = _grouped_quant(c, spb=spb, tiles=tiles)
+    pc.compare(c, out, ref)
+    lead = int(tiles[0, 2])
+    bad_tables = c.tables_np.copy()
+    bad_tables[lead, 2] = wl.num_blocks + 1
+    c.tables = torch.from_numpy(bad_tables).to(DEV)
+    out, _, _ = _grouped_quant(c, spb=spb, tiles=tiles)
+    members = tiles[0, 2:2 + tiles[0, 1]].tolist()
+    assert torch.isnan(out[members].float()).all()
+    got = out[3].float().cpu().numpy()
+    assert np.all(np.abs(got - ref[3]) <= pc.tolerance(wl.dtype, ref[3]))
+    # f32 queries have no matrix-core path
+    q32 = c.q.float()
+    with pytest.raises(pkv.InvalidArgument):
+        pkv.pkv_attention_decode_grouped_quant(torch.empty_like(q32), q32, c.k_cache, c.v_cache, c.k_scales,
+                                               c.v_scales, c.tables, c.lens, wl.max_seq_len,
+                                               torch.from_numpy(spb).to(DEV), torch.from_numpy(tiles).to(DEV), "i8")
