@@ -60,7 +60,7 @@ os.environ.setdefault("HSA_ENABLE_SDMA", "0")
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, 8 TB/s
 METRIC = "paged-attn decode KV GB/s and % of MI355X HBM peak; tokens-steps/sec"
 KERNEL_SOURCES = [os.path.join(ROOT, "paged_attention_amd", "csrc", f)
-                  for f in ("decode_common.h", "kernels.hip", "kernels_q8.hip")]
+                  for f in ("decode_common.h", "prefix_common.h", "kernels.hip", "kernels_q8.hip")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
 
 

@@ -580,11 +580,6 @@ __device__ __forceinline__ void merge_pieces(const DecodeArgs& a, int bx, int v)
   constexpr int BATCH = RPW * kMergeRows;
   static_assert(BATCH <= 64, "a batch of pieces must fit one (m, l) per lane");
   static_assert(BATCH >= kPrefixPartsMax, "a shared prefix's parts fit one batch");
-  const int first = a.ws_plan[2 * v];
-  const int word = a.ws_plan[2 * v + 1];
-  const int count = word & kPlanCount;
-  const bool pre = GROUPED && (word & kPlanPrefix) != 0;
-  if (count == 0 && !pre) return;
   const int b = v % a.batch, y = v / a.batch;
   const int slice_lo = y * a.waves_per_group * a.heads_per_wave;
   const int slice_hi = min(a.num_heads, slice_lo + a.waves_per_group * a.heads_per_wave);
@@ -594,43 +589,29 @@ __device__ __forceinline__ void merge_pieces(const DecodeArgs& a, int bx, int v)
   const int grp = lane / LPR;
   const int sub = lane % LPR;
 
-  float mx = -INFINITY;   // running max over batches (wave-uniform)
-  float sum = 0.f;        // running sum, scaled to mx
-  float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-  // Folds states 0 .. n-1 (n <= BATCH): ml_at(i) = (m, l), row_at(i) = this
-  // lane's float4 of the weighted values.
-  auto fold = [&](int n, auto ml_at, auto row_at) {
-    // issue every load of the batch first
-    const float2 mine = lane < n ? ml_at(lane) : make_float2(-INFINITY, 0.f);
+  // A batch of states 0 .. n-1 (n <= BATCH): lane i holds state i's (m, l),
+  // the lane groups hold float4s of the weighted values.
+  struct Batch {
+    float2 mine;
     float4 rows[kMergeRows];
+  };
+  auto load_batch = [&](int n, auto ml_at, auto row_at) {
+    Batch bt;
+    bt.mine = lane < n ? ml_at(lane) : make_float2(-INFINITY, 0.f);
 #pragma unroll
     for (int k = 0; k < kMergeRows; ++k) {
       const int i = grp + k * RPW;
-      rows[k] = i < n ? row_at(i) : make_float4(0.f, 0.f, 0.f, 0.f);
+      bt.rows[k] = i < n ? row_at(i) : make_float4(0.f, 0.f, 0.f, 0.f);
     }
-    const float bmx = wave_max(mine.x);
-    const float nmx = fmaxf(mx, bmx);
-    const float rescale = __builtin_amdgcn_exp2f(mx - nmx);  // 0 on the first batch
-    const float w = lane < n ? __builtin_amdgcn_exp2f(mine.x - nmx) : 0.f;
-    sum = sum * rescale + wave_sum(mine.y * w);
-    o.x *= rescale;
-    o.y *= rescale;
-    o.z *= rescale;
-    o.w *= rescale;
-#pragma unroll
-    for (int k = 0; k < kMergeRows; ++k) {
-      const float wk = __shfl(w, grp + k * RPW, 64);
-      o.x = fmaf(rows[k].x, wk, o.x);
-      o.y = fmaf(rows[k].y, wk, o.y);
-      o.z = fmaf(rows[k].z, wk, o.z);
-      o.w = fmaf(rows[k].w, wk, o.w);
-    }
-    mx = nmx;
+    return bt;
   };
-  if (GROUPED && pre) {  // the shared prefix's parts: [part][prefix_batch][H][prefix_row] = acc[D], max, sum
-    const float* ps = a.prefix_state + (static_cast<int64_t>(b) * a.num_heads + h) * a.prefix_row;
-    const int64_t part_stride = static_cast<int64_t>(a.prefix_batch) * a.num_heads * a.prefix_row;
-    fold(
+  // GROUPED: the prefix parts' loads go out with the plan's (their addresses
+  // do not depend on it); they are used only if the plan marks a prefix.
+  const float* ps = a.prefix_state + (static_cast<int64_t>(b) * a.num_heads + h) * a.prefix_row;
+  const int64_t part_stride = static_cast<int64_t>(a.prefix_batch) * a.num_heads * a.prefix_row;
+  Batch pre_batch{};
+  if constexpr (GROUPED) {
+    pre_batch = load_batch(
         a.prefix_parts,
         [&](int i) {
           const float* p = ps + i * part_stride + D;
@@ -638,13 +619,45 @@ __device__ __forceinline__ void merge_pieces(const DecodeArgs& a, int bx, int v)
         },
         [&](int i) { return *reinterpret_cast<const float4*>(ps + i * part_stride + sub * 4); });
   }
+  const int first = a.ws_plan[2 * v];
+  const int word = a.ws_plan[2 * v + 1];
+  const int count = word & kPlanCount;
+  const bool pre = GROUPED && (word & kPlanPrefix) != 0;
+  if (count == 0 && !pre) return;
+
+  float mx = -INFINITY;   // running max over batches (wave-uniform)
+  float sum = 0.f;        // running sum, scaled to mx
+  float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+  auto fold = [&](int n, const Batch& bt) {
+    const float bmx = wave_max(bt.mine.x);
+    const float nmx = fmaxf(mx, bmx);
+    const float rescale = __builtin_amdgcn_exp2f(mx - nmx);  // 0 on the first batch
+    const float w = lane < n ? __builtin_amdgcn_exp2f(bt.mine.x - nmx) : 0.f;
+    sum = sum * rescale + wave_sum(bt.mine.y * w);
+    o.x *= rescale;
+    o.y *= rescale;
+    o.z *= rescale;
+    o.w *= rescale;
+#pragma unroll
+    for (int k = 0; k < kMergeRows; ++k) {
+      const float wk = __shfl(w, grp + k * RPW, 64);
+      o.x = fmaf(bt.rows[k].x, wk, o.x);
+      o.y = fmaf(bt.rows[k].y, wk, o.y);
+      o.z = fmaf(bt.rows[k].z, wk, o.z);
+      o.w = fmaf(bt.rows[k].w, wk, o.w);
+    }
+    mx = nmx;
+  };
+  if (pre) fold(a.prefix_parts, pre_batch);  // the shared prefix's parts first
   const float2* ml = a.ws_ml + static_cast<int64_t>(first) * a.num_heads + h;  // stride num_heads
   const float* accp = a.ws_acc + (static_cast<int64_t>(first) * a.num_heads + h) * D + sub * 4;
   const int64_t row_stride = static_cast<int64_t>(a.num_heads) * D;
-  for (int i0 = 0; i0 < count; i0 += BATCH)
-    fold(
-        min(BATCH, count - i0), [&](int i) { return ml[static_cast<int64_t>(i0 + i) * a.num_heads]; },
-        [&](int i) { return *reinterpret_cast<const float4*>(accp + static_cast<int64_t>(i0 + i) * row_stride); });
+  for (int i0 = 0; i0 < count; i0 += BATCH) {
+    const int n = min(BATCH, count - i0);
+    fold(n, load_batch(
+                n, [&](int i) { return ml[static_cast<int64_t>(i0 + i) * a.num_heads]; },
+                [&](int i) { return *reinterpret_cast<const float4*>(accp + static_cast<int64_t>(i0 + i) * row_stride); }));
+  }
 #pragma unroll
   for (int off = LPR; off < 64; off <<= 1) {
     o.x += __shfl_xor(o.x, off, 64);
