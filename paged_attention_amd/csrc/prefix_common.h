@@ -397,7 +397,8 @@ int run_grouped(DecodeArgs& a, int wg, void* out, const void* q, const int32_t* 
   const size_t need = grouped_workspace_bytes(batch, num_heads, head_dim, cache_dtype, wg);
   if (workspace_bytes < need)
     return pkv::fail(PKV_ERR_INVALID, "%s: workspace of %zu bytes needed, %zu given", what, need, workspace_bytes);
-  a.prefix_blocks = seq_prefix_blocks;
+  // no tiles: exactly the plain call's kernels
+  a.prefix_blocks = num_tiles > 0 ? seq_prefix_blocks : nullptr;
   a.prefix_state = reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                             workspace_layout(batch, num_heads, head_dim, cache_dtype, wg, true).total);
   a.prefix_row = head_dim + 4;
