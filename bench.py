@@ -92,8 +92,9 @@ def parse():
                    help="also update cumulative attention scores per cached token (16/32-bit caches; two launches "
                         "per layer)")
     p.add_argument("--grouped", action="store_true",
-                   help="decode with pkv_attention_decode_grouped[_quant]: shared prefixes read once per tile of "
-                        "sequences (three launches per layer)")
+                   help="decode with pkv_append_attention_decode_grouped[_quant] (with --separate: "
+                        "pkv_attention_decode_grouped[_quant] after pkv_append): shared prefixes read once per tile "
+                        "of sequences (prefix, decode and merge kernels)")
     p.add_argument("--separate", action="store_true",
                    help="scatter and attend in two launches per layer (pkv_append, pkv_attention_decode) instead "
                         "of one (pkv_append_attention_decode)")
@@ -561,7 +562,7 @@ def main():
     if args.grouped and (args.scores or wl.dtype not in ("f16", "bf16")):
         print("--grouped runs with fp16/bf16 queries and no scores", file=sys.stderr)
         sys.exit(2)
-    fused = not (args.separate or args.scores or args.grouped)
+    fused = not (args.separate or args.scores)
     timed_steps = -(-max(50, args.timed_calls) // NL)
     total_steps = args.warmup + args.steps + timed_steps
     # K/V bytes one token adds to one layer's cache (codes and scales for 8-bit)
@@ -707,7 +708,8 @@ def main():
                         qk["k_scales"], qk["v_scales"] = k_scales[l], v_scales[l]
                     calls_l.append(pkv.PreparedAppendDecode(out, q_all[0, l], k_new[0, l], v_new[0, l], k_caches[l],
                                                             v_caches[l], tb_t, ln_t, max_len, scale=wl.scale,
-                                                            work_groups=wgs, workspace=workspace, **qk))
+                                                            work_groups=wgs, workspace=workspace, prefix=prefix,
+                                                            **qk))
                 per_slot[key] = (None, calls_l)
             elif kv == "dense" and args.scores:
                 if not score_bufs:
@@ -891,8 +893,8 @@ def main():
         cpu = cpu_baseline(wl, rows, args.cpu_seconds, kv)
 
     ms_per_step = elapsed / args.steps * 1e3
-    call_name = ("pkv_attention_decode_grouped" + ("_quant" if kv != "dense" else "")
-                 + " (prefix_kernel + decode_kernel + decode_merge_kernel)"
+    call_name = (("pkv_append_attention_decode_grouped" if fused else "pkv_attention_decode_grouped")
+                 + ("_quant" if kv != "dense" else "") + " (prefix_kernel + decode_kernel + decode_merge_kernel)"
                  if prefix is not None else
                  "pkv_attention_decode_scores (decode_kernel + merge_score_kernel)" if args.scores else
                  ("pkv_append_attention_decode" if fused else "pkv_attention_decode")

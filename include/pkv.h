@@ -610,6 +610,37 @@ PKV_API int pkv_attention_decode_grouped_quant(void* out, const void* q, const v
                                                const int32_t* tiles, int32_t num_tiles, int32_t num_work_groups,
                                                void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Grouped decode with the step's new rows stored in the same launch: for
+ * every sequence b with L = seq_lens[b] >= 1, k_new[b] and v_new[b] (device
+ * [batch][num_heads][head_dim] of `dtype`) are stored at logical position
+ * L - 1 as pkv_append_attention_decode stores them, then attention runs as
+ * pkv_attention_decode_grouped.  A tile's prefix ends before each member's
+ * last block (pkv_prefix_tiles), so the rows stored never lie in a prefix
+ * the prefix kernel reads; the result, in `out` and in the pools, equals
+ * pkv_append followed by pkv_attention_decode_grouped.  A sequence whose
+ * length is invalid, or whose block for L - 1 is outside [0, num_blocks),
+ * writes nothing and gets NaN rows.  Every other argument is that of
+ * pkv_attention_decode_grouped. */
+PKV_API int pkv_append_attention_decode_grouped(void* out, const void* q, const void* k_new, const void* v_new,
+                                                void* k_cache, void* v_cache, const int32_t* block_tables,
+                                                int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                                                int32_t max_seq_len, int32_t batch, int32_t num_heads,
+                                                int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
+                                                pkv_dtype dtype, const int32_t* seq_prefix_blocks,
+                                                const int32_t* tiles, int32_t num_tiles, int32_t num_work_groups,
+                                                void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* pkv_append_attention_decode_grouped for an 8-bit cache: the new rows
+ * (k_new, v_new of q_dtype, 16-byte aligned) are quantised and stored with
+ * their scales as pkv_append_attention_decode_quant stores them, then
+ * attention runs as pkv_attention_decode_grouped_quant. */
+PKV_API int pkv_append_attention_decode_grouped_quant(
+    void* out, const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache, float* k_scales,
+    float* v_scales, const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* seq_lens,
+    int32_t max_seq_len, int32_t batch, int32_t num_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+    float scale, pkv_dtype q_dtype, pkv_dtype cache_dtype, const int32_t* seq_prefix_blocks, const int32_t* tiles,
+    int32_t num_tiles, int32_t num_work_groups, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

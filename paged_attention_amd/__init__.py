@@ -127,6 +127,13 @@ def _load():
         "pkv_append_attention_decode_quant": (ctypes.c_int, [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, i32, i32,
                                                              i32, i32, i32, i32, ctypes.c_float, ctypes.c_int,
                                                              ctypes.c_int, i32, vp, sz, vp]),
+        "pkv_append_attention_decode_grouped": (ctypes.c_int, [vp, vp, vp, vp, vp, vp, vp, i32, vp, i32, i32, i32,
+                                                               i32, i32, i32, ctypes.c_float, ctypes.c_int, vp, vp,
+                                                               i32, i32, vp, sz, vp]),
+        "pkv_append_attention_decode_grouped_quant": (ctypes.c_int, [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, i32,
+                                                                     i32, i32, i32, i32, i32, ctypes.c_float,
+                                                                     ctypes.c_int, ctypes.c_int, vp, vp, i32, i32, vp,
+                                                                     sz, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -952,30 +959,67 @@ def pkv_append_attention_decode_quant(out, q, k_new, v_new, k_cache, v_cache, k_
     _check(_lib.pkv_append_attention_decode_quant(*(args[:2] + _check_new_rows(k_new, v_new, q) + args[2:])))
 
 
+def pkv_append_attention_decode_grouped(out, q, k_new, v_new, k_cache, v_cache, block_tables, seq_lens,
+                                        max_seq_len, seq_prefix_blocks, tiles, scale=None, work_groups=0,
+                                        workspace=None, stream=None) -> None:
+    """pkv_append_attention_decode with shared prefixes read once per tile (f16 or bf16 caches)."""
+    if q.shape[0] == 0:
+        return
+    args, _ = _grouped_args(out, q, k_cache, v_cache, block_tables, seq_lens, max_seq_len, seq_prefix_blocks, tiles,
+                            scale, work_groups, workspace, stream)
+    _check(_lib.pkv_append_attention_decode_grouped(*(args[:2] + _check_new_rows(k_new, v_new, q) + args[2:])))
+
+
+def pkv_append_attention_decode_grouped_quant(out, q, k_new, v_new, k_cache, v_cache, k_scales, v_scales,
+                                              block_tables, seq_lens, max_seq_len, seq_prefix_blocks, tiles,
+                                              cache_dtype, scale=None, work_groups=0, workspace=None,
+                                              stream=None) -> None:
+    """pkv_append_attention_decode_grouped for an 8-bit cache (the new rows are quantised on the way in)."""
+    if q.shape[0] == 0:
+        return
+    args, _ = _grouped_quant_args(out, q, k_cache, v_cache, k_scales, v_scales, block_tables, seq_lens,
+                                  max_seq_len, seq_prefix_blocks, tiles, cache_dtype, scale, work_groups, workspace,
+                                  stream)
+    _check(_lib.pkv_append_attention_decode_grouped_quant(*(args[:2] + _check_new_rows(k_new, v_new, q) +
+                                                            args[2:])))
+
+
 class PreparedAppendDecode(PreparedDecode):
     """A pkv_append_attention_decode[_quant] call checked once.
 
     ``launch(q, k_new, v_new, out)`` swaps the per-step row pointers (same
     shapes and dtype as at preparation); ``set_metadata`` repoints the tables
     and lengths.  Pass ``k_scales``, ``v_scales`` and ``cache_dtype`` for an
-    8-bit cache.
+    8-bit cache, and ``prefix = (seq_prefix_blocks, tiles)`` for the grouped
+    call (pkv_append_attention_decode_grouped[_quant]).
     """
 
     def __init__(self, out, q, k_new, v_new, k_cache, v_cache, block_tables, seq_lens, max_seq_len, scale=None,
                  work_groups=0, workspace=None, stream=None, k_scales=None, v_scales=None,
-                 cache_dtype=None):  # noqa: D107
+                 cache_dtype=None, prefix=None):  # noqa: D107
         if cache_dtype is None:
-            args, ws = _decode_args(out, q, k_cache, v_cache, block_tables, seq_lens, max_seq_len, scale,
-                                    work_groups, workspace, stream)
-            self._fn = _lib.pkv_append_attention_decode
+            if prefix is None:
+                args, ws = _decode_args(out, q, k_cache, v_cache, block_tables, seq_lens, max_seq_len, scale,
+                                        work_groups, workspace, stream)
+                self._fn = _lib.pkv_append_attention_decode
+            else:
+                args, ws = _grouped_args(out, q, k_cache, v_cache, block_tables, seq_lens, max_seq_len, prefix[0],
+                                         prefix[1], scale, work_groups, workspace, stream)
+                self._fn = _lib.pkv_append_attention_decode_grouped
             self._ti = 6
         else:
-            args, ws = _decode_quant_args(out, q, k_cache, v_cache, k_scales, v_scales, block_tables, seq_lens,
-                                          max_seq_len, cache_dtype, scale, work_groups, workspace, stream)
-            self._fn = _lib.pkv_append_attention_decode_quant
+            if prefix is None:
+                args, ws = _decode_quant_args(out, q, k_cache, v_cache, k_scales, v_scales, block_tables, seq_lens,
+                                              max_seq_len, cache_dtype, scale, work_groups, workspace, stream)
+                self._fn = _lib.pkv_append_attention_decode_quant
+            else:
+                args, ws = _grouped_quant_args(out, q, k_cache, v_cache, k_scales, v_scales, block_tables, seq_lens,
+                                               max_seq_len, prefix[0], prefix[1], cache_dtype, scale, work_groups,
+                                               workspace, stream)
+                self._fn = _lib.pkv_append_attention_decode_grouped_quant
             self._ti = 8
         self._args = args[:2] + _check_new_rows(k_new, v_new, q) + args[2:]
-        self._keep = (k_cache, v_cache, k_scales, v_scales, block_tables, seq_lens, ws)
+        self._keep = (k_cache, v_cache, k_scales, v_scales, block_tables, seq_lens, ws, prefix)
         self._shape, self._dtype = tuple(q.shape), q.dtype
 
     def launch(self, q=None, k_new=None, v_new=None, out=None) -> None:
@@ -999,6 +1043,7 @@ __all__ = [
     "CACHE_FORMATS", "prefix_block_keys", "pkv_swap_blocks", "pkv_attention_decode_scores",
     "pkv_attention_decode_quant_scores", "pkv_decode_scores_workspace_bytes", "scores_workspace",
     "prefix_tiles", "pkv_attention_decode_grouped", "pkv_decode_grouped_workspace_bytes", "PREFIX_TILE_SEQS",
-    "pkv_attention_decode_grouped_quant",
+    "pkv_attention_decode_grouped_quant", "pkv_append_attention_decode_grouped",
+    "pkv_append_attention_decode_grouped_quant",
     "PREFIX_TILE_INTS", "pkv_append_attention_decode", "pkv_append_attention_decode_quant", "PreparedAppendDecode",
 ]

@@ -922,7 +922,7 @@ void launch_decode_g(const DecodeArgs& a, int wg, hipStream_t stream, const pkv:
 
 template <class KV, int D, int BS, int MODE>
 void launch_decode(const DecodeArgs& a, int wg, hipStream_t stream, const pkv::CallEvents& tm) {
-  if constexpr (MODE == kPlain && KV::kGrouped) {
+  if constexpr ((MODE == kPlain || MODE == kAppend) && KV::kGrouped) {
     if (a.prefix_blocks != nullptr) {
       launch_decode_g<KV, D, BS, MODE, true>(a, wg, stream, tm);
       return;

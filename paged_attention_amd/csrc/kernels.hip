@@ -129,13 +129,16 @@ int decode_dense(void* out, const void* q, const void* k_new, const void* v_new,
                     });
 }
 
-int decode_grouped(void* out, const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
-                   int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t max_seq_len, int32_t batch,
-                   int32_t num_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
-                   pkv_dtype dtype, const int32_t* seq_prefix_blocks, const int32_t* tiles, int32_t num_tiles,
-                   int32_t num_work_groups, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+// Both grouped entry points; k_new != nullptr selects the variant that first
+// stores each sequence's new row at its position L - 1 (never a prefix
+// position: a tile's prefix ends before every member's last block).
+int decode_grouped(void* out, const void* q, const void* k_new, const void* v_new, const void* k_cache,
+                   const void* v_cache, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                   const int32_t* seq_lens, int32_t max_seq_len, int32_t batch, int32_t num_heads, int32_t head_dim,
+                   int32_t block_size, int32_t num_blocks, float scale, pkv_dtype dtype,
+                   const int32_t* seq_prefix_blocks, const int32_t* tiles, int32_t num_tiles, int32_t num_work_groups,
+                   void* workspace, size_t workspace_bytes, hipStream_t stream, const char* what) {
   const pkv::CallEvents timing = pkv::take_call_events();  // consumed by this call, whatever its outcome
-  const char* what = "attention_decode_grouped";
   const int sz = check_grouped_sizes(what, batch, num_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
                                      max_seq_len, num_tiles);
   if (sz != PKV_OK) return sz;
@@ -151,6 +154,8 @@ int decode_grouped(void* out, const void* q, const void* k_cache, const void* v_
                                 batch, num_heads, head_dim, block_size, num_blocks, scale, dtype, num_work_groups,
                                 workspace, workspace_bytes, out, /*grouped=*/true);
   if (wg <= 0) return wg;
+  a.k_new = k_new;
+  a.v_new = v_new;
   const int64_t row = static_cast<int64_t>(num_heads) * head_dim * dtype_bytes(dtype);
   return run_grouped(
       a, wg, out, q, block_tables, max_blocks_per_seq, seq_lens, batch, num_heads, head_dim, dtype, row,
@@ -165,8 +170,13 @@ int decode_grouped(void* out, const void* q, const void* k_cache, const void* v_
         }
       },
       [&](const DecodeArgs& s, const pkv::CallEvents& tm) {
-        if (dtype == PKV_F16) launch_decode_m<DenseKV<PKV_F16>, kPlain>(s, wg, block_size, head_dim, stream, tm);
-        else launch_decode_m<DenseKV<PKV_BF16>, kPlain>(s, wg, block_size, head_dim, stream, tm);
+        if (k_new != nullptr) {
+          if (dtype == PKV_F16) launch_decode_m<DenseKV<PKV_F16>, kAppend>(s, wg, block_size, head_dim, stream, tm);
+          else launch_decode_m<DenseKV<PKV_BF16>, kAppend>(s, wg, block_size, head_dim, stream, tm);
+        } else {
+          if (dtype == PKV_F16) launch_decode_m<DenseKV<PKV_F16>, kPlain>(s, wg, block_size, head_dim, stream, tm);
+          else launch_decode_m<DenseKV<PKV_BF16>, kPlain>(s, wg, block_size, head_dim, stream, tm);
+        }
       });
 }
 
@@ -268,9 +278,28 @@ PKV_API int pkv_attention_decode_grouped(void* out, const void* q, const void* k
                                          float scale, pkv_dtype dtype, const int32_t* seq_prefix_blocks,
                                          const int32_t* tiles, int32_t num_tiles, int32_t num_work_groups,
                                          void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  return decode_grouped(out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, seq_lens, max_seq_len, batch,
-                        num_heads, head_dim, block_size, num_blocks, scale, dtype, seq_prefix_blocks, tiles, num_tiles,
-                        num_work_groups, workspace, workspace_bytes, stream);
+  return decode_grouped(out, q, nullptr, nullptr, k_cache, v_cache, block_tables, max_blocks_per_seq, seq_lens,
+                        max_seq_len, batch, num_heads, head_dim, block_size, num_blocks, scale, dtype,
+                        seq_prefix_blocks, tiles, num_tiles, num_work_groups, workspace, workspace_bytes, stream,
+                        "attention_decode_grouped");
+}
+
+PKV_API int pkv_append_attention_decode_grouped(void* out, const void* q, const void* k_new, const void* v_new,
+                                                void* k_cache, void* v_cache, const int32_t* block_tables,
+                                                int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                                                int32_t max_seq_len, int32_t batch, int32_t num_heads,
+                                                int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
+                                                pkv_dtype dtype, const int32_t* seq_prefix_blocks,
+                                                const int32_t* tiles, int32_t num_tiles, int32_t num_work_groups,
+                                                void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (batch > 0 && (!k_new || !v_new)) {
+    pkv::take_call_events();  // a pending timing request belongs to this call
+    return pkv::fail(PKV_ERR_INVALID, "append_attention_decode_grouped: null new rows");
+  }
+  return decode_grouped(out, q, k_new, v_new, k_cache, v_cache, block_tables, max_blocks_per_seq, seq_lens,
+                        max_seq_len, batch, num_heads, head_dim, block_size, num_blocks, scale, dtype,
+                        seq_prefix_blocks, tiles, num_tiles, num_work_groups, workspace, workspace_bytes, stream,
+                        "append_attention_decode_grouped");
 }
 
 PKV_API int32_t pkv_decode_work_groups(pkv_dtype cache_dtype) {

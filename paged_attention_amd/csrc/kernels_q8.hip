@@ -409,15 +409,16 @@ void launch_prefix_q8(const DecodeArgs& pa, int32_t bs, int32_t d, const int32_t
   else launch_prefix<PrefixQ8<Q, K>, 128>(pa, bs, tiles, num_tiles, stream, start);
 }
 
-int decode_grouped_q8(void* out, const void* q, const void* k_cache, const void* v_cache, const float* k_scales,
-                      const float* v_scales, const int32_t* block_tables, int32_t max_blocks_per_seq,
-                      const int32_t* seq_lens, int32_t max_seq_len, int32_t batch, int32_t num_heads,
-                      int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale, pkv_dtype q_dtype,
-                      pkv_dtype cache_dtype, const int32_t* seq_prefix_blocks, const int32_t* tiles,
-                      int32_t num_tiles, int32_t num_work_groups, void* workspace, size_t workspace_bytes,
-                      hipStream_t stream) {
+// Both 8-bit grouped entry points; k_new != nullptr selects the variant that
+// first quantises and stores each sequence's new row at its position L - 1.
+int decode_grouped_q8(void* out, const void* q, const void* k_new, const void* v_new, const void* k_cache,
+                      const void* v_cache, const float* k_scales, const float* v_scales, const int32_t* block_tables,
+                      int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t max_seq_len, int32_t batch,
+                      int32_t num_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
+                      pkv_dtype q_dtype, pkv_dtype cache_dtype, const int32_t* seq_prefix_blocks,
+                      const int32_t* tiles, int32_t num_tiles, int32_t num_work_groups, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream, const char* what) {
   const pkv::CallEvents timing = pkv::take_call_events();  // consumed by this call, whatever its outcome
-  const char* what = "attention_decode_grouped_quant";
   const int sz = check_grouped_sizes(what, batch, num_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
                                      max_seq_len, num_tiles);
   if (sz != PKV_OK) return sz;
@@ -440,6 +441,8 @@ int decode_grouped_q8(void* out, const void* q, const void* k_cache, const void*
   if (wg <= 0) return wg;
   a.k_scales = const_cast<float*>(k_scales);
   a.v_scales = const_cast<float*>(v_scales);
+  a.k_new = k_new;
+  a.v_new = v_new;
   const int64_t row = static_cast<int64_t>(num_heads) * head_dim * dtype_bytes(q_dtype);
   const bool fp8 = cache_dtype == PKV_FP8_E4M3;
   return run_grouped(
@@ -455,12 +458,22 @@ int decode_grouped_q8(void* out, const void* q, const void* k_cache, const void*
         }
       },
       [&](const DecodeArgs& s, const pkv::CallEvents& tm) {
-        if (q_dtype == PKV_F16) {
-          if (fp8) launch_decode_m<Q8KV<PKV_F16, PKV_FP8_E4M3>, kPlain>(s, wg, block_size, head_dim, stream, tm);
-          else launch_decode_m<Q8KV<PKV_F16, PKV_I8>, kPlain>(s, wg, block_size, head_dim, stream, tm);
+        if (k_new != nullptr) {
+          if (q_dtype == PKV_F16) {
+            if (fp8) launch_decode_m<Q8KV<PKV_F16, PKV_FP8_E4M3>, kAppend>(s, wg, block_size, head_dim, stream, tm);
+            else launch_decode_m<Q8KV<PKV_F16, PKV_I8>, kAppend>(s, wg, block_size, head_dim, stream, tm);
+          } else {
+            if (fp8) launch_decode_m<Q8KV<PKV_BF16, PKV_FP8_E4M3>, kAppend>(s, wg, block_size, head_dim, stream, tm);
+            else launch_decode_m<Q8KV<PKV_BF16, PKV_I8>, kAppend>(s, wg, block_size, head_dim, stream, tm);
+          }
         } else {
-          if (fp8) launch_decode_m<Q8KV<PKV_BF16, PKV_FP8_E4M3>, kPlain>(s, wg, block_size, head_dim, stream, tm);
-          else launch_decode_m<Q8KV<PKV_BF16, PKV_I8>, kPlain>(s, wg, block_size, head_dim, stream, tm);
+          if (q_dtype == PKV_F16) {
+            if (fp8) launch_decode_m<Q8KV<PKV_F16, PKV_FP8_E4M3>, kPlain>(s, wg, block_size, head_dim, stream, tm);
+            else launch_decode_m<Q8KV<PKV_F16, PKV_I8>, kPlain>(s, wg, block_size, head_dim, stream, tm);
+          } else {
+            if (fp8) launch_decode_m<Q8KV<PKV_BF16, PKV_FP8_E4M3>, kPlain>(s, wg, block_size, head_dim, stream, tm);
+            else launch_decode_m<Q8KV<PKV_BF16, PKV_I8>, kPlain>(s, wg, block_size, head_dim, stream, tm);
+          }
         }
       });
 }
@@ -478,10 +491,27 @@ PKV_API int pkv_attention_decode_grouped_quant(void* out, const void* q, const v
                                                pkv_dtype cache_dtype, const int32_t* seq_prefix_blocks,
                                                const int32_t* tiles, int32_t num_tiles, int32_t num_work_groups,
                                                void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  return decode_grouped_q8(out, q, k_cache, v_cache, k_scales, v_scales, block_tables, max_blocks_per_seq, seq_lens,
-                           max_seq_len, batch, num_heads, head_dim, block_size, num_blocks, scale, q_dtype,
-                           cache_dtype, seq_prefix_blocks, tiles, num_tiles, num_work_groups, workspace,
-                           workspace_bytes, stream);
+  return decode_grouped_q8(out, q, nullptr, nullptr, k_cache, v_cache, k_scales, v_scales, block_tables,
+                           max_blocks_per_seq, seq_lens, max_seq_len, batch, num_heads, head_dim, block_size,
+                           num_blocks, scale, q_dtype, cache_dtype, seq_prefix_blocks, tiles, num_tiles,
+                           num_work_groups, workspace, workspace_bytes, stream, "attention_decode_grouped_quant");
+}
+
+PKV_API int pkv_append_attention_decode_grouped_quant(
+    void* out, const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache, float* k_scales,
+    float* v_scales, const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* seq_lens,
+    int32_t max_seq_len, int32_t batch, int32_t num_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+    float scale, pkv_dtype q_dtype, pkv_dtype cache_dtype, const int32_t* seq_prefix_blocks, const int32_t* tiles,
+    int32_t num_tiles, int32_t num_work_groups, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  const char* what = "append_attention_decode_grouped_quant";
+  if (batch > 0 && (!k_new || !v_new || !aligned16(k_new) || !aligned16(v_new))) {
+    pkv::take_call_events();  // a pending timing request belongs to this call
+    return pkv::fail(PKV_ERR_INVALID, "%s: new rows must be non-null and 16-byte aligned", what);
+  }
+  return decode_grouped_q8(out, q, k_new, v_new, k_cache, v_cache, k_scales, v_scales, block_tables,
+                           max_blocks_per_seq, seq_lens, max_seq_len, batch, num_heads, head_dim, block_size,
+                           num_blocks, scale, q_dtype, cache_dtype, seq_prefix_blocks, tiles, num_tiles,
+                           num_work_groups, workspace, workspace_bytes, stream, what);
 }
 
 PKV_API int pkv_append_quant(const void* k_new, const void* v_new, int32_t num_tokens, const int64_t* slot_mapping,

@@ -113,6 +113,30 @@ def test_device_calls_reject_bad_shapes_before_launch():
     assert lib.pkv_copy_blocks(None, None, 1, null, 0, 8, 4096, null) == pkv.PKV_OK
 
 
+def test_fused_grouped_calls_reject_bad_arguments_before_launch():
+    lib = pkv._lib
+    null = ctypes.c_void_p(0)
+    odd = ctypes.c_void_p(0x1008)   # never dereferenced: rejected first
+    f16, f32, fp8 = pkv.PKV_F16, pkv.PKV_F32, pkv.PKV_FP8_E4M3
+
+    def dense(batch=1, dt=f16, rows=null):
+        return lib.pkv_append_attention_decode_grouped(odd, odd, rows, rows, odd, odd, odd, 4, odd, 64, batch, 4, 128,
+                                                       16, 8, 1.0, dt, odd, null, 0, 0, null, 0, null)
+
+    assert dense() == pkv.PKV_ERR_INVALID                   # null new rows
+    assert dense(rows=odd, dt=f32) == pkv.PKV_ERR_INVALID   # grouped decode runs on f16 / bf16 caches
+    assert dense(batch=0) == pkv.PKV_OK
+
+    def quant(batch=1, qdt=f16, rows=null):
+        return lib.pkv_append_attention_decode_grouped_quant(odd, odd, rows, rows, odd, odd, odd, odd, odd, 4, odd, 64,
+                                                             batch, 4, 128, 16, 8, 1.0, qdt, fp8, odd, null, 0, 0,
+                                                             null, 0, null)
+
+    assert quant() == pkv.PKV_ERR_INVALID                   # null new rows
+    assert quant(rows=odd) == pkv.PKV_ERR_INVALID           # misaligned new rows
+    assert quant(batch=0) == pkv.PKV_OK
+
+
 def test_quant_calls_reject_bad_arguments_before_launch():
     lib = pkv._lib
     null = ctypes.c_void_p(0)

@@ -213,3 +213,79 @@ def test_quant_bad_prefix_block_gives_nan_and_refuses_f32_queries():
         pkv.pkv_attention_decode_grouped_quant(torch.empty_like(q32), q32, c.k_cache, c.v_cache, c.k_scales,
                                                c.v_scales, c.tables, c.lens, wl.max_seq_len,
                                                torch.from_numpy(spb).to(DEV), torch.from_numpy(tiles).to(DEV), "i8")
+
+
+# ---- scatter + grouped decode in one launch ----------------------------------
+# (pkv_append_attention_decode_grouped[_quant]).  As for the ungrouped fused
+# call: the slot of each sequence's newest token is poisoned, the fused call
+# stores the row again, and the pools must come back bit-identical to the
+# oracle's; the output meets the decode bound and equals the separate grouped
+# call (same kernels and schedule) bit for bit.
+
+from tests.test_gpu_fused import _assert_pools, _poison_newest  # noqa: E402
+
+
+def _grouped_fused(c, work_groups, spb, tiles):
+    kn = pc.to_device(c.dec_k, c.wl.dtype, DEV)
+    vn = pc.to_device(c.dec_v, c.wl.dtype, DEV)
+    out = torch.empty_like(c.q)
+    spb_d = torch.from_numpy(np.ascontiguousarray(spb)).to(DEV)
+    tiles_d = torch.from_numpy(np.ascontiguousarray(tiles)).to(DEV)
+    if c.kv == "dense":
+        pkv.pkv_append_attention_decode_grouped(out, c.q, kn, vn, c.k_cache, c.v_cache, c.tables, c.lens,
+                                                c.wl.max_seq_len, spb_d, tiles_d, scale=c.wl.scale,
+                                                work_groups=work_groups)
+    else:
+        pkv.pkv_append_attention_decode_grouped_quant(out, c.q, kn, vn, c.k_cache, c.v_cache, c.k_scales, c.v_scales,
+                                                      c.tables, c.lens, c.wl.max_seq_len, spb_d, tiles_d, c.kv,
+                                                      scale=c.wl.scale, work_groups=work_groups)
+    torch.cuda.synchronize()
+    return out
+
+
+FUSED_CASES = [("dense", "f16", 128, 16), ("dense", "bf16", 64, 8), ("dense", "f16", 64, 32),
+               ("i8", "f16", 128, 16), ("fp8", "bf16", 128, 8), ("fp8", "f16", 64, 32)]
+
+
+@pytest.mark.parametrize("kv,dtype,head_dim,block_size", FUSED_CASES)
+def test_fused_grouped_matches_oracle_and_separate_calls(kv, dtype, head_dim, block_size):
+    wl = workloads.custom(LENS, num_heads=5, head_dim=head_dim, dtype=dtype, block_size=block_size,
+                          seed=head_dim + block_size + 2, prefix_len=40, sharers=SHARERS)
+    c = pc.build(wl, DEV, kv=kv)
+    ref = pc.oracle_out(c)
+    spb, tiles = pkv.prefix_tiles(c.tables_np, wl.seq_lens, block_size)
+    assert len(tiles) == 1 and spb[SHARERS].min() == 40 // block_size
+    separate = (_grouped(c, 0, spb, tiles) if kv == "dense" else _grouped_quant(c, 0, spb, tiles))[0].clone()
+    for wg in (0, 3, 50):
+        _poison_newest(c)
+        out = _grouped_fused(c, wg, spb, tiles)
+        _assert_pools(c)
+        pc.compare(c, out, ref)
+        if wg == 0:
+            assert torch.equal(out.view(torch.uint8), separate.view(torch.uint8))
+
+
+@pytest.mark.parametrize("kv", ["dense", "fp8"])
+def test_fused_grouped_prefix_cow_full_size(kv):
+    wl = workloads.prefix_cow()
+    c = pc.build(wl, DEV, kv=kv)
+    ref = pc.oracle_out(c)
+    spb, tiles = pkv.prefix_tiles(c.tables_np, wl.seq_lens, wl.block_size)
+    assert len(tiles) == 4 and spb.min() == 32
+    _poison_newest(c)
+    out = _grouped_fused(c, 0, spb, tiles)
+    _assert_pools(c)
+    err = pc.compare(c, out, ref, record=f"config 3 prefix+CoW {kv} cache grouped, append fused")
+    _log(f"prefix+CoW {kv} fused grouped max err {err:.2e}")
+
+
+def test_fused_grouped_refuses_missing_rows():
+    wl = workloads.custom([70, 70, 90], num_heads=4, head_dim=64, dtype="f16", block_size=16, seed=19,
+                          prefix_len=64, sharers=[0, 1])
+    c = pc.build(wl, DEV)
+    spb, tiles = pkv.prefix_tiles(c.tables_np, wl.seq_lens, 16)
+    out = torch.empty_like(c.q)
+    spb_d, tiles_d = torch.from_numpy(spb).to(DEV), torch.from_numpy(tiles).to(DEV)
+    with pytest.raises(pkv.InvalidArgument):
+        pkv.pkv_append_attention_decode_grouped(out, c.q, c.q[:, :2], c.q[:, :2], c.k_cache, c.v_cache, c.tables,
+                                                c.lens, wl.max_seq_len, spb_d, tiles_d)
