@@ -205,6 +205,7 @@ __device__ __forceinline__ float wave_sum(float x) {
 // positions, so the result does not depend on where blocks sit physically.
 
 constexpr int kMaxVirtual = 5460;   // sequences x head slices per launch (the LDS arrays: 3 x (5460 + 1) int32 <= 64 KiB)
+constexpr int kMaxVirtualGrouped = 4095;  // the same for a grouped launch, which also stages the prefix blocks in LDS
 constexpr int kTableWindow = 64;    // block ids held in registers at a time (one per lane)
 constexpr int kMergeWaves = 4;      // heads per merge work-group
 constexpr int32_t kPlanPrefix = 1 << 30;  // plan flag: the sequence has a shared prefix's partial states
@@ -300,16 +301,13 @@ __device__ __forceinline__ bool length_ok(int L, const DecodeArgs& a) {
   return L >= 0 && L <= a.max_seq_len && static_cast<int64_t>(L) <= static_cast<int64_t>(a.max_blocks) * BS;
 }
 
-// First logical position the decode kernel attends for sequence b of valid
-// length L: in a grouped call, the end of a shared prefix shorter than L
-// (the prefix itself is attended by prefix_kernel, whose partial states the
-// merge kernel folds in); else 0.  Compiled only for formats with a grouped
-// entry point (GROUPED).
-template <int BS, bool GROUPED>
-__device__ __forceinline__ int suffix_start(int b, int L, const DecodeArgs& a) {
-  if (!GROUPED || a.prefix_blocks == nullptr) return 0;
-  const int64_t p = a.prefix_blocks[b];
-  return p > 0 && p * BS < L ? static_cast<int>(p * BS) : 0;
+// First logical position the decode kernel attends for a sequence of valid
+// length L in a grouped call: the end of a shared prefix of prefix_blocks
+// blocks if it is shorter than L (the prefix itself is attended by
+// prefix_kernel, whose partial states the merge kernel folds in); else 0.
+template <int BS>
+__device__ __forceinline__ int suffix_start(int64_t prefix_blocks, int L) {
+  return prefix_blocks > 0 && prefix_blocks * BS < L ? static_cast<int>(prefix_blocks * BS) : 0;
 }
 
 // Scaled logits (score variant) leave the decode kernel in whole 128-byte
@@ -397,16 +395,24 @@ __global__ void __launch_bounds__(KV::kMaxWaves * 64) decode_kernel(DecodeArgs a
   int32_t* s_pref = s_dyn;           // [nv + 1]: first chunk of each virtual sequence
   int32_t* s_part = s_dyn + nv + 1;  // [nv + 1]: first partial slot of each virtual sequence
   int32_t* s_len = s_part + nv + 1;  // [batch]: the lengths, read once (they may be host memory)
+  int32_t* s_pblk = s_len + a.batch;  // GROUPED, [batch]: shared-prefix blocks, read with the lengths
   const int g = blockIdx.x;
 
   // 1. chunk counts of every (head slice, sequence); bad lengths count zero.
-  for (int b = threadIdx.x; b < a.batch; b += blockDim.x) s_len[b] = a.lens[b];
+  for (int b = threadIdx.x; b < a.batch; b += blockDim.x) {
+    s_len[b] = a.lens[b];
+    if constexpr (GROUPED) s_pblk[b] = a.prefix_blocks[b];
+  }
   __syncthreads();
+  auto start_of = [&](int b, int L) -> int {  // first attended position (L valid)
+    if constexpr (GROUPED) return suffix_start<BS>(s_pblk[b], L);
+    return 0;
+  };
   block_exclusive_scan(
       [&](int v) {
         const int b = v % a.batch;
         const int L = s_len[b];
-        return length_ok<BS>(L, a) ? (L - suffix_start<BS, GROUPED>(b, L, a) + kChunk - 1) / kChunk : 0;
+        return length_ok<BS>(L, a) ? (L - start_of(b, L) + kChunk - 1) / kChunk : 0;
       },
       nv, s_pref, s_waves);
   const int64_t total = s_pref[nv];
@@ -418,7 +424,7 @@ __global__ void __launch_bounds__(KV::kMaxWaves * 64) decode_kernel(DecodeArgs a
   auto prefixed = [&](int v) -> bool {
     const int b = v % a.batch;
     const int L = s_len[b];
-    return length_ok<BS>(L, a) && suffix_start<BS, GROUPED>(b, L, a) > 0;
+    return length_ok<BS>(L, a) && start_of(b, L) > 0;
   };
   auto pieces = [&](int v) -> int32_t {
     const int64_t c0 = s_pref[v], c1 = s_pref[v + 1];
@@ -485,7 +491,7 @@ __global__ void __launch_bounds__(KV::kMaxWaves * 64) decode_kernel(DecodeArgs a
       const Elem* kp = static_cast<const Elem*>(a.k) + e0 * KB;
       const Elem* vp = static_cast<const Elem*>(a.v) + e0 * KB;
       const int L = s_len[b];
-      const int start = suffix_start<BS, GROUPED>(b, L, a);
+      const int start = start_of(b, L);
       const int t_begin = start + static_cast<int>(cur - seq0) * kChunk;
       const int t_end = min(L, start + static_cast<int>(seg_end - seq0) * kChunk);
       const int32_t* trow = a.tables + static_cast<int64_t>(b) * a.max_blocks;
@@ -905,7 +911,8 @@ inline Layout workspace_layout(int32_t batch, int32_t num_heads, int32_t head_di
 // GROUPED: a grouped call (shared prefixes attended by the prefix kernel).
 template <class KV, int D, int BS, int MODE, bool GROUPED>
 void launch_decode_g(const DecodeArgs& a, int wg, hipStream_t stream, const pkv::CallEvents& tm) {
-  const size_t lds = (2 * (static_cast<size_t>(a.batch) * a.groups_y + 1) + a.batch) * sizeof(int32_t);
+  const size_t lds = (2 * (static_cast<size_t>(a.batch) * a.groups_y + 1) + a.batch * (GROUPED ? 2 : 1)) *
+                    sizeof(int32_t);
   const bool scores = MODE == kScores && a.max_seq_len > 0;
   hipExtLaunchKernelGGL((decode_kernel<KV, D, BS, MODE, GROUPED>), dim3(wg), dim3(a.waves_per_group * 64), lds,
                         stream, tm.start, nullptr, 0, a);
@@ -1067,7 +1074,7 @@ int run_sliced(const DecodeArgs& base, void* out, const void* q, const int32_t* 
                int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t batch, int64_t q_row_bytes,
                const pkv::CallEvents& timing, Launch launch) {
   DecodeArgs a = base;
-  const int32_t per_launch = kMaxVirtual / a.groups_y;
+  const int32_t per_launch = (base.prefix_blocks != nullptr ? kMaxVirtualGrouped : kMaxVirtual) / a.groups_y;
   for (int32_t b0 = 0; b0 < batch; b0 += per_launch) {
     const pkv::CallEvents tm{b0 == 0 ? timing.start : nullptr,
                              b0 + per_launch >= batch ? timing.stop : nullptr};
