@@ -289,3 +289,27 @@ def test_fused_grouped_refuses_missing_rows():
     with pytest.raises(pkv.InvalidArgument):
         pkv.pkv_append_attention_decode_grouped(out, c.q, c.q[:, :2], c.q[:, :2], c.k_cache, c.v_cache, c.tables,
                                                 c.lens, wl.max_seq_len, spb_d, tiles_d)
+
+
+def test_fused_grouped_bad_block_writes_nothing():
+    # A member whose block for position L - 1 is outside the pool stores
+    # nothing and gets a NaN row; the other sequences, grouped or not, are
+    # unaffected and rewrite their newest rows with the same bytes.
+    bs = 16
+    wl = workloads.custom([70, 70, 70, 90], num_heads=4, head_dim=64, dtype="f16", block_size=bs, seed=23,
+                          prefix_len=64, sharers=[0, 1, 2])
+    c = pc.build(wl, DEV)
+    ref = pc.oracle_out(c)
+    spb, tiles = pkv.prefix_tiles(c.tables_np, wl.seq_lens, bs)
+    assert spb.tolist() == [4, 4, 4, 0]
+    tables = c.tables.clone()
+    tables[1, (70 - 1) // bs] = wl.num_blocks + 3
+    c.tables = tables
+    before_k, before_v = c.k_cache.clone(), c.v_cache.clone()
+    out = _grouped_fused(c, 0, spb, tiles)
+    assert torch.isnan(out[1].float()).all()
+    others = [0, 2, 3]
+    got = out[others].float().cpu().numpy()
+    assert np.all(np.abs(got - ref[others]) <= pc.tolerance(wl.dtype, ref[others]))
+    assert torch.equal(c.k_cache.view(torch.int16), before_k.view(torch.int16))
+    assert torch.equal(c.v_cache.view(torch.int16), before_v.view(torch.int16))
