@@ -576,8 +576,10 @@ PKV_API size_t pkv_decode_grouped_workspace_bytes(int32_t batch, int32_t num_hea
  * longer than its prefix, is attended as an ungrouped sequence (with the
  * plain call's handling of refused lengths); out-of-range sequence indices
  * in a tile are skipped.  A prefix block id outside [0, num_blocks) makes
- * the tile's members NaN.  Every other argument is that of
- * pkv_attention_decode; workspace: pkv_decode_grouped_workspace_bytes. */
+ * the tile's members NaN.  With num_tiles = 0 the call runs
+ * pkv_attention_decode's kernels (seq_prefix_blocks is not read).  Every
+ * other argument is that of pkv_attention_decode; workspace:
+ * pkv_decode_grouped_workspace_bytes. */
 PKV_API int pkv_attention_decode_grouped(void* out, const void* q, const void* k_cache, const void* v_cache,
                                          const int32_t* block_tables, int32_t max_blocks_per_seq,
                                          const int32_t* seq_lens, int32_t max_seq_len, int32_t batch,
