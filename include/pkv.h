@@ -37,6 +37,10 @@
  *     block * block_size + pos % block_size.
  *   - Supported shapes: head_dim 64 or 128; block_size 8, 16 or 32; dtype
  *     f32, f16 or bf16.  Anything else returns PKV_ERR_INVALID.
+ *   - Pools, K/V rows, queries, outputs and scale pools are moved 16 bytes
+ *     per lane: their base addresses must be 16-byte aligned (any device
+ *     allocation is).  Calls check this on the host and return
+ *     PKV_ERR_INVALID before enqueueing anything.
  *   - The allocator is not thread-safe; callers serialise access to one
  *     allocator.  Device operations are reentrant.
  *   - Device-side indices are always range-checked, in every build: a block

@@ -113,6 +113,8 @@ PKV_API int pkv_append(const void* k_new, const void* v_new, int32_t num_tokens,
                      static_cast<int>(dtype));
   if (num_tokens == 0) return PKV_OK;
   if (!k_new || !v_new || !slot_mapping || !k_cache || !v_cache) return pkv::fail(PKV_ERR_INVALID, "append: null pointer");
+  if (!pkv::aligned16(k_new) || !pkv::aligned16(v_new) || !pkv::aligned16(k_cache) || !pkv::aligned16(v_cache))
+    return pkv::fail(PKV_ERR_INVALID, "append: rows and pools must be 16-byte aligned");
   const int64_t row_vec = static_cast<int64_t>(num_heads) * head_dim * dtype_bytes(dtype) / 16;
   const int64_t total = static_cast<int64_t>(num_tokens) * row_vec;
   const int64_t blocks = (total + 255) / 256;
@@ -132,11 +134,13 @@ PKV_API int pkv_copy_blocks(void* const* k_caches, void* const* v_caches, int32_
   if (n_pairs == 0 || num_layers == 0) return PKV_OK;
   if (!k_caches || !v_caches || !pairs) return pkv::fail(PKV_ERR_INVALID, "copy_blocks: null pointer");
   if (n_pairs > 0x7fffffff / 2) return pkv::fail(PKV_ERR_INVALID, "copy_blocks: too many pairs");
+  for (int32_t l = 0; l < num_layers; ++l)  // every pool before any launch: nothing is copied on an error
+    if (!k_caches[l] || !v_caches[l] || !pkv::aligned16(k_caches[l]) || !pkv::aligned16(v_caches[l]))
+      return pkv::fail(PKV_ERR_INVALID, "copy_blocks: layer %d's pools must be non-null and 16-byte aligned", l);
   for (int32_t l0 = 0; l0 < num_layers; l0 += kCopyLayers) {
     const int32_t nl = num_layers - l0 < kCopyLayers ? num_layers - l0 : kCopyLayers;
     LayerPtrs ptrs{};
     for (int32_t i = 0; i < nl; ++i) {
-      if (!k_caches[l0 + i] || !v_caches[l0 + i]) return pkv::fail(PKV_ERR_INVALID, "copy_blocks: null layer pool");
       ptrs.k[i] = static_cast<Vec16*>(k_caches[l0 + i]);
       ptrs.v[i] = static_cast<Vec16*>(v_caches[l0 + i]);
     }

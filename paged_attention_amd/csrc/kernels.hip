@@ -109,6 +109,9 @@ int decode_dense(void* out, const void* q, const void* k_new, const void* v_new,
   const int st = check_decode_scalars(scale, num_work_groups);
   if (st != PKV_OK) return st;
   if (batch == 0) return PKV_OK;
+  if (!pkv::aligned16(q) || !pkv::aligned16(out) || !pkv::aligned16(k_cache) || !pkv::aligned16(v_cache) ||
+      !pkv::aligned16(k_new) || !pkv::aligned16(v_new))
+    return pkv::fail(PKV_ERR_INVALID, "%s: q, out, pools and new rows must be 16-byte aligned", what);
   DecodeArgs a;
   const int wg = prepare_decode(a, q, k_cache, v_cache, block_tables, max_blocks_per_seq, seq_lens, max_seq_len,
                                 batch, num_heads, head_dim, block_size, num_blocks, scale, dtype, num_work_groups,
@@ -149,6 +152,9 @@ int decode_grouped(void* out, const void* q, const void* k_new, const void* v_ne
   if (batch == 0) return PKV_OK;
   if (!seq_prefix_blocks || (num_tiles > 0 && !tiles))
     return pkv::fail(PKV_ERR_INVALID, "%s: null prefix arrays", what);
+  if (!pkv::aligned16(q) || !pkv::aligned16(out) || !pkv::aligned16(k_cache) || !pkv::aligned16(v_cache) ||
+      !pkv::aligned16(k_new) || !pkv::aligned16(v_new))
+    return pkv::fail(PKV_ERR_INVALID, "%s: q, out, pools and new rows must be 16-byte aligned", what);
   DecodeArgs a;
   const int wg = prepare_decode(a, q, k_cache, v_cache, block_tables, max_blocks_per_seq, seq_lens, max_seq_len,
                                 batch, num_heads, head_dim, block_size, num_blocks, scale, dtype, num_work_groups,

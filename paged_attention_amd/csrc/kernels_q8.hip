@@ -332,7 +332,7 @@ struct PrefixQ8 {
   __device__ static const float* v_scales(const DecodeArgs& a) { return a.v_scales; }
 };
 
-bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+using pkv::aligned16;
 
 template <int ST, int KT>
 void launch_append_q8(int32_t head_dim, dim3 grid, hipStream_t stream, const void* k_new, const void* v_new,

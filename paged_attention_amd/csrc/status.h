@@ -2,10 +2,15 @@
 #pragma once
 
 #include <cstdarg>
+#include <cstdint>
 
 #include "pkv.h"
 
 namespace pkv {
+
+// Rows, pools and queries are moved 16 bytes per lane: their base addresses
+// must be 16-byte aligned (null counts as aligned; callers check it apart).
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // Records a formatted detail for pkv_last_error() and returns `status`.
 int fail(int status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));

@@ -113,6 +113,32 @@ def test_device_calls_reject_bad_shapes_before_launch():
     assert lib.pkv_copy_blocks(None, None, 1, null, 0, 8, 4096, null) == pkv.PKV_OK
 
 
+def test_misaligned_rows_and_pools_are_refused_before_launch():
+    # Kernels move 16 bytes per lane; odd addresses (never dereferenced)
+    # must be refused on the host.
+    lib = pkv._lib
+    null = ctypes.c_void_p(0)
+    odd, even = ctypes.c_void_p(0x1008), ctypes.c_void_p(0x1000)
+    f16 = pkv.PKV_F16
+
+    def decode(q=even, pool=even):
+        return lib.pkv_attention_decode(even, q, pool, pool, even, 4, even, 64, 1, 4, 128, 16, 8, 1.0, f16, 8, null,
+                                        0, null)
+
+    assert decode(q=odd) == pkv.PKV_ERR_INVALID
+    assert b"16-byte aligned" in lib.pkv_last_error()
+    assert decode(pool=odd) == pkv.PKV_ERR_INVALID
+    assert b"16-byte aligned" in lib.pkv_last_error()
+    assert decode() == pkv.PKV_ERR_INVALID                  # aligned, but no workspace
+    assert b"workspace" in lib.pkv_last_error()
+    assert lib.pkv_append(odd, even, 3, even, even, even, 8, 16, 4, 128, f16, null) == pkv.PKV_ERR_INVALID
+    assert lib.pkv_append(even, even, 3, even, odd, even, 8, 16, 4, 128, f16, null) == pkv.PKV_ERR_INVALID
+    pools_ok = (ctypes.c_void_p * 2)(0x1000, 0x2000)
+    pools_odd = (ctypes.c_void_p * 2)(0x1000, 0x2008)
+    st = lib.pkv_copy_blocks(pools_ok, pools_odd, 2, even, 1, 8, 4096, null)
+    assert st == pkv.PKV_ERR_INVALID and b"layer 1" in lib.pkv_last_error()
+
+
 def test_fused_grouped_calls_reject_bad_arguments_before_launch():
     lib = pkv._lib
     null = ctypes.c_void_p(0)
