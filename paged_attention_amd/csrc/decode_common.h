@@ -252,10 +252,55 @@ struct DecodeArgs {
 };
 
 // Exclusive prefix sums of f(0..n-1) into out[0..n] (out[n] = total), over
-// the whole work-group; every thread must call it.  Thread t sums a
-// contiguous run, runs are scanned across lanes and then across wavefronts.
+// the whole work-group; every thread must call it.  Up to 64 * kScanRun
+// terms (batches of up to 1024 sequences per launch and head slice) one
+// wavefront scans alone: each lane sums a contiguous run (up to 64 terms:
+// one term, evaluated once), the runs are scanned across lanes, and a single
+// barrier publishes the result.  Longer inputs are spread over all threads,
+// scanned across lanes and then across wavefronts.
+constexpr int kScanRun = 16;
 template <typename F>
 __device__ void block_exclusive_scan(F f, int n, int32_t* out, int32_t* s_waves) {
+  if (n <= 64) {  // one term per lane, each evaluated once
+    if (threadIdx.x < 64) {
+      const int lane = threadIdx.x;
+      const int32_t local = lane < n ? f(lane) : 0;
+      int32_t x = local;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int32_t y = __shfl_up(x, off, 64);
+        if (lane >= off) x += y;
+      }
+      if (lane < n) out[lane] = x - local;
+      if (lane == 63) out[n] = x;
+    }
+    __syncthreads();
+    return;
+  }
+  if (n <= 64 * kScanRun) {
+    if (threadIdx.x < 64) {
+      const int lane = threadIdx.x;
+      const int run = (n + 63) / 64;
+      const int i0 = min(n, lane * run);
+      const int i1 = min(n, i0 + run);
+      int32_t local = 0;
+      for (int i = i0; i < i1; ++i) local += f(i);
+      int32_t x = local;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int32_t y = __shfl_up(x, off, 64);
+        if (lane >= off) x += y;
+      }
+      int32_t pre = x - local;
+      for (int i = i0; i < i1; ++i) {
+        out[i] = pre;
+        pre += f(i);
+      }
+      if (lane == 63) out[n] = x;
+    }
+    __syncthreads();
+    return;
+  }
   const int nt = blockDim.x;
   const int t = threadIdx.x;
   const int lane = t & 63;
@@ -292,8 +337,14 @@ __device__ void block_exclusive_scan(F f, int n, int32_t* out, int32_t* s_waves)
 }
 
 // Index of the work-group whose chunk range [c*G/W...) holds chunk c.
+// floor(x / d) for 0 <= x, 0 < d: 32-bit division where both fit (the usual
+// case; a 64-bit division is a long instruction sequence on the GPU).
+__device__ __forceinline__ int64_t div_nonneg(int64_t x, int64_t d) {
+  if (((x | d) >> 32) == 0) return static_cast<uint32_t>(x) / static_cast<uint32_t>(d);
+  return x / d;
+}
 __device__ __forceinline__ int range_owner(int64_t c, int64_t nwg, int64_t total) {
-  return static_cast<int>(((c + 1) * nwg - 1) / total);
+  return static_cast<int>(div_nonneg((c + 1) * nwg - 1, total));
 }
 
 template <int BS>
@@ -408,31 +459,34 @@ __global__ void __launch_bounds__(KV::kMaxWaves * 64) decode_kernel(DecodeArgs a
     if constexpr (GROUPED) return suffix_start<BS>(s_pblk[b], L);
     return 0;
   };
-  block_exclusive_scan(
-      [&](int v) {
-        const int b = v % a.batch;
-        const int L = s_len[b];
-        return length_ok<BS>(L, a) ? (L - start_of(b, L) + kChunk - 1) / kChunk : 0;
-      },
-      nv, s_pref, s_waves);
-  const int64_t total = s_pref[nv];
-  // Ranges are dealt over min(grid, chunks) work-groups so none is empty.
-  const int64_t nwg = total < gridDim.x ? total : static_cast<int64_t>(gridDim.x);
+  auto chunks = [&](int v) -> int32_t {
+    const int b = v % a.batch;
+    const int L = s_len[b];
+    return length_ok<BS>(L, a) ? (L - start_of(b, L) + kChunk - 1) / kChunk : 0;
+  };
   // 2. pieces of every sequence the ranges cut; slots for their partials.
   // A sequence with a shared prefix (grouped call) always leaves pieces: the
   // merge kernel folds the prefix's partial states in with them.
+  // Ranges are dealt over min(grid, chunks) work-groups so none is empty.
   auto prefixed = [&](int v) -> bool {
     const int b = v % a.batch;
     const int L = s_len[b];
     return length_ok<BS>(L, a) && start_of(b, L) > 0;
   };
-  auto pieces = [&](int v) -> int32_t {
-    const int64_t c0 = s_pref[v], c1 = s_pref[v + 1];
+  auto pieces_of = [&](int v, int64_t c0, int64_t c1, int64_t nwg, int64_t total) -> int32_t {
     if (c1 == c0) return 0;
     const int k = range_owner(c1 - 1, nwg, total) - range_owner(c0, nwg, total) + 1;
     return k > 1 || prefixed(v) ? k : 0;
   };
-  block_exclusive_scan(pieces, nv, s_part, s_waves);
+  block_exclusive_scan(chunks, nv, s_pref, s_waves);
+  {
+    const int64_t tot = s_pref[nv];
+    const int64_t nw = tot < gridDim.x ? tot : static_cast<int64_t>(gridDim.x);
+    block_exclusive_scan([&](int v) { return pieces_of(v, s_pref[v], s_pref[v + 1], nw, tot); }, nv, s_part,
+                         s_waves);
+  }
+  const int64_t total = s_pref[nv];
+  const int64_t nwg = total < gridDim.x ? total : static_cast<int64_t>(gridDim.x);
   if (g == 0) {
     for (int v = threadIdx.x; v < nv; v += blockDim.x) {
       a.ws_plan[2 * v] = s_part[v];
@@ -464,17 +518,22 @@ __global__ void __launch_bounds__(KV::kMaxWaves * 64) decode_kernel(DecodeArgs a
 
   // 4. this work-group's chunks [first, last)
   if (g >= nwg) return;
-  const int64_t first = g * total / nwg;
-  const int64_t last = (g + 1) * total / nwg;
+  const int64_t first = div_nonneg(g * total, nwg);
+  const int64_t last = div_nonneg((g + 1) * total, nwg);
   if (first >= last) return;
   int v;
-  {  // virtual sequence holding chunk `first`: s_pref[v] <= first < s_pref[v + 1]
-    int lo = 0, hi = nv;
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (s_pref[mid] <= first) lo = mid; else hi = mid;
+  {  // virtual sequence holding chunk `first`: the last v < nv with s_pref[v] <= first
+    if (nv <= 64) {  // one LDS read per lane and a ballot (s_pref is non-decreasing)
+      const bool le = lane < nv && s_pref[lane] <= first;
+      v = __popcll(__ballot(le)) - 1;
+    } else {
+      int lo = 0, hi = nv;
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (s_pref[mid] <= first) lo = mid; else hi = mid;
+      }
+      v = lo;
     }
-    v = lo;
     while (s_pref[v + 1] == s_pref[v]) ++v;
   }
 
