@@ -336,13 +336,15 @@ __device__ void block_exclusive_scan(F f, int n, int32_t* out, int32_t* s_waves)
   __syncthreads();
 }
 
-// Index of the work-group whose chunk range [c*G/W...) holds chunk c.
 // floor(x / d) for 0 <= x, 0 < d: 32-bit division where both fit (the usual
 // case; a 64-bit division is a long instruction sequence on the GPU).
 __device__ __forceinline__ int64_t div_nonneg(int64_t x, int64_t d) {
   if (((x | d) >> 32) == 0) return static_cast<uint32_t>(x) / static_cast<uint32_t>(d);
   return x / d;
 }
+
+// Index of the work-group whose chunk range [g*total/nwg, (g+1)*total/nwg)
+// holds chunk c.
 __device__ __forceinline__ int range_owner(int64_t c, int64_t nwg, int64_t total) {
   return static_cast<int>(div_nonneg((c + 1) * nwg - 1, total));
 }
@@ -465,9 +467,9 @@ __global__ void __launch_bounds__(KV::kMaxWaves * 64) decode_kernel(DecodeArgs a
     return length_ok<BS>(L, a) ? (L - start_of(b, L) + kChunk - 1) / kChunk : 0;
   };
   // 2. pieces of every sequence the ranges cut; slots for their partials.
+  // Ranges are dealt over min(grid, chunks) work-groups so none is empty.
   // A sequence with a shared prefix (grouped call) always leaves pieces: the
   // merge kernel folds the prefix's partial states in with them.
-  // Ranges are dealt over min(grid, chunks) work-groups so none is empty.
   auto prefixed = [&](int v) -> bool {
     const int b = v % a.batch;
     const int L = s_len[b];
