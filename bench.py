@@ -894,7 +894,10 @@ def main():
 
     ms_per_step = elapsed / args.steps * 1e3
     call_name = (("pkv_append_attention_decode_grouped" if fused else "pkv_attention_decode_grouped")
-                 + ("_quant" if kv != "dense" else "") + " (prefix_kernel + decode_kernel + decode_merge_kernel)"
+                 + ("_quant" if kv != "dense" else "")
+                 + (" (grouped_decode_kernel: decode ranges and prefix units in one launch + decode_merge_kernel)"
+                    if kv == "dense" and wgs < torch.cuda.get_device_properties(0).multi_processor_count else
+                    " (prefix_kernel + decode_kernel + decode_merge_kernel)")
                  if prefix is not None else
                  "pkv_attention_decode_scores (decode_kernel + merge_score_kernel)" if args.scores else
                  ("pkv_append_attention_decode" if fused else "pkv_attention_decode")

@@ -300,9 +300,9 @@ PKV_API int pkv_swap_blocks(void* const* dst_pools, const void* const* src_pools
                             size_t bytes_per_block, hipStream_t stream);
 
 /* Work-groups a decode call launches when called with num_work_groups = 0,
- * for caches of `cache_dtype`: one per compute unit of the current device
- * for F32/F16/BF16 caches (256 on MI355X), two per compute unit for I8 and
- * FP8_E4M3 caches.  PKV_ERR_HIP if no device is current, PKV_ERR_INVALID for
+ * for caches of `cache_dtype`: seven eighths of the compute units of the
+ * current device for F32/F16/BF16 caches (224 on MI355X), two per compute
+ * unit for I8 and FP8_E4M3 caches (512).  PKV_ERR_HIP if no device is current, PKV_ERR_INVALID for
  * an unknown type. */
 PKV_API int32_t pkv_decode_work_groups(pkv_dtype cache_dtype);
 

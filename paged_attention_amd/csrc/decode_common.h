@@ -32,6 +32,7 @@
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cmath>
 #include <cstdint>
@@ -234,6 +235,7 @@ struct DecodeArgs {
   int32_t prefix_row;            // = D + 4 (rows stay 16-byte aligned)
   int32_t prefix_parts;          // work-groups per prefix tile and head (partial states per sequence)
   int32_t prefix_batch;          // the whole call's batch (stride of the parts)
+  int32_t grid_decode;           // work-groups sharing the chunks (a fused grouped grid runs prefix units after them)
   const int32_t* tables;
   const int32_t* lens;
   float* ws_acc;      // [partial slot][H][D]
@@ -427,8 +429,10 @@ enum DecodeMode { kPlain = 0, kAppend = 1, kScores = 2 };
 // work-group whose range holds a sequence's last chunk is the only one that
 // reads position L - 1, and it stores the row itself, lane by lane, before
 // reading it back with the same lanes: no other work-group is involved.
+// decode_body is the work of one of the `grid` work-groups that share the
+// chunks (work-group g); decode_kernel runs it over its whole grid.
 template <class KV, int D, int BS, int MODE, bool GROUPED>
-__global__ void __launch_bounds__(KV::kMaxWaves * 64) decode_kernel(DecodeArgs a) {
+__device__ __forceinline__ void decode_body(const DecodeArgs& a, const int grid, const int g) {
   constexpr bool APPEND = MODE == kAppend;
   constexpr bool SCORES = MODE == kScores;
   constexpr int EPL = KV::EPL;
@@ -449,7 +453,6 @@ __global__ void __launch_bounds__(KV::kMaxWaves * 64) decode_kernel(DecodeArgs a
   int32_t* s_part = s_dyn + nv + 1;  // [nv + 1]: first partial slot of each virtual sequence
   int32_t* s_len = s_part + nv + 1;  // [batch]: the lengths, read once (they may be host memory)
   int32_t* s_pblk = s_len + a.batch;  // GROUPED, [batch]: shared-prefix blocks, read with the lengths
-  const int g = blockIdx.x;
 
   // 1. chunk counts of every (head slice, sequence); bad lengths count zero.
   for (int b = threadIdx.x; b < a.batch; b += blockDim.x) {
@@ -483,12 +486,12 @@ __global__ void __launch_bounds__(KV::kMaxWaves * 64) decode_kernel(DecodeArgs a
   block_exclusive_scan(chunks, nv, s_pref, s_waves);
   {
     const int64_t tot = s_pref[nv];
-    const int64_t nw = tot < gridDim.x ? tot : static_cast<int64_t>(gridDim.x);
+    const int64_t nw = tot < grid ? tot : static_cast<int64_t>(grid);
     block_exclusive_scan([&](int v) { return pieces_of(v, s_pref[v], s_pref[v + 1], nw, tot); }, nv, s_part,
                          s_waves);
   }
   const int64_t total = s_pref[nv];
-  const int64_t nwg = total < gridDim.x ? total : static_cast<int64_t>(gridDim.x);
+  const int64_t nwg = total < grid ? total : static_cast<int64_t>(grid);
   if (g == 0) {
     for (int v = threadIdx.x; v < nv; v += blockDim.x) {
       a.ws_plan[2 * v] = s_part[v];
@@ -505,7 +508,7 @@ __global__ void __launch_bounds__(KV::kMaxWaves * 64) decode_kernel(DecodeArgs a
 
   // 3. sequences with no chunks (length 0, or a length the table cannot
   // hold) are written here: zero rows, or NaN rows for an invalid length.
-  for (int v = g; v < nv; v += gridDim.x) {
+  for (int v = g; v < nv; v += grid) {
     if (s_pref[v + 1] != s_pref[v]) continue;
     const int b = v % a.batch, y = v / a.batch;
     const int h = (y * a.waves_per_group + wave) * HPW + r;
@@ -626,6 +629,11 @@ __global__ void __launch_bounds__(KV::kMaxWaves * 64) decode_kernel(DecodeArgs a
       while (s_pref[v + 1] == s_pref[v]) ++v;
     }
   }
+}
+
+template <class KV, int D, int BS, int MODE, bool GROUPED>
+__global__ void __launch_bounds__(KV::kMaxWaves * 64) decode_kernel(DecodeArgs a) {
+  decode_body<KV, D, BS, MODE, GROUPED>(a, static_cast<int>(gridDim.x), static_cast<int>(blockIdx.x));
 }
 
 // Merges the pieces of every cut sequence, after the partial states of its
@@ -894,16 +902,9 @@ inline int heads_per_wave(int32_t head_dim, pkv_dtype cache_dtype) {
   return 64 / (head_dim / epl);
 }
 
-// Work-groups per compute unit of the automatic choice.  Measured on MI355X
-// (7B-shaped layer): for 16-bit caches, 256 work-groups of 8 wavefronts read
-// at 5.7 TB/s; 512 at 5.4 TB/s, 1024 at 5.1 TB/s — fewer, longer streams keep
-// more DRAM pages open per request.  8-bit caches carry twice the elements
-// per byte and run 4 wavefronts per work-group for 32 heads, so they take two
-// work-groups per compute unit to keep the same wavefronts resident.
-inline int work_groups_per_cu(pkv_dtype cache_dtype) { return is_8bit(cache_dtype) ? 2 : 1; }
-
-// Work-groups of the automatic choice on the current device.
-inline int32_t auto_work_groups(pkv_dtype cache_dtype) {
+// Compute units of the current device (cached per device); PKV_ERR_HIP
+// (negative) when no device is current or the query fails.
+inline int32_t device_compute_units() {
   static std::atomic<int32_t> cus_cached[64];  // zero-initialised; calls from several threads may fill it
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) return pkv::fail(PKV_ERR_HIP, "no current HIP device");
@@ -913,7 +914,25 @@ inline int32_t auto_work_groups(pkv_dtype cache_dtype) {
       return pkv::fail(PKV_ERR_HIP, "cannot query the compute-unit count");
     if (dev < 64) cus_cached[dev].store(cus, std::memory_order_relaxed);
   }
-  return cus * work_groups_per_cu(cache_dtype);
+  return cus;
+}
+
+// Work-groups of the automatic choice on the current device.  Measured on
+// MI355X with 16-bit caches (µs per call, 160 / 192 / 208 / 224 / 240 / 256
+// work-groups of 8 wavefronts): 7B-shaped layer 104.9 / 99.8 / 99.5 / 98.7 /
+// 99.8 / 99.8, 13B long context 229.7 / 216.6 / 215.5 / 214.4 / 214.8 /
+// 216.0; 512 read 5 % slower than 256.  Fewer, longer streams keep more DRAM
+// pages open per request until too few remain to cover the latency: seven
+// eighths of the compute units (28 of the 32 of each XCD, as the dispatcher
+// deals work-groups to the XCDs in turn) is the best of the sweep.  8-bit
+// caches carry twice the elements per byte and run 4 wavefronts per
+// work-group for 32 heads, so they take two work-groups per compute unit to
+// keep the same wavefronts resident (FP8 7B layer 416 / 448 / 480 / 512:
+// 67.4 / 66.9 / 67.1 / 66.2 µs).
+inline int32_t auto_work_groups(pkv_dtype cache_dtype) {
+  const int32_t cus = device_compute_units();
+  if (cus <= 0) return cus;
+  return is_8bit(cache_dtype) ? 2 * cus : std::max<int32_t>(1, cus - cus / 8);
 }
 
 inline int check_launch(const char* what) {
@@ -970,22 +989,32 @@ inline Layout workspace_layout(int32_t batch, int32_t num_heads, int32_t head_di
 // first and `tm.stop` with the second (kernel timestamps, no extra queue
 // packets).
 // GROUPED: a grouped call (shared prefixes attended by the prefix kernel).
-template <class KV, int D, int BS, int MODE, bool GROUPED>
-void launch_decode_g(const DecodeArgs& a, int wg, hipStream_t stream, const pkv::CallEvents& tm) {
-  const size_t lds = (2 * (static_cast<size_t>(a.batch) * a.groups_y + 1) + a.batch * (GROUPED ? 2 : 1)) *
-                    sizeof(int32_t);
+// Dynamic LDS of a decode work-group: the two prefix-sum arrays and the
+// lengths (and, grouped, the shared-prefix blocks).
+inline size_t decode_lds_bytes(const DecodeArgs& a, bool grouped) {
+  return (2 * (static_cast<size_t>(a.batch) * a.groups_y + 1) + a.batch * (grouped ? 2 : 1)) * sizeof(int32_t);
+}
+
+// The merge (or merge-and-score) launch after a decode launch.
+template <class KV, int D, int MODE, bool GROUPED>
+void launch_merge(const DecodeArgs& a, hipStream_t stream, hipEvent_t stop) {
   const bool scores = MODE == kScores && a.max_seq_len > 0;
-  hipExtLaunchKernelGGL((decode_kernel<KV, D, BS, MODE, GROUPED>), dim3(wg), dim3(a.waves_per_group * 64), lds,
-                        stream, tm.start, nullptr, 0, a);
   const int slice_heads = a.waves_per_group * a.heads_per_wave;
   const int merge_x = ceil_div(slice_heads, kMergeWaves);
   if (scores)
     hipExtLaunchKernelGGL((merge_score_kernel<KV::QT, D>),
                           dim3(merge_x + ceil_div(a.max_seq_len, 256), a.batch * a.groups_y), dim3(kMergeWaves * 64),
-                          0, stream, nullptr, tm.stop, 0, a, merge_x);
+                          0, stream, nullptr, stop, 0, a, merge_x);
   else
     hipExtLaunchKernelGGL((decode_merge_kernel<KV::QT, D, GROUPED>), dim3(merge_x, a.batch * a.groups_y),
-                          dim3(kMergeWaves * 64), 0, stream, nullptr, tm.stop, 0, a);
+                          dim3(kMergeWaves * 64), 0, stream, nullptr, stop, 0, a);
+}
+
+template <class KV, int D, int BS, int MODE, bool GROUPED>
+void launch_decode_g(const DecodeArgs& a, int wg, hipStream_t stream, const pkv::CallEvents& tm) {
+  hipExtLaunchKernelGGL((decode_kernel<KV, D, BS, MODE, GROUPED>), dim3(wg), dim3(a.waves_per_group * 64),
+                        decode_lds_bytes(a, GROUPED), stream, tm.start, nullptr, 0, a);
+  launch_merge<KV, D, MODE, GROUPED>(a, stream, tm.stop);
 }
 
 template <class KV, int D, int BS, int MODE>
@@ -1111,6 +1140,7 @@ inline int prepare_decode(DecodeArgs& a, const void* q, const void* k_cache, con
   a.prefix_row = 0;
   a.prefix_parts = 0;
   a.prefix_batch = 0;
+  a.grid_decode = wg;
   a.ws_plan = reinterpret_cast<int32_t*>(base + ws.plan);
   a.ws_acc = reinterpret_cast<float*>(base + ws.acc);
   a.ws_ml = reinterpret_cast<float2*>(base + ws.ml);

@@ -183,6 +183,21 @@ int decode_grouped(void* out, const void* q, const void* k_new, const void* v_ne
           if (dtype == PKV_F16) launch_decode_m<DenseKV<PKV_F16>, kPlain>(s, wg, block_size, head_dim, stream, tm);
           else launch_decode_m<DenseKV<PKV_BF16>, kPlain>(s, wg, block_size, head_dim, stream, tm);
         }
+      },
+      [&](const DecodeArgs& s, const pkv::CallEvents& tm, int32_t units) {
+        using F16 = DenseKV<PKV_F16>;
+        using B16 = DenseKV<PKV_BF16>;
+        if (k_new != nullptr) {
+          if (dtype == PKV_F16)
+            launch_fused<F16, PrefixDense<PKV_F16>, kAppend>(s, block_size, head_dim, tiles, units, stream, tm);
+          else
+            launch_fused<B16, PrefixDense<PKV_BF16>, kAppend>(s, block_size, head_dim, tiles, units, stream, tm);
+        } else {
+          if (dtype == PKV_F16)
+            launch_fused<F16, PrefixDense<PKV_F16>, kPlain>(s, block_size, head_dim, tiles, units, stream, tm);
+          else
+            launch_fused<B16, PrefixDense<PKV_BF16>, kPlain>(s, block_size, head_dim, tiles, units, stream, tm);
+        }
       });
 }
 

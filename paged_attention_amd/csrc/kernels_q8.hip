@@ -475,7 +475,8 @@ int decode_grouped_q8(void* out, const void* q, const void* k_new, const void* v
             else launch_decode_m<Q8KV<PKV_BF16, PKV_I8>, kPlain>(s, wg, block_size, head_dim, stream, tm);
           }
         }
-      });
+      },
+      nullptr);  // the 8-bit ranges fill every compute unit: no fused launch
 }
 
 }  // namespace

@@ -46,6 +46,7 @@
 #pragma once
 
 #include <algorithm>
+#include <type_traits>
 
 #include "decode_common.h"
 
@@ -116,39 +117,50 @@ __device__ __forceinline__ int tile_member(const int32_t* tp, int j, int n, int 
   return length_ok<BS>(L, a) && prefix_tokens < L ? b : -1;
 }
 
-template <class PF, int D, int BS>
-__global__ void __launch_bounds__(kPrefixWaves * 64) prefix_kernel(DecodeArgs a, const int32_t* tiles) {
+// One unit of prefix work: tile x / prefix_parts, its part x % prefix_parts
+// and head h, taken by the kPrefixWaves wavefronts of sub-group `sub` of the
+// work-group (local thread index tid < kPrefixWaves * 64).  A work-group of
+// NSUB sub-groups runs NSUB units side by side; all its threads reach the
+// same barriers, so a sub-group with no unit (live = false) or a malformed
+// tile takes no step and writes nothing, but does not leave early.
+template <class PF, int D, int BS, int NSUB>
+__device__ __forceinline__ void prefix_unit(const DecodeArgs& a, const int32_t* tiles, const int x, const int h,
+                                            const int sub, const int tid, const bool live) {
   using M = PrefixMma<PF::MT>;
   constexpr int KS = D / 16;   // products per S^T step; 16-element tiles of O^T
   constexpr int RUN = D / 4;   // elements of a lane's K (and V) run
   constexpr int RW = RUN * PF::KB / 4;  // 32-bit words of a run in the cache
   constexpr int EPT = D / (kPrefixWaves * 4);  // elements per thread in the final merge (16 threads a column)
   constexpr int NS = PKV_PREFIX_TILE_SEQS;
+  constexpr int kUnitThreads = kPrefixWaves * 64;
   static_assert(NS == 16, "one MFMA column per sequence");
   static_assert(RW % 4 == 0, "whole 16-byte loads");
-  // LDS: the V^T of each wavefront's step, and after the steps (in the same
-  // bytes) the wavefronts' weighted values for the merge; 37 KB at D = 128,
-  // so that four work-groups share a compute unit.
-  __shared__ __align__(16) float s_buf[kPrefixWaves * D * NS];
-  auto s_v = reinterpret_cast<uint16_t(*)[D][kPrefixStep]>(s_buf);
-  auto s_acc = reinterpret_cast<float(*)[D][NS]>(s_buf);
-  __shared__ float s_m[kPrefixWaves][NS];
-  __shared__ float s_l[kPrefixWaves][NS];
+  // LDS per sub-group: the V^T of each wavefront's step, and after the steps
+  // (in the same bytes) the wavefronts' weighted values for the merge; 37 KB
+  // at D = 128, so that four one-unit work-groups share a compute unit.
+  __shared__ __align__(16) float s_buf_all[NSUB][kPrefixWaves * D * NS];
+  __shared__ float s_m_all[NSUB][kPrefixWaves][NS];
+  __shared__ float s_l_all[NSUB][kPrefixWaves][NS];
+  __shared__ int32_t s_bad[NSUB];
+  auto s_v = reinterpret_cast<uint16_t(*)[D][kPrefixStep]>(s_buf_all[sub]);
+  auto s_acc = reinterpret_cast<float(*)[D][NS]>(s_buf_all[sub]);
+  auto s_m = s_m_all[sub];
+  auto s_l = s_l_all[sub];
 
-  const int part = blockIdx.x % a.prefix_parts;  // which share of the tile's steps
-  const int32_t* tp = tiles + static_cast<int64_t>(blockIdx.x / a.prefix_parts) * PKV_PREFIX_TILE_INTS;
-  const int h = blockIdx.y;
+  const int part = x % a.prefix_parts;  // which share of the tile's steps
+  const int32_t* tp = tiles + static_cast<int64_t>(x / a.prefix_parts) * PKV_PREFIX_TILE_INTS;
   const int P = tp[0], n = tp[1], lead = tp[2];
-  if (P <= 0 || P > a.max_blocks || n < 1 || n > NS || static_cast<uint32_t>(lead) >= static_cast<uint32_t>(a.batch))
-    return;  // a malformed tile (uniform over the work-group)
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: the step loop does not diverge
-  const int lane = threadIdx.x & 63;
+  // a malformed tile (uniform over the sub-group) is taken as no unit
+  const bool ok = live && P > 0 && P <= a.max_blocks && n >= 1 && n <= NS &&
+                  static_cast<uint32_t>(lead) < static_cast<uint32_t>(a.batch);
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: the step loop does not diverge
+  const int lane = tid & 63;
   const int col = lane & 15, grp = lane >> 4;
-  const int prefix_tokens = P * BS;
+  const int prefix_tokens = ok ? P * BS : 0;
   const uint8_t* kpool = static_cast<const uint8_t*>(a.k);
   const uint8_t* vpool = static_cast<const uint8_t*>(a.v);
   const int64_t row_bytes = static_cast<int64_t>(a.num_heads) * D * PF::KB;  // one token's cache row
-  const int32_t* trow = a.tables + static_cast<int64_t>(lead) * a.max_blocks;
+  const int32_t* trow = a.tables + static_cast<int64_t>(ok ? lead : 0) * a.max_blocks;
 
   // Prologue: after the tile header, one round of independent loads.  The
   // tables and lengths may be pinned host memory, where every read is a PCIe
@@ -160,11 +172,15 @@ __global__ void __launch_bounds__(kPrefixWaves * 64) prefix_kernel(DecodeArgs a,
   //   - this lane's Q^T operand (its column's sequence, elements grp D/4 ..
   //     grp D/4 + D/4 - 1), loaded for the header's index clamped into the
   //     batch and zeroed after the barrier when the member is not valid.
-  __shared__ int32_t s_ids[kPrefixIdsLds];
-  __shared__ int32_t s_member[NS];
+  __shared__ int32_t s_ids_all[NSUB][kPrefixIdsLds];
+  __shared__ int32_t s_member_all[NSUB][NS];
+  int32_t* s_ids = s_ids_all[sub];
+  int32_t* s_member = s_member_all[sub];
   const bool too_long = P > kPrefixIdsLds;
-  for (int i = threadIdx.x; i < P && i < kPrefixIdsLds; i += blockDim.x) s_ids[i] = trow[i];
-  if (threadIdx.x < NS) s_member[threadIdx.x] = tile_member<BS>(tp, threadIdx.x, n, prefix_tokens, a);
+  const int nids = ok ? min(P, kPrefixIdsLds) : 0;
+  for (int i = tid; i < nids; i += kUnitThreads) s_ids[i] = trow[i];
+  if (tid < NS) s_member[tid] = ok ? tile_member<BS>(tp, tid, n, prefix_tokens, a) : -1;
+  if (tid == 0) s_bad[sub] = 0;
   uint2 qb[KS];
   {
     const int bh = col < n ? tp[2 + col] : 0;
@@ -290,7 +306,7 @@ __global__ void __launch_bounds__(kPrefixWaves * 64) prefix_kernel(DecodeArgs a,
   // step is loaded before its current one is folded.  The loads are
   // unconditional (the last step is read again at the end) so that the
   // compiler's waits stay partial.
-  const int nsteps = too_long ? 0 : (prefix_tokens + kPrefixStep - 1) / kPrefixStep;
+  const int nsteps = too_long || !ok ? 0 : (prefix_tokens + kPrefixStep - 1) / kPrefixStep;
   const int stride = kPrefixWaves * a.prefix_parts;
   int st = part * kPrefixWaves + wave;
   if (st < nsteps) {
@@ -318,12 +334,14 @@ __global__ void __launch_bounds__(kPrefixWaves * 64) prefix_kernel(DecodeArgs a,
   for (int c = 0; c < KS; ++c)
 #pragma unroll
     for (int r = 0; r < 4; ++r) s_acc[wave][16 * c + 4 * grp + r][col] = acc[c][r];
-  bad = __syncthreads_or(bad);
+  if (__any(bad) && lane == 0) s_bad[sub] = 1;  // the sub-group's bad-block flag (same value from any wavefront)
+  __syncthreads();
+  bad = s_bad[sub];
 
   // merge the wavefronts' states; thread t: column t % 16, elements EPT * (t / 16) + (0 .. EPT)
   static_assert(EPT % 2 == 0 && EPT * kPrefixWaves * 4 == D, "the merge covers every element");
-  const int j = threadIdx.x & 15;
-  const int e0 = EPT * (threadIdx.x >> 4);
+  const int j = tid & 15;
+  const int e0 = EPT * (tid >> 4);
   const int bj = s_member[j];
   if (bj < 0) return;
   float mmax = -INFINITY;
@@ -350,6 +368,43 @@ __global__ void __launch_bounds__(kPrefixWaves * 64) prefix_kernel(DecodeArgs a,
   }
 }
 
+// Grid (tiles x parts, heads): one unit per work-group.
+template <class PF, int D, int BS>
+__global__ void __launch_bounds__(kPrefixWaves * 64) prefix_kernel(DecodeArgs a, const int32_t* tiles) {
+  prefix_unit<PF, D, BS, 1>(a, tiles, static_cast<int>(blockIdx.x), static_cast<int>(blockIdx.y), 0,
+                            static_cast<int>(threadIdx.x), true);
+}
+
+// A grouped call's decode and prefix work in one grid.  Work-groups
+// [0, a.grid_decode) take the stream-K ranges of the sequences' own
+// positions, as decode_kernel; the ones after them take the prefix units,
+// blockDim.x / (kPrefixWaves * 64) units each (unit u: tile part u / H, head
+// u % H), into the same partial prefix states as prefix_kernel.  Neither half
+// reads what the other writes: the merge kernel, launched after, combines
+// them.  Work-groups start in index order, so the ranges are resident first,
+// and the fused kernel's register count (the prefix body's) leaves no room
+// for a second work-group beside a range's: prefix units run on the compute
+// units the ranges leave free instead of slowing a range down.
+constexpr int kFusedMaxWaves = 8;  // work-groups of 4 or 8 wavefronts: one or two prefix units
+template <class KV, class PF, int D, int BS, int MODE>
+__global__ void __launch_bounds__(kFusedMaxWaves * 64)
+    grouped_decode_kernel(DecodeArgs a, const int32_t* tiles, int32_t prefix_units) {
+  const int g = static_cast<int>(blockIdx.x);
+  if (g < a.grid_decode) {
+    decode_body<KV, D, BS, MODE, true>(a, a.grid_decode, g);
+    return;
+  }
+  constexpr int kUnitThreads = kPrefixWaves * 64;
+  constexpr int NSUB = kFusedMaxWaves / kPrefixWaves;
+  const int nsub = static_cast<int>(blockDim.x) / kUnitThreads;  // the host launches whole units
+  const int sub = static_cast<int>(threadIdx.x) / kUnitThreads;
+  const int64_t u = static_cast<int64_t>(g - a.grid_decode) * nsub + sub;
+  const bool live = u < prefix_units;
+  const int uu = live ? static_cast<int>(u) : 0;
+  prefix_unit<PF, D, BS, NSUB>(a, tiles, uu / a.num_heads, uu % a.num_heads, sub,
+                               static_cast<int>(threadIdx.x) % kUnitThreads, live);
+}
+
 // ---- host side of a grouped call ---------------------------------------------
 
 // Workspace of a grouped call: the decode workspace (with a piece slot per
@@ -373,6 +428,42 @@ void launch_prefix(const DecodeArgs& a, int32_t bs, const int32_t* tiles, int32_
   }
 }
 
+// A grouped call's decode and prefix work in one launch (grouped_decode_kernel,
+// `units` prefix units after the a.grid_decode ranges), then the merge.
+template <class KV, class PF, int D, int BS, int MODE>
+void launch_fused_g(const DecodeArgs& a, const int32_t* tiles, int32_t units, hipStream_t stream,
+                    const pkv::CallEvents& tm) {
+  const int nsub = a.waves_per_group / kPrefixWaves;
+  const int grid = a.grid_decode + (units + nsub - 1) / nsub;
+  hipExtLaunchKernelGGL((grouped_decode_kernel<KV, PF, D, BS, MODE>), dim3(grid), dim3(a.waves_per_group * 64),
+                        decode_lds_bytes(a, true), stream, tm.start, nullptr, 0, a, tiles, units);
+  launch_merge<KV, D, MODE, true>(a, stream, tm.stop);
+}
+
+template <class KV, class PF, int MODE>
+void launch_fused(const DecodeArgs& a, int32_t bs, int32_t d, const int32_t* tiles, int32_t units, hipStream_t stream,
+                  const pkv::CallEvents& tm) {
+  if (d == 64) {
+    switch (bs) {
+      case 8: launch_fused_g<KV, PF, 64, 8, MODE>(a, tiles, units, stream, tm); break;
+      case 16: launch_fused_g<KV, PF, 64, 16, MODE>(a, tiles, units, stream, tm); break;
+      default: launch_fused_g<KV, PF, 64, 32, MODE>(a, tiles, units, stream, tm); break;
+    }
+  } else {
+    switch (bs) {
+      case 8: launch_fused_g<KV, PF, 128, 8, MODE>(a, tiles, units, stream, tm); break;
+      case 16: launch_fused_g<KV, PF, 128, 16, MODE>(a, tiles, units, stream, tm); break;
+      default: launch_fused_g<KV, PF, 128, 32, MODE>(a, tiles, units, stream, tm); break;
+    }
+  }
+}
+
+// Batches (times head slices) up to this run fused: the decode half's LDS
+// arrays then stay small beside the prefix half's.
+constexpr int32_t kFusedMaxVirtual = 1024;
+// Prefix units of one fused launch at most (the grid stays far from any limit).
+constexpr int64_t kFusedMaxUnits = int64_t{1} << 24;
+
 inline int check_grouped_sizes(const char* what, int32_t batch, int32_t num_heads, int32_t head_dim,
                                int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
                                int32_t max_seq_len, int32_t num_tiles) {
@@ -385,15 +476,26 @@ inline int check_grouped_sizes(const char* what, int32_t batch, int32_t num_head
 }
 
 // The rest of a grouped call once `a` is prepared (prepare_decode with
-// grouped = true): prefix arrays, parts, the prefix launch
-// (launch_prefix_fn(pa, start event)) and the decode and merge launches over
-// slices of the batch (launch_decode_fn(slice args, events)).
-template <class LaunchPrefix, class LaunchDecode>
+// grouped = true): prefix arrays, parts, then either one fused launch
+// (launch_fused_fn(args, events, units); nullptr where the format has none)
+// or the prefix launch (launch_prefix_fn(pa, start event)) followed by the
+// decode and merge launches over slices of the batch (launch_decode_fn(slice
+// args, events)).
+//
+// Fused when the ranges leave compute units free (fewer work-groups than
+// compute units), the whole batch fits one launch and every work-group holds
+// whole prefix units: the prefix then costs no time of its own where it
+// fits beside the ranges.  Its parts per (tile, head) are then chosen so
+// that the units cover the free compute units' slots (at least one part);
+// otherwise they give the separate prefix launch two work-groups per compute
+// unit.
+template <class LaunchPrefix, class LaunchDecode, class LaunchFused>
 int run_grouped(DecodeArgs& a, int wg, void* out, const void* q, const int32_t* block_tables,
                 int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t batch, int32_t num_heads,
                 int32_t head_dim, pkv_dtype cache_dtype, int64_t q_row_bytes, const int32_t* seq_prefix_blocks,
                 int32_t num_tiles, void* workspace, size_t workspace_bytes, const pkv::CallEvents& timing,
-                const char* what, LaunchPrefix launch_prefix_fn, LaunchDecode launch_decode_fn) {
+                const char* what, LaunchPrefix launch_prefix_fn, LaunchDecode launch_decode_fn,
+                LaunchFused launch_fused_fn) {
   const size_t need = grouped_workspace_bytes(batch, num_heads, head_dim, cache_dtype, wg);
   if (workspace_bytes < need)
     return pkv::fail(PKV_ERR_INVALID, "%s: workspace of %zu bytes needed, %zu given", what, need, workspace_bytes);
@@ -403,13 +505,33 @@ int run_grouped(DecodeArgs& a, int wg, void* out, const void* q, const int32_t* 
                                             workspace_layout(batch, num_heads, head_dim, cache_dtype, wg, true).total);
   a.prefix_row = head_dim + 4;
   a.prefix_batch = batch;
-  // Parts per (tile, head): enough work-groups for two per compute unit.
-  {
-    const int64_t units = static_cast<int64_t>(num_tiles) * num_heads;
-    const int64_t want = 2 * static_cast<int64_t>(auto_work_groups(PKV_F16));
-    a.prefix_parts = units <= 0 ? 1 : static_cast<int32_t>(std::max<int64_t>(1, std::min<int64_t>(
-                                                                kPrefixPartsMax, (want + units - 1) / units)));
+  a.grid_decode = wg;
+  const int64_t units = static_cast<int64_t>(num_tiles) * num_heads;  // (tile, head) pairs
+  const int32_t cus = device_compute_units();
+  auto parts_for = [&](int64_t slots) {
+    return units <= 0 ? 1 : static_cast<int32_t>(std::max<int64_t>(1, std::min<int64_t>(
+                                kPrefixPartsMax, (slots + units - 1) / units)));
+  };
+  if constexpr (!std::is_same_v<LaunchFused, std::nullptr_t>) {
+    const int nsub = a.waves_per_group / kPrefixWaves;
+    if (num_tiles > 0 && cus > wg && nsub >= 1 && a.waves_per_group % kPrefixWaves == 0 &&
+        a.waves_per_group <= kFusedMaxWaves &&
+        static_cast<int64_t>(batch) * a.groups_y <= kFusedMaxVirtual) {
+      a.prefix_parts = parts_for(static_cast<int64_t>(cus - wg) * nsub);
+      const int64_t prefix_units = units * a.prefix_parts;
+      if (prefix_units <= kFusedMaxUnits) {
+        a.batch = batch;
+        a.out = out;
+        a.q = q;
+        a.tables = block_tables;
+        a.lens = seq_lens;
+        launch_fused_fn(static_cast<const DecodeArgs&>(a), timing, static_cast<int32_t>(prefix_units));
+        return check_launch(what);
+      }
+    }
   }
+  // Parts per (tile, head): enough work-groups for two per compute unit.
+  a.prefix_parts = parts_for(2 * static_cast<int64_t>(cus));
   pkv::CallEvents rest = timing;
   if (num_tiles > 0) {  // the shared prefixes first, over the whole batch
     DecodeArgs pa = a;

@@ -139,6 +139,63 @@ def test_batch_slices_with_groups():
     pc.compare(c, out)
 
 
+# ---- decode ranges and prefix units in one launch ----------------------------
+# A 16-bit grouped call whose decode work-groups are fewer than the compute
+# units, hold 4 or 8 wavefronts and whose batch fits one launch runs its
+# prefix units in the same grid, after the ranges; otherwise the prefix has a
+# launch of its own.  Both must meet the decode bound against the oracle.
+# Counts below the compute units take the one-launch path (with more parts per
+# tile and head the more units are free); counts at or above it the other.
+# 31 heads of 128 in three tiles: 8 wavefronts (two units per work-group) and
+# an odd number of units at one part, so the last work-group holds one unit
+# and an idle half.
+
+ONE_LAUNCH_SHAPES = [("f16", 32, 128, 16), ("bf16", 16, 128, 8), ("f16", 32, 64, 32), ("bf16", 31, 128, 16)]
+
+
+def _cus():
+    return torch.cuda.get_device_properties(0).multi_processor_count
+
+
+@pytest.mark.parametrize("dtype,num_heads,head_dim,block_size", ONE_LAUNCH_SHAPES)
+def test_one_launch_grouped_matches_oracle(dtype, num_heads, head_dim, block_size):
+    lens = LENS + [200 + 7 * i for i in range(30)]
+    sharers = SHARERS + list(range(len(LENS), len(LENS) + 30))  # 37 sharers: three tiles
+    wl = workloads.custom(lens, num_heads=num_heads, head_dim=head_dim, dtype=dtype, block_size=block_size,
+                          seed=num_heads + head_dim + block_size, prefix_len=40, sharers=sharers)
+    c = pc.build(wl, DEV)
+    ref = pc.oracle_out(c)
+    spb, tiles = pkv.prefix_tiles(c.tables_np, wl.seq_lens, block_size)
+    assert len(tiles) == 3 and spb[sharers].min() == 40 // block_size
+    cus = _cus()
+    for wg in (0, 3, 50, cus - 8, cus - 1, cus, cus + 44):
+        _log(f"one-launch grouped {dtype} H={num_heads} D={head_dim} BS={block_size} work_groups={wg}")
+        out, _, _ = _grouped(c, wg, spb, tiles)
+        pc.compare(c, out, ref)
+        _poison_newest(c)
+        out = _grouped_fused(c, wg, spb, tiles)
+        _assert_pools(c)
+        pc.compare(c, out, ref)
+
+
+def test_one_launch_grouped_is_deterministic_and_reads_no_stale_state():
+    # Two calls with the same arguments give the same bytes; a call after one
+    # with other lengths (a different prefix share and parts) as well.
+    wl = workloads.custom(LENS + [150] * 12, num_heads=32, head_dim=128, dtype="f16", block_size=16, seed=31,
+                          prefix_len=40, sharers=SHARERS + list(range(len(LENS), len(LENS) + 12)))
+    c = pc.build(wl, DEV)
+    spb, tiles = pkv.prefix_tiles(c.tables_np, wl.seq_lens, 16)
+    first, _, _ = _grouped(c, 0, spb, tiles)
+    first = first.clone()
+    other = workloads.custom([90] * 40, num_heads=32, head_dim=128, dtype="f16", block_size=16, seed=32,
+                             prefix_len=80, sharers=list(range(40)))
+    co = pc.build(other, DEV)
+    out_o, _, _ = _grouped(co, 0)
+    pc.compare(co, out_o)
+    again, _, _ = _grouped(c, 0, spb, tiles)
+    assert torch.equal(first.view(torch.uint8), again.view(torch.uint8))
+
+
 # ---- 8-bit caches (pkv_attention_decode_grouped_quant) -----------------------
 
 def _grouped_quant(c, work_groups=0, spb=None, tiles=None, min_sharers=2):
