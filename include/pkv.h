@@ -581,8 +581,15 @@ PKV_API size_t pkv_decode_grouped_workspace_bytes(int32_t batch, int32_t num_hea
  * plain call's handling of refused lengths); out-of-range sequence indices
  * in a tile are skipped.  A prefix block id outside [0, num_blocks) makes
  * the tile's members NaN.  With num_tiles = 0 the call runs
- * pkv_attention_decode's kernels (seq_prefix_blocks is not read).  Every
- * other argument is that of pkv_attention_decode; workspace:
+ * pkv_attention_decode's kernels (seq_prefix_blocks is not read).  When the
+ * decode work-groups are fewer than the device's compute units (the
+ * automatic count is), hold 4 or 8 wavefronts (32 heads
+ * of 128, for instance) and batch is at most 1024 per head slice, the prefix
+ * work runs in the decode launch, in work-groups placed after the decode
+ * ones; otherwise it has a launch of its own before the decode launch.  The
+ * two ways split the prefix differently (results agree within rounding;
+ * each is deterministic for given arguments and device).  Every other
+ * argument is that of pkv_attention_decode; workspace:
  * pkv_decode_grouped_workspace_bytes. */
 PKV_API int pkv_attention_decode_grouped(void* out, const void* q, const void* k_cache, const void* v_cache,
                                          const int32_t* block_tables, int32_t max_blocks_per_seq,
@@ -604,8 +611,9 @@ PKV_API int pkv_attention_decode_grouped(void* out, const void* q, const void* k
  * cache_dtype I8 or FP8_E4M3; k_scales, v_scales as for
  * pkv_attention_decode_quant; seq_prefix_blocks, tiles, num_tiles as for
  * pkv_attention_decode_grouped; workspace:
- * pkv_decode_grouped_workspace_bytes with dtype = cache_dtype.  Every other
- * argument is that of pkv_attention_decode_quant. */
+ * pkv_decode_grouped_workspace_bytes with dtype = cache_dtype.  The prefix
+ * work always has a launch of its own here.  Every other argument is that of
+ * pkv_attention_decode_quant. */
 PKV_API int pkv_attention_decode_grouped_quant(void* out, const void* q, const void* k_cache, const void* v_cache,
                                                const float* k_scales, const float* v_scales,
                                                const int32_t* block_tables, int32_t max_blocks_per_seq,

@@ -476,7 +476,7 @@ int decode_grouped_q8(void* out, const void* q, const void* k_new, const void* v
           }
         }
       },
-      nullptr);  // the 8-bit ranges fill every compute unit: no fused launch
+      nullptr);  // two work-groups of 4 wavefronts per compute unit: prefix units would share them
 }
 
 }  // namespace

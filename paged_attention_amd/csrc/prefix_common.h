@@ -378,16 +378,19 @@ __global__ void __launch_bounds__(kPrefixWaves * 64) prefix_kernel(DecodeArgs a,
 // A grouped call's decode and prefix work in one grid.  Work-groups
 // [0, a.grid_decode) take the stream-K ranges of the sequences' own
 // positions, as decode_kernel; the ones after them take the prefix units,
-// blockDim.x / (kPrefixWaves * 64) units each (unit u: tile part u / H, head
-// u % H), into the same partial prefix states as prefix_kernel.  Neither half
-// reads what the other writes: the merge kernel, launched after, combines
-// them.  Work-groups start in index order, so the ranges are resident first,
-// and the fused kernel's register count (the prefix body's) leaves no room
-// for a second work-group beside a range's: prefix units run on the compute
-// units the ranges leave free instead of slowing a range down.
-constexpr int kFusedMaxWaves = 8;  // work-groups of 4 or 8 wavefronts: one or two prefix units
-template <class KV, class PF, int D, int BS, int MODE>
-__global__ void __launch_bounds__(kFusedMaxWaves * 64)
+// NSUB units each (unit u: tile part u / H, head u % H; NSUB * kPrefixWaves
+// wavefronts are the decode work-group's, and the host launches only such
+// shapes), into the same partial prefix states as prefix_kernel.  Neither
+// half reads what the other writes: the merge kernel, launched after,
+// combines them.  Work-groups start in index order, so the ranges are
+// resident first, and the fused kernel's register count (the prefix body's)
+// lets a compute unit hold one work-group of 8 wavefronts: with fewer ranges
+// than compute units, prefix units run on the units the ranges leave free
+// instead of sharing a compute unit's issue slots with a range.  (8-bit
+// caches run two 4-wavefront ranges per compute unit, so a prefix unit
+// could only share one; they keep the separate prefix launch.)
+template <class KV, class PF, int D, int BS, int MODE, int NSUB>
+__global__ void __launch_bounds__(NSUB * kPrefixWaves * 64)
     grouped_decode_kernel(DecodeArgs a, const int32_t* tiles, int32_t prefix_units) {
   const int g = static_cast<int>(blockIdx.x);
   if (g < a.grid_decode) {
@@ -395,10 +398,8 @@ __global__ void __launch_bounds__(kFusedMaxWaves * 64)
     return;
   }
   constexpr int kUnitThreads = kPrefixWaves * 64;
-  constexpr int NSUB = kFusedMaxWaves / kPrefixWaves;
-  const int nsub = static_cast<int>(blockDim.x) / kUnitThreads;  // the host launches whole units
   const int sub = static_cast<int>(threadIdx.x) / kUnitThreads;
-  const int64_t u = static_cast<int64_t>(g - a.grid_decode) * nsub + sub;
+  const int64_t u = static_cast<int64_t>(g - a.grid_decode) * NSUB + sub;
   const bool live = u < prefix_units;
   const int uu = live ? static_cast<int>(u) : 0;
   prefix_unit<PF, D, BS, NSUB>(a, tiles, uu / a.num_heads, uu % a.num_heads, sub,
@@ -433,10 +434,14 @@ void launch_prefix(const DecodeArgs& a, int32_t bs, const int32_t* tiles, int32_
 template <class KV, class PF, int D, int BS, int MODE>
 void launch_fused_g(const DecodeArgs& a, const int32_t* tiles, int32_t units, hipStream_t stream,
                     const pkv::CallEvents& tm) {
-  const int nsub = a.waves_per_group / kPrefixWaves;
-  const int grid = a.grid_decode + (units + nsub - 1) / nsub;
-  hipExtLaunchKernelGGL((grouped_decode_kernel<KV, PF, D, BS, MODE>), dim3(grid), dim3(a.waves_per_group * 64),
-                        decode_lds_bytes(a, true), stream, tm.start, nullptr, 0, a, tiles, units);
+  const dim3 block(a.waves_per_group * 64);
+  const size_t lds = decode_lds_bytes(a, true);
+  if (a.waves_per_group == 2 * kPrefixWaves)
+    hipExtLaunchKernelGGL((grouped_decode_kernel<KV, PF, D, BS, MODE, 2>), dim3(a.grid_decode + (units + 1) / 2),
+                          block, lds, stream, tm.start, nullptr, 0, a, tiles, units);
+  else
+    hipExtLaunchKernelGGL((grouped_decode_kernel<KV, PF, D, BS, MODE, 1>), dim3(a.grid_decode + units), block, lds,
+                          stream, tm.start, nullptr, 0, a, tiles, units);
   launch_merge<KV, D, MODE, true>(a, stream, tm.stop);
 }
 
@@ -463,6 +468,15 @@ void launch_fused(const DecodeArgs& a, int32_t bs, int32_t d, const int32_t* til
 constexpr int32_t kFusedMaxVirtual = 1024;
 // Prefix units of one fused launch at most (the grid stays far from any limit).
 constexpr int64_t kFusedMaxUnits = int64_t{1} << 24;
+constexpr int kFusedMaxWaves = 2 * kPrefixWaves;  // work-groups of one or two prefix units
+
+// Whether a grouped call of this shape and batch can run its prefix units in
+// the decode launch: work-groups of whole prefix units, one launch.
+inline bool fusable_shape(int32_t batch, int32_t num_heads, int32_t head_dim, pkv_dtype cache_dtype) {
+  const Shape sh = decode_shape(num_heads, head_dim, cache_dtype);
+  return sh.wpg % kPrefixWaves == 0 && sh.wpg <= kFusedMaxWaves &&
+         static_cast<int64_t>(batch) * sh.groups_y <= kFusedMaxVirtual;
+}
 
 inline int check_grouped_sizes(const char* what, int32_t batch, int32_t num_heads, int32_t head_dim,
                                int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
@@ -483,9 +497,9 @@ inline int check_grouped_sizes(const char* what, int32_t batch, int32_t num_head
 // args, events)).
 //
 // Fused when the ranges leave compute units free (fewer work-groups than
-// compute units), the whole batch fits one launch and every work-group holds
-// whole prefix units: the prefix then costs no time of its own where it
-// fits beside the ranges.  Its parts per (tile, head) are then chosen so
+// compute units), the whole batch fits one launch and every work-group
+// holds whole prefix units: the prefix then costs no time of its own where
+// it fits beside the ranges.  Its parts per (tile, head) are then chosen so
 // that the units cover the free compute units' slots (at least one part);
 // otherwise they give the separate prefix launch two work-groups per compute
 // unit.
@@ -513,11 +527,9 @@ int run_grouped(DecodeArgs& a, int wg, void* out, const void* q, const int32_t* 
                                 kPrefixPartsMax, (slots + units - 1) / units)));
   };
   if constexpr (!std::is_same_v<LaunchFused, std::nullptr_t>) {
-    const int nsub = a.waves_per_group / kPrefixWaves;
-    if (num_tiles > 0 && cus > wg && nsub >= 1 && a.waves_per_group % kPrefixWaves == 0 &&
-        a.waves_per_group <= kFusedMaxWaves &&
-        static_cast<int64_t>(batch) * a.groups_y <= kFusedMaxVirtual) {
-      a.prefix_parts = parts_for(static_cast<int64_t>(cus - wg) * nsub);
+    const int64_t free_slots = static_cast<int64_t>(cus) - wg;  // compute units no range takes
+    if (num_tiles > 0 && free_slots > 0 && fusable_shape(batch, num_heads, head_dim, cache_dtype)) {
+      a.prefix_parts = parts_for(free_slots * (a.waves_per_group / kPrefixWaves));
       const int64_t prefix_units = units * a.prefix_parts;
       if (prefix_units <= kFusedMaxUnits) {
         a.batch = batch;

@@ -142,35 +142,39 @@ def test_batch_slices_with_groups():
 # ---- decode ranges and prefix units in one launch ----------------------------
 # A 16-bit grouped call whose decode work-groups are fewer than the compute
 # units, hold 4 or 8 wavefronts and whose batch fits one launch runs its
-# prefix units in the same grid, after the ranges; otherwise the prefix has a
-# launch of its own.  Both must meet the decode bound against the oracle.
-# Counts below the compute units take the one-launch path (with more parts per
-# tile and head the more units are free); counts at or above it the other.
-# 31 heads of 128 in three tiles: 8 wavefronts (two units per work-group) and
-# an odd number of units at one part, so the last work-group holds one unit
-# and an idle half.
+# prefix units in the same grid, after the ranges; otherwise (and always for
+# 8-bit caches) the prefix has a launch of its own.  Both must meet the
+# decode bound against the oracle.  Counts below the compute units take the
+# one-launch path (with more parts per tile and head the more units are
+# free); counts at or above it the other.  Shapes with an odd head count in
+# three tiles give an odd number of units at one part: with 8 wavefronts the
+# last work-group holds one unit and an idle half.  The 8-bit shapes run the
+# same counts through the two-launch path.
 
-ONE_LAUNCH_SHAPES = [("f16", 32, 128, 16), ("bf16", 16, 128, 8), ("f16", 32, 64, 32), ("bf16", 31, 128, 16)]
+ONE_LAUNCH_SHAPES = [("dense", "f16", 32, 128, 16), ("dense", "bf16", 16, 128, 8), ("dense", "f16", 32, 64, 32),
+                     ("dense", "bf16", 31, 128, 16), ("fp8", "f16", 32, 128, 16), ("i8", "bf16", 64, 64, 8),
+                     ("fp8", "bf16", 61, 128, 32), ("i8", "f16", 29, 128, 16)]
 
 
 def _cus():
     return torch.cuda.get_device_properties(0).multi_processor_count
 
 
-@pytest.mark.parametrize("dtype,num_heads,head_dim,block_size", ONE_LAUNCH_SHAPES)
-def test_one_launch_grouped_matches_oracle(dtype, num_heads, head_dim, block_size):
+@pytest.mark.parametrize("kv,dtype,num_heads,head_dim,block_size", ONE_LAUNCH_SHAPES)
+def test_one_launch_grouped_matches_oracle(kv, dtype, num_heads, head_dim, block_size):
     lens = LENS + [200 + 7 * i for i in range(30)]
     sharers = SHARERS + list(range(len(LENS), len(LENS) + 30))  # 37 sharers: three tiles
     wl = workloads.custom(lens, num_heads=num_heads, head_dim=head_dim, dtype=dtype, block_size=block_size,
                           seed=num_heads + head_dim + block_size, prefix_len=40, sharers=sharers)
-    c = pc.build(wl, DEV)
+    c = pc.build(wl, DEV, kv=kv)
     ref = pc.oracle_out(c)
     spb, tiles = pkv.prefix_tiles(c.tables_np, wl.seq_lens, block_size)
     assert len(tiles) == 3 and spb[sharers].min() == 40 // block_size
     cus = _cus()
+    run = _grouped if kv == "dense" else _grouped_quant
     for wg in (0, 3, 50, cus - 8, cus - 1, cus, cus + 44):
-        _log(f"one-launch grouped {dtype} H={num_heads} D={head_dim} BS={block_size} work_groups={wg}")
-        out, _, _ = _grouped(c, wg, spb, tiles)
+        _log(f"one-launch grouped {kv} {dtype} H={num_heads} D={head_dim} BS={block_size} work_groups={wg}")
+        out, _, _ = run(c, wg, spb, tiles)
         pc.compare(c, out, ref)
         _poison_newest(c)
         out = _grouped_fused(c, wg, spb, tiles)
