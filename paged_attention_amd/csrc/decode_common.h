@@ -431,10 +431,19 @@ enum DecodeMode { kPlain = 0, kAppend = 1, kScores = 2 };
 // reading it back with the same lanes: no other work-group is involved.
 // decode_body is the work of one of the `grid` work-groups that share the
 // chunks (work-group g); decode_kernel runs it over its whole grid.
-template <class KV, int D, int BS, int MODE, bool GROUPED>
+//
+// With DUAL the work-group holds two chunk streams of waves_per_group
+// wavefronts each: stream s takes the chunks s, s + 2, s + 4, ... of every
+// segment of its range, and at the segment's end stream 1 hands its state to
+// stream 0 through LDS, which folds it in and writes the piece or the row.
+// So one work-group of 8 wavefronts does what two of 4 did, with one range
+// (and at most one piece per segment) instead of two.
+template <class KV, int D, int BS, int MODE, bool GROUPED, bool DUAL = false>
 __device__ __forceinline__ void decode_body(const DecodeArgs& a, const int grid, const int g) {
   constexpr bool APPEND = MODE == kAppend;
   constexpr bool SCORES = MODE == kScores;
+  static_assert(!(DUAL && SCORES), "the score variant stages logits per chunk group: one stream");
+  constexpr int NSTREAM = DUAL ? 2 : 1;
   constexpr int EPL = KV::EPL;
   constexpr int LPH = D / EPL;   // lanes holding one head's row
   constexpr int HPW = 64 / LPH;  // heads per wavefront
@@ -448,6 +457,9 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, const int grid,
   __shared__ int32_t s_waves[kMaxWaves + 1];
   // score variant: one staged logit group per head slot of every wavefront
   __shared__ __align__(16) float s_logits[SCORES ? KV::kMaxWaves * HPW * kLogitGroup : 4];
+  // DUAL: stream 1's (acc[EPL], m, l) per lane of each of its wavefronts, element-major
+  constexpr int kDualWaves = KV::kMaxWaves / 2;
+  __shared__ float s_dual[DUAL ? (EPL + 2) * kDualWaves * 64 : 1];
   const int nv = a.batch * a.groups_y;
   int32_t* s_pref = s_dyn;           // [nv + 1]: first chunk of each virtual sequence
   int32_t* s_part = s_dyn + nv + 1;  // [nv + 1]: first partial slot of each virtual sequence
@@ -499,7 +511,13 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, const int grid,
     }
   }
 
-  const int wave = threadIdx.x >> 6;
+  // DUAL: the stream index is made uniform for the compiler (it bounds the
+  // chunk loop; a loop it took for divergent would wait for every load in
+  // flight at each turn)
+  const int wave_all = DUAL ? __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6))
+                            : static_cast<int>(threadIdx.x >> 6);
+  const int stream = DUAL ? wave_all / a.waves_per_group : 0;
+  const int wave = wave_all - stream * a.waves_per_group;  // head group in the slice
   const int lane = threadIdx.x & 63;
   const int r = lane / LPH;
   const int c = lane % LPH;
@@ -508,7 +526,7 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, const int grid,
 
   // 3. sequences with no chunks (length 0, or a length the table cannot
   // hold) are written here: zero rows, or NaN rows for an invalid length.
-  for (int v = g; v < nv; v += grid) {
+  for (int v = g; v < nv && stream == 0; v += grid) {
     if (s_pref[v + 1] != s_pref[v]) continue;
     const int b = v % a.batch, y = v / a.batch;
     const int h = (y * a.waves_per_group + wave) * HPW + r;
@@ -548,20 +566,50 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, const int grid,
     const int b = v % a.batch, y = v / a.batch;
     const int hg = y * a.waves_per_group + wave;
     const int h = hg * HPW + r;
-    if (hg * HPW < a.num_heads) {
-      const bool head_ok = h < a.num_heads;
-      const int hl = head_ok ? h : a.num_heads - 1;  // clamped head for loads
-      const int e0 = hl * D + c * EPL;                // this lane's first element of the row
+    const bool active = hg * HPW < a.num_heads;  // uniform per wavefront (and equal in both streams)
+    const bool head_ok = h < a.num_heads;
+    const int hl = head_ok ? h : a.num_heads - 1;  // clamped head for loads
+    const int e0 = hl * D + c * EPL;                // this lane's first element of the row
+    const int L = s_len[b];
+    const int start = start_of(b, L);
+    const int t_begin = start + static_cast<int>(cur - seq0) * kChunk;
+    const int t_end = min(L, start + static_cast<int>(seg_end - seq0) * kChunk);
+    // a piece of a sequence with a shared prefix never writes the output:
+    // the merge kernel adds the prefix's partial states
+    const bool whole = cur == seq0 && seg_end == seq1 && start == 0;
+    float m = -INFINITY, l = 0.f;
+    float acc[EPL];
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
+    // the output row (whole sequence) or the piece's partial state
+    auto finish = [&]() {
+      if (!head_ok) return;
+      if (SCORES && whole && c == 0) a.final_ml[static_cast<int64_t>(b) * a.num_heads + h] = make_float2(m, l);
+      if (whole) {
+        const float inv = 1.f / l;
+        float o[EPL];
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) o[e] = acc[e] * inv;
+        store_row<KV::QT, EPL>(static_cast<Elem*>(a.out) + b * q_row_bytes + e0 * QB, o);
+      } else {
+        const int piece = g - range_owner(seq0, nwg, total);
+        const int64_t slot = static_cast<int64_t>(s_part[v] + piece) * a.num_heads + h;
+        float* dst = a.ws_acc + slot * D + c * EPL;
+#pragma unroll
+        for (int e = 0; e < EPL; e += 4)
+          *reinterpret_cast<float4*>(dst + e) = make_float4(acc[e], acc[e + 1], acc[e + 2], acc[e + 3]);
+        if (c == 0) a.ws_ml[slot] = make_float2(m, l);
+      }
+    };
+    if (active) {
       const Elem* kp = static_cast<const Elem*>(a.k) + e0 * KB;
       const Elem* vp = static_cast<const Elem*>(a.v) + e0 * KB;
-      const int L = s_len[b];
-      const int start = start_of(b, L);
-      const int t_begin = start + static_cast<int>(cur - seq0) * kChunk;
-      const int t_end = min(L, start + static_cast<int>(seg_end - seq0) * kChunk);
       const int32_t* trow = a.tables + static_cast<int64_t>(b) * a.max_blocks;
       const typename KV::QReg qv = KV::load_q(static_cast<const Elem*>(a.q) + b * q_row_bytes + e0 * QB);
       if constexpr (APPEND) {
-        if (head_ok && seg_end == seq1 && L >= 1) {
+        // stored by the stream that reads position L - 1 back
+        const bool mine = !DUAL || (((L - 1 - t_begin) / kChunk) & 1) == stream;
+        if (head_ok && seg_end == seq1 && L >= 1 && mine) {
           const int pos = L - 1;
           const int32_t id = trow[pos / BS];
           if (static_cast<uint32_t>(id) < static_cast<uint32_t>(a.num_blocks))
@@ -569,20 +617,13 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, const int grid,
         }
       }
 
-      // a piece of a sequence with a shared prefix never writes the output:
-      // the merge kernel adds the prefix's partial states
-      const bool whole = cur == seq0 && seg_end == seq1 && start == 0;
-      float m = -INFINITY, l = 0.f;
-      float acc[EPL];
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
       bool bad_block = false;
       float* lrow = SCORES && head_ok ? a.logits + (static_cast<int64_t>(b) * a.num_heads + h) * a.logit_stride
                                       : nullptr;
       float* lslot = SCORES ? s_logits + (wave * HPW + r) * kLogitGroup : nullptr;
       int win = -kTableWindow;  // first block index held in `tbl`
       int32_t tbl = 0;
-      for (int t0 = t_begin; t0 < t_end; t0 += kChunk) {
+      for (int t0 = t_begin + stream * kChunk; t0 < t_end; t0 += NSTREAM * kChunk) {
         const int j = t0 / BS;
         if (j - win >= kTableWindow) {  // next window of block ids, one per lane, each checked once
           win = j;
@@ -604,24 +645,36 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, const int grid,
         }
       }
       if (bad_block) l = __builtin_nanf("");
-      if (head_ok) {
-        if (SCORES && whole && c == 0) a.final_ml[static_cast<int64_t>(b) * a.num_heads + h] = make_float2(m, l);
-        if (whole) {
-          const float inv = 1.f / l;
-          float o[EPL];
+      if constexpr (!DUAL) finish();
+    }
+    if constexpr (DUAL) {
+      // stream 1's state to stream 0 (element-major, so that lanes store
+      // and load consecutive words), which folds it in:
+      //   M = max(m0, m1), l = l0 2^(m0 - M) + l1 2^(m1 - M), acc likewise;
+      // a stream with no chunk of the segment holds (-inf, 0, 0) and weighs 0
+      // (a NaN sum, from a bad block id, stays NaN).
+      float* s_x = s_dual + wave * 64 + lane;
+      constexpr int kStride = kDualWaves * 64;
+      if (active && stream == 1) {
 #pragma unroll
-          for (int e = 0; e < EPL; ++e) o[e] = acc[e] * inv;
-          store_row<KV::QT, EPL>(static_cast<Elem*>(a.out) + b * q_row_bytes + e0 * QB, o);
-        } else {
-          const int piece = g - range_owner(seq0, nwg, total);
-          const int64_t slot = static_cast<int64_t>(s_part[v] + piece) * a.num_heads + h;
-          float* dst = a.ws_acc + slot * D + c * EPL;
-#pragma unroll
-          for (int e = 0; e < EPL; e += 4)
-            *reinterpret_cast<float4*>(dst + e) = make_float4(acc[e], acc[e + 1], acc[e + 2], acc[e + 3]);
-          if (c == 0) a.ws_ml[slot] = make_float2(m, l);
-        }
+        for (int e = 0; e < EPL; ++e) s_x[e * kStride] = acc[e];
+        s_x[EPL * kStride] = m;
+        s_x[(EPL + 1) * kStride] = l;
       }
+      __syncthreads();
+      if (active && stream == 0) {
+        const float m1 = s_x[EPL * kStride], l1 = s_x[(EPL + 1) * kStride];
+        const float mn = fmaxf(m, m1);
+        const float w0 = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - mn);
+        const float w1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - mn);
+        const bool nan = l != l || l1 != l1;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[e] = acc[e] * w0 + s_x[e * kStride] * w1;
+        l = nan ? __builtin_nanf("") : l * w0 + l1 * w1;
+        m = mn;
+        finish();
+      }
+      __syncthreads();  // the next segment's hand-over reuses the buffer
     }
     cur = seg_end;
     if (cur < last) {
@@ -631,9 +684,9 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, const int grid,
   }
 }
 
-template <class KV, int D, int BS, int MODE, bool GROUPED>
+template <class KV, int D, int BS, int MODE, bool GROUPED, bool DUAL>
 __global__ void __launch_bounds__(KV::kMaxWaves * 64) decode_kernel(DecodeArgs a) {
-  decode_body<KV, D, BS, MODE, GROUPED>(a, static_cast<int>(gridDim.x), static_cast<int>(blockIdx.x));
+  decode_body<KV, D, BS, MODE, GROUPED, DUAL>(a, static_cast<int>(gridDim.x), static_cast<int>(blockIdx.x));
 }
 
 // Merges the pieces of every cut sequence, after the partial states of its
@@ -917,22 +970,31 @@ inline int32_t device_compute_units() {
   return cus;
 }
 
-// Work-groups of the automatic choice on the current device.  Measured on
-// MI355X with 16-bit caches (µs per call, 160 / 192 / 208 / 224 / 240 / 256
-// work-groups of 8 wavefronts): 7B-shaped layer 104.9 / 99.8 / 99.5 / 98.7 /
-// 99.8 / 99.8, 13B long context 229.7 / 216.6 / 215.5 / 214.4 / 214.8 /
-// 216.0; 512 read 5 % slower than 256.  Fewer, longer streams keep more DRAM
-// pages open per request until too few remain to cover the latency: seven
-// eighths of the compute units (28 of the 32 of each XCD, as the dispatcher
-// deals work-groups to the XCDs in turn) is the best of the sweep.  8-bit
-// caches carry twice the elements per byte and run 4 wavefronts per
-// work-group for 32 heads, so they take two work-groups per compute unit to
-// keep the same wavefronts resident (FP8 7B layer 416 / 448 / 480 / 512:
-// 67.4 / 66.9 / 67.1 / 66.2 µs).
+// Chunk streams of the automatic choice on the current device (a stream is
+// one work-group's set of wavefronts over the heads; see chunk_streams for
+// 8-bit caches).  Measured on MI355X with 16-bit caches (µs per call, 160 /
+// 192 / 208 / 224 / 240 / 256 work-groups of 8 wavefronts): 7B-shaped layer
+// 104.9 / 99.8 / 99.5 / 98.7 / 99.8 / 99.8, 13B long context 229.7 / 216.6 /
+// 215.5 / 214.4 / 214.8 / 216.0; 512 read 5 % slower than 256.  Fewer,
+// longer streams keep more DRAM pages open per request until too few remain
+// to cover the latency: seven eighths of the compute units (28 of the 32 of
+// each XCD, as the dispatcher deals work-groups to the XCDs in turn) is the
+// best of the sweep.  8-bit caches carry twice the elements per byte and
+// run 4 wavefronts per stream for 32 heads, so they take two streams per
+// compute unit to keep the same wavefronts resident.
 inline int32_t auto_work_groups(pkv_dtype cache_dtype) {
   const int32_t cus = device_compute_units();
   if (cus <= 0) return cus;
-  return is_8bit(cache_dtype) ? 2 * cus : std::max<int32_t>(1, cus - cus / 8);
+  const int32_t per_cu = is_8bit(cache_dtype) ? 2 : 1;
+  return std::max<int32_t>(1, per_cu * (cus - cus / 8));
+}
+
+// Chunk streams per decode work-group outside the score variant: 8-bit
+// caches run two streams of 4 wavefronts in one work-group of 8 when both
+// fit (decode_body's DUAL), so the automatic 448 streams take 224 work-groups
+// and leave the same compute units free as 16-bit caches do.
+inline int chunk_streams(pkv_dtype cache_dtype, int waves_per_group) {
+  return is_8bit(cache_dtype) && 2 * waves_per_group <= max_waves_for(cache_dtype) ? 2 : 1;
 }
 
 inline int check_launch(const char* what) {
@@ -1010,10 +1072,22 @@ void launch_merge(const DecodeArgs& a, hipStream_t stream, hipEvent_t stop) {
                           dim3(kMergeWaves * 64), 0, stream, nullptr, stop, 0, a);
 }
 
+// `wg` counts chunk streams; a format with two streams per work-group
+// (KV::kDual, outside the score variant, when both fit a work-group) runs
+// them in ceil(wg / 2) work-groups of twice the wavefronts.
 template <class KV, int D, int BS, int MODE, bool GROUPED>
 void launch_decode_g(const DecodeArgs& a, int wg, hipStream_t stream, const pkv::CallEvents& tm) {
-  hipExtLaunchKernelGGL((decode_kernel<KV, D, BS, MODE, GROUPED>), dim3(wg), dim3(a.waves_per_group * 64),
-                        decode_lds_bytes(a, GROUPED), stream, tm.start, nullptr, 0, a);
+  const size_t lds = decode_lds_bytes(a, GROUPED);
+  if constexpr (KV::kDual && MODE != kScores) {
+    if (2 * a.waves_per_group <= KV::kMaxWaves) {
+      hipExtLaunchKernelGGL((decode_kernel<KV, D, BS, MODE, GROUPED, true>), dim3((wg + 1) / 2),
+                            dim3(2 * a.waves_per_group * 64), lds, stream, tm.start, nullptr, 0, a);
+      launch_merge<KV, D, MODE, GROUPED>(a, stream, tm.stop);
+      return;
+    }
+  }
+  hipExtLaunchKernelGGL((decode_kernel<KV, D, BS, MODE, GROUPED, false>), dim3(wg), dim3(a.waves_per_group * 64),
+                        lds, stream, tm.start, nullptr, 0, a);
   launch_merge<KV, D, MODE, GROUPED>(a, stream, tm.stop);
 }
 

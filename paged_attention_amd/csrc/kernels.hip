@@ -49,6 +49,7 @@ struct DenseKV {
   static constexpr int EPL = 16 / KB;
   static constexpr int kMaxWaves = ::kMaxWaves;
   static constexpr bool kGrouped = true;  // pkv_attention_decode_grouped uses this policy
+  static constexpr bool kDual = false;    // one chunk stream per work-group
   using QReg = Vec16;
 
   __device__ static Vec16 load_q(const uint8_t* p) { return *reinterpret_cast<const Vec16*>(p); }
@@ -189,14 +190,14 @@ int decode_grouped(void* out, const void* q, const void* k_new, const void* v_ne
         using B16 = DenseKV<PKV_BF16>;
         if (k_new != nullptr) {
           if (dtype == PKV_F16)
-            launch_fused<F16, PrefixDense<PKV_F16>, kAppend>(s, block_size, head_dim, tiles, units, stream, tm);
+            return launch_fused<F16, PrefixDense<PKV_F16>, kAppend>(s, block_size, head_dim, tiles, units, stream, tm);
           else
-            launch_fused<B16, PrefixDense<PKV_BF16>, kAppend>(s, block_size, head_dim, tiles, units, stream, tm);
+            return launch_fused<B16, PrefixDense<PKV_BF16>, kAppend>(s, block_size, head_dim, tiles, units, stream, tm);
         } else {
           if (dtype == PKV_F16)
-            launch_fused<F16, PrefixDense<PKV_F16>, kPlain>(s, block_size, head_dim, tiles, units, stream, tm);
+            return launch_fused<F16, PrefixDense<PKV_F16>, kPlain>(s, block_size, head_dim, tiles, units, stream, tm);
           else
-            launch_fused<B16, PrefixDense<PKV_BF16>, kPlain>(s, block_size, head_dim, tiles, units, stream, tm);
+            return launch_fused<B16, PrefixDense<PKV_BF16>, kPlain>(s, block_size, head_dim, tiles, units, stream, tm);
         }
       });
 }

@@ -128,6 +128,7 @@ struct Q8KV {
   static constexpr int EPL = 16;
   static constexpr int kMaxWaves = 8;
   static constexpr bool kGrouped = true;   // pkv_attention_decode_grouped_quant uses this policy
+  static constexpr bool kDual = true;      // two chunk streams of 4 wavefronts per work-group where they fit
   // q.k on 16-bit pairs (see qk16).
   static constexpr bool kPairQK = K == PKV_FP8_E4M3 && (Q == PKV_F16 || Q == PKV_BF16);
   struct QReg {
@@ -476,7 +477,34 @@ int decode_grouped_q8(void* out, const void* q, const void* k_new, const void* v
           }
         }
       },
-      nullptr);  // two work-groups of 4 wavefronts per compute unit: prefix units would share them
+      [&](const DecodeArgs& s, const pkv::CallEvents& tm, int32_t units) {
+        const int32_t bs = block_size, d = head_dim;
+        if (k_new != nullptr) {
+          if (q_dtype == PKV_F16) {
+            if (fp8) return launch_fused<Q8KV<PKV_F16, PKV_FP8_E4M3>, PrefixQ8<PKV_F16, PKV_FP8_E4M3>, kAppend>(
+                         s, bs, d, tiles, units, stream, tm);
+            else return launch_fused<Q8KV<PKV_F16, PKV_I8>, PrefixQ8<PKV_F16, PKV_I8>, kAppend>(s, bs, d, tiles, units,
+                                                                                         stream, tm);
+          } else {
+            if (fp8) return launch_fused<Q8KV<PKV_BF16, PKV_FP8_E4M3>, PrefixQ8<PKV_BF16, PKV_FP8_E4M3>, kAppend>(
+                         s, bs, d, tiles, units, stream, tm);
+            else return launch_fused<Q8KV<PKV_BF16, PKV_I8>, PrefixQ8<PKV_BF16, PKV_I8>, kAppend>(s, bs, d, tiles, units,
+                                                                                           stream, tm);
+          }
+        } else {
+          if (q_dtype == PKV_F16) {
+            if (fp8) return launch_fused<Q8KV<PKV_F16, PKV_FP8_E4M3>, PrefixQ8<PKV_F16, PKV_FP8_E4M3>, kPlain>(
+                         s, bs, d, tiles, units, stream, tm);
+            else return launch_fused<Q8KV<PKV_F16, PKV_I8>, PrefixQ8<PKV_F16, PKV_I8>, kPlain>(s, bs, d, tiles, units,
+                                                                                        stream, tm);
+          } else {
+            if (fp8) return launch_fused<Q8KV<PKV_BF16, PKV_FP8_E4M3>, PrefixQ8<PKV_BF16, PKV_FP8_E4M3>, kPlain>(
+                         s, bs, d, tiles, units, stream, tm);
+            else return launch_fused<Q8KV<PKV_BF16, PKV_I8>, PrefixQ8<PKV_BF16, PKV_I8>, kPlain>(s, bs, d, tiles, units,
+                                                                                          stream, tm);
+          }
+        }
+      });
 }
 
 }  // namespace

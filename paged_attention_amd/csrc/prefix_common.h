@@ -387,14 +387,16 @@ __global__ void __launch_bounds__(kPrefixWaves * 64) prefix_kernel(DecodeArgs a,
 // lets a compute unit hold one work-group of 8 wavefronts: with fewer ranges
 // than compute units, prefix units run on the units the ranges leave free
 // instead of sharing a compute unit's issue slots with a range.  (8-bit
-// caches run two 4-wavefront ranges per compute unit, so a prefix unit
-// could only share one; they keep the separate prefix launch.)
-template <class KV, class PF, int D, int BS, int MODE, int NSUB>
+// caches get there with both chunk streams of a range in one work-group of
+// 8 wavefronts: 224 ranges for the automatic 448 streams.)
+// DUAL: the ranges run two chunk streams (decode_body), as the plain launch
+// of the same shape does.
+template <class KV, class PF, int D, int BS, int MODE, int NSUB, bool DUAL>
 __global__ void __launch_bounds__(NSUB * kPrefixWaves * 64)
     grouped_decode_kernel(DecodeArgs a, const int32_t* tiles, int32_t prefix_units) {
   const int g = static_cast<int>(blockIdx.x);
   if (g < a.grid_decode) {
-    decode_body<KV, D, BS, MODE, true>(a, a.grid_decode, g);
+    decode_body<KV, D, BS, MODE, true, DUAL>(a, a.grid_decode, g);
     return;
   }
   constexpr int kUnitThreads = kPrefixWaves * 64;
@@ -431,35 +433,51 @@ void launch_prefix(const DecodeArgs& a, int32_t bs, const int32_t* tiles, int32_
 
 // A grouped call's decode and prefix work in one launch (grouped_decode_kernel,
 // `units` prefix units after the a.grid_decode ranges), then the merge.
+template <class KV, class PF, int D, int BS, int MODE, int NSUB, bool DUAL>
+void launch_fused_k(const DecodeArgs& a, const int32_t* tiles, int32_t units, hipStream_t stream, hipEvent_t start) {
+  hipExtLaunchKernelGGL((grouped_decode_kernel<KV, PF, D, BS, MODE, NSUB, DUAL>),
+                        dim3(a.grid_decode + (units + NSUB - 1) / NSUB), dim3(NSUB * kPrefixWaves * 64),
+                        decode_lds_bytes(a, true), stream, start, nullptr, 0, a, tiles, units);
+}
+
+// The work-group holds the ranges' wavefronts: waves_per_group per stream,
+// two streams where the plain launch of the shape runs two (launch_decode_g's
+// rule).  Only totals of 4 or 8 wavefronts (one or two prefix units) are
+// launched; run_grouped offers no other shape (fusable_shape).
 template <class KV, class PF, int D, int BS, int MODE>
-void launch_fused_g(const DecodeArgs& a, const int32_t* tiles, int32_t units, hipStream_t stream,
-                    const pkv::CallEvents& tm) {
-  const dim3 block(a.waves_per_group * 64);
-  const size_t lds = decode_lds_bytes(a, true);
-  if (a.waves_per_group == 2 * kPrefixWaves)
-    hipExtLaunchKernelGGL((grouped_decode_kernel<KV, PF, D, BS, MODE, 2>), dim3(a.grid_decode + (units + 1) / 2),
-                          block, lds, stream, tm.start, nullptr, 0, a, tiles, units);
-  else
-    hipExtLaunchKernelGGL((grouped_decode_kernel<KV, PF, D, BS, MODE, 1>), dim3(a.grid_decode + units), block, lds,
-                          stream, tm.start, nullptr, 0, a, tiles, units);
+int launch_fused_g(const DecodeArgs& a, const int32_t* tiles, int32_t units, hipStream_t stream,
+                   const pkv::CallEvents& tm) {
+  const bool dual = KV::kDual && 2 * a.waves_per_group <= KV::kMaxWaves;
+  const int waves = a.waves_per_group * (dual ? 2 : 1);
+  if (waves != kPrefixWaves && waves != 2 * kPrefixWaves)
+    return pkv::fail(PKV_ERR_INVALID, "grouped decode: %d wavefronts per work-group in one launch", waves);
+  if (dual) {
+    if constexpr (KV::kDual) {
+      if (waves == 2 * kPrefixWaves) launch_fused_k<KV, PF, D, BS, MODE, 2, true>(a, tiles, units, stream, tm.start);
+      else launch_fused_k<KV, PF, D, BS, MODE, 1, true>(a, tiles, units, stream, tm.start);
+    }
+  } else {
+    if (waves == 2 * kPrefixWaves) launch_fused_k<KV, PF, D, BS, MODE, 2, false>(a, tiles, units, stream, tm.start);
+    else launch_fused_k<KV, PF, D, BS, MODE, 1, false>(a, tiles, units, stream, tm.start);
+  }
   launch_merge<KV, D, MODE, true>(a, stream, tm.stop);
+  return PKV_OK;
 }
 
 template <class KV, class PF, int MODE>
-void launch_fused(const DecodeArgs& a, int32_t bs, int32_t d, const int32_t* tiles, int32_t units, hipStream_t stream,
-                  const pkv::CallEvents& tm) {
+int launch_fused(const DecodeArgs& a, int32_t bs, int32_t d, const int32_t* tiles, int32_t units, hipStream_t stream,
+                 const pkv::CallEvents& tm) {
   if (d == 64) {
     switch (bs) {
-      case 8: launch_fused_g<KV, PF, 64, 8, MODE>(a, tiles, units, stream, tm); break;
-      case 16: launch_fused_g<KV, PF, 64, 16, MODE>(a, tiles, units, stream, tm); break;
-      default: launch_fused_g<KV, PF, 64, 32, MODE>(a, tiles, units, stream, tm); break;
+      case 8: return launch_fused_g<KV, PF, 64, 8, MODE>(a, tiles, units, stream, tm);
+      case 16: return launch_fused_g<KV, PF, 64, 16, MODE>(a, tiles, units, stream, tm);
+      default: return launch_fused_g<KV, PF, 64, 32, MODE>(a, tiles, units, stream, tm);
     }
-  } else {
-    switch (bs) {
-      case 8: launch_fused_g<KV, PF, 128, 8, MODE>(a, tiles, units, stream, tm); break;
-      case 16: launch_fused_g<KV, PF, 128, 16, MODE>(a, tiles, units, stream, tm); break;
-      default: launch_fused_g<KV, PF, 128, 32, MODE>(a, tiles, units, stream, tm); break;
-    }
+  }
+  switch (bs) {
+    case 8: return launch_fused_g<KV, PF, 128, 8, MODE>(a, tiles, units, stream, tm);
+    case 16: return launch_fused_g<KV, PF, 128, 16, MODE>(a, tiles, units, stream, tm);
+    default: return launch_fused_g<KV, PF, 128, 32, MODE>(a, tiles, units, stream, tm);
   }
 }
 
@@ -471,10 +489,12 @@ constexpr int64_t kFusedMaxUnits = int64_t{1} << 24;
 constexpr int kFusedMaxWaves = 2 * kPrefixWaves;  // work-groups of one or two prefix units
 
 // Whether a grouped call of this shape and batch can run its prefix units in
-// the decode launch: work-groups of whole prefix units, one launch.
+// the decode launch: work-groups (both chunk streams) of whole prefix units,
+// one launch.
 inline bool fusable_shape(int32_t batch, int32_t num_heads, int32_t head_dim, pkv_dtype cache_dtype) {
   const Shape sh = decode_shape(num_heads, head_dim, cache_dtype);
-  return sh.wpg % kPrefixWaves == 0 && sh.wpg <= kFusedMaxWaves &&
+  const int waves = sh.wpg * chunk_streams(cache_dtype, sh.wpg);
+  return waves % kPrefixWaves == 0 && waves <= kFusedMaxWaves &&
          static_cast<int64_t>(batch) * sh.groups_y <= kFusedMaxVirtual;
 }
 
@@ -496,9 +516,10 @@ inline int check_grouped_sizes(const char* what, int32_t batch, int32_t num_head
 // decode and merge launches over slices of the batch (launch_decode_fn(slice
 // args, events)).
 //
-// Fused when the ranges leave compute units free (fewer work-groups than
-// compute units), the whole batch fits one launch and every work-group
-// holds whole prefix units: the prefix then costs no time of its own where
+// Fused when the ranges leave compute units free (fewer decode work-groups,
+// i.e. streams over chunk_streams, than compute units), the whole batch
+// fits one launch and every work-group holds whole prefix units: the prefix
+// then costs no time of its own where
 // it fits beside the ranges.  Its parts per (tile, head) are then chosen so
 // that the units cover the free compute units' slots (at least one part);
 // otherwise they give the separate prefix launch two work-groups per compute
@@ -527,9 +548,12 @@ int run_grouped(DecodeArgs& a, int wg, void* out, const void* q, const int32_t* 
                                 kPrefixPartsMax, (slots + units - 1) / units)));
   };
   if constexpr (!std::is_same_v<LaunchFused, std::nullptr_t>) {
-    const int64_t free_slots = static_cast<int64_t>(cus) - wg;  // compute units no range takes
+    const int streams = chunk_streams(cache_dtype, a.waves_per_group);
+    const int ranges = (wg + streams - 1) / streams;                 // decode work-groups
+    const int64_t free_slots = static_cast<int64_t>(cus) - ranges;  // compute units no range takes
     if (num_tiles > 0 && free_slots > 0 && fusable_shape(batch, num_heads, head_dim, cache_dtype)) {
-      a.prefix_parts = parts_for(free_slots * (a.waves_per_group / kPrefixWaves));
+      a.grid_decode = ranges;
+      a.prefix_parts = parts_for(free_slots * (streams * a.waves_per_group / kPrefixWaves));
       const int64_t prefix_units = units * a.prefix_parts;
       if (prefix_units <= kFusedMaxUnits) {
         a.batch = batch;
@@ -537,7 +561,8 @@ int run_grouped(DecodeArgs& a, int wg, void* out, const void* q, const int32_t* 
         a.q = q;
         a.tables = block_tables;
         a.lens = seq_lens;
-        launch_fused_fn(static_cast<const DecodeArgs&>(a), timing, static_cast<int32_t>(prefix_units));
+        const int fst = launch_fused_fn(static_cast<const DecodeArgs&>(a), timing, static_cast<int32_t>(prefix_units));
+        if (fst != PKV_OK) return fst;
         return check_launch(what);
       }
     }

@@ -102,6 +102,34 @@ def test_small_cases(fmt, dtype, head_dim, block_size):
         pc.compare(c, pc.run_gpu(c, work_groups=wg), ref)
 
 
+# Two chunk streams per work-group: where both sets of wavefronts fit a
+# work-group of 8 (32 heads of 128, 64 of 64), a range's chunks alternate
+# between them and stream 1 hands its state to stream 0 at every segment's
+# end; 33 heads of 128 (5 wavefronts) keep one stream.  Lengths put the last
+# chunk of a segment on either stream and give segments of one chunk (stream
+# 1 idle); counts from one range (every sequence a segment of it) up.  The
+# fused append+decode call must store each new row from the stream that
+# reads it back: the pools come back bit-identical to the oracle's.
+DUAL_LENS = [1, 8, 9, 16, 17, 24, 25, 40, 333, 1000, 2, 64]
+
+
+@pytest.mark.parametrize("fmt,dtype,num_heads,head_dim", [("fp8", "f16", 32, 128), ("i8", "bf16", 64, 64),
+                                                         ("fp8", "f32", 32, 64), ("i8", "f16", 33, 128)])
+def test_two_chunk_streams_per_work_group(fmt, dtype, num_heads, head_dim):
+    from tests.test_gpu_fused import _assert_pools, _poison_newest, _run_fused
+    wl = workloads.custom(DUAL_LENS, num_heads=num_heads, head_dim=head_dim, dtype=dtype, block_size=16,
+                          seed=num_heads + head_dim)
+    c = pc.build(wl, DEV, kv=fmt)
+    ref = pc.oracle_out(c)
+    for wg in (1, 2, 3, 5, 24, 448, 512, 0):
+        _log(f"two streams {fmt} {dtype} H={num_heads} D={head_dim} work_groups={wg}")
+        pc.compare(c, pc.run_gpu(c, work_groups=wg), ref)
+        _poison_newest(c)
+        out = _run_fused(c, work_groups=wg)
+        _assert_pools(c)
+        pc.compare(c, out, ref)
+
+
 @pytest.mark.parametrize("fmt", ["i8", "fp8"])
 def test_many_heads_span_head_slices(fmt):
     # 160 heads x 128 at 8 heads per wavefront = 20 wavefronts: 3 head slices.
