@@ -299,11 +299,13 @@ PKV_API int pkv_swap_blocks(void* const* dst_pools, const void* const* src_pools
                             const int32_t* pairs, int32_t n_pairs, int32_t src_num_blocks, int32_t dst_num_blocks,
                             size_t bytes_per_block, hipStream_t stream);
 
-/* Work-groups a decode call launches when called with num_work_groups = 0,
+/* Chunk streams a decode call runs when called with num_work_groups = 0,
  * for caches of `cache_dtype`: seven eighths of the compute units of the
- * current device for F32/F16/BF16 caches (224 on MI355X), two per compute
- * unit for I8 and FP8_E4M3 caches (512).  PKV_ERR_HIP if no device is current, PKV_ERR_INVALID for
- * an unknown type. */
+ * current device for F32/F16/BF16 caches (224 on MI355X, one work-group
+ * each), seven eighths of two per compute unit for I8 and FP8_E4M3 caches
+ * (448, run two to a work-group where both fit, see
+ * pkv_attention_decode_quant).  PKV_ERR_HIP if no device is current,
+ * PKV_ERR_INVALID for an unknown type. */
 PKV_API int32_t pkv_decode_work_groups(pkv_dtype cache_dtype);
 
 /* Device workspace a decode call needs for `num_work_groups` (0 = the
@@ -440,8 +442,12 @@ PKV_API int pkv_append_quant(const void* k_new, const void* v_new, int32_t num_t
  * (F32, F16 or BF16); k_scales / v_scales the scale pools above;
  * cache_dtype I8 or FP8_E4M3; every other argument, the workspace
  * (pkv_decode_workspace_bytes with dtype = cache_dtype) and the handling of
- * bad lengths and block ids are those of pkv_attention_decode.  q, out,
- * pools and scale pools must be 16-byte aligned. */
+ * bad lengths and block ids are those of pkv_attention_decode, except that
+ * num_work_groups counts chunk streams: where two sets of the wavefronts
+ * that cover the heads fit one work-group of 8 (32 heads of 128, 64 of 64),
+ * the call runs ceil(num_work_groups / 2) work-groups whose two streams take
+ * alternate chunks of one range (the score variant keeps one stream per
+ * work-group).  q, out, pools and scale pools must be 16-byte aligned. */
 PKV_API int pkv_attention_decode_quant(void* out, const void* q, const void* k_cache, const void* v_cache,
                                        const float* k_scales, const float* v_scales,
                                        const int32_t* block_tables, int32_t max_blocks_per_seq,
@@ -612,7 +618,9 @@ PKV_API int pkv_attention_decode_grouped(void* out, const void* q, const void* k
  * pkv_attention_decode_quant; seq_prefix_blocks, tiles, num_tiles as for
  * pkv_attention_decode_grouped; workspace:
  * pkv_decode_grouped_workspace_bytes with dtype = cache_dtype.  The prefix
- * work always has a launch of its own here.  Every other argument is that of
+ * work runs in the decode launch under pkv_attention_decode_grouped's rule,
+ * counting the decode work-groups (two chunk streams each where they fit,
+ * as in pkv_attention_decode_quant).  Every other argument is that of
  * pkv_attention_decode_quant. */
 PKV_API int pkv_attention_decode_grouped_quant(void* out, const void* q, const void* k_cache, const void* v_cache,
                                                const float* k_scales, const float* v_scales,
