@@ -81,7 +81,9 @@ def parse():
                    help="layers per step, each with its own cache read in turn (0 = the workload's default: 4 for "
                         "the single-layer 7B and prefix workloads, so that no call finds the previous call's rows "
                         "in the Infinity Cache; 1 for long13b and tiny; 32 for full7b_step)")
-    p.add_argument("--work-groups", type=int, default=0, help="decode work-groups (0 = library choice)")
+    p.add_argument("--work-groups", type=int, default=0,
+                   help="decode chunk streams, i.e. work-groups for 16/32-bit caches and two per work-group for "
+                        "8-bit ones where both fit (0 = library choice)")
     p.add_argument("--ring", type=int, default=4, help="host staging buffers (how many steps the host may run ahead)")
     p.add_argument("--metadata", choices=["pinned", "device", "staged"], default="pinned",
                    help="where kernels read step metadata: pinned host memory in place, a device copy on the "
