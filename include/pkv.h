@@ -368,7 +368,7 @@ PKV_API int pkv_attention_decode(void* out, const void* q, const void* k_cache, 
  * same work split: bit-identical output for the same num_work_groups).
  * Sizes whose workspace (pkv_decode_workspace_bytes) would exceed
  * PKV_DECODE_SCRATCH_BYTES return PKV_ERR_INVALID and launch nothing (the
- * 7B shape, 32 heads x 128 at the automatic 256 work-groups, needs about 8.6
+ * 7B shape, 32 heads x 128 at the automatic 224 work-groups, needs about 7.5
  * MB).  The array is shared by every call on its device and keeps the last
  * call's contents (nothing in it needs clearing): calls that may overlap on
  * one device must go through one stream, in order.  The first call on a
