@@ -182,6 +182,26 @@ def test_one_launch_grouped_matches_oracle(kv, dtype, num_heads, head_dim, block
         pc.compare(c, out, ref)
 
 
+@pytest.mark.parametrize("kv,dtype", [("dense", "f16"), ("fp8", "bf16")])
+@pytest.mark.parametrize("batch", [1024, 1025])
+def test_one_launch_grouped_batch_limit(kv, dtype, batch):
+    # Up to 1024 sequences per head slice the prefix units share the decode
+    # launch; one more and the prefix has a launch of its own.  Both sides of
+    # the limit, 32 heads of 128 (8 wavefronts per work-group), against the
+    # oracle: groups of 40 sequences share a 32-token prefix.
+    rng = np.random.default_rng(batch)
+    lens = (33 + rng.integers(1, 40, size=batch)).tolist()
+    sharers = [b for b in range(batch) if b % 50 < 40]
+    wl = workloads.custom(lens, num_heads=32, head_dim=128, dtype=dtype, block_size=16, seed=batch,
+                          prefix_len=32, sharers=sharers)
+    c = pc.build(wl, DEV, kv=kv, check_pools=False)
+    spb, tiles = pkv.prefix_tiles(c.tables_np, wl.seq_lens, 16)
+    assert spb[sharers].min() == 2 and len(tiles) >= 2
+    run = _grouped if kv == "dense" else _grouped_quant
+    out, _, _ = run(c, 0, spb, tiles)
+    pc.compare(c, out)
+
+
 def test_one_launch_grouped_is_deterministic_and_reads_no_stale_state():
     # Two calls with the same arguments give the same bytes; a call after one
     # with other lengths (a different prefix share and parts) as well.
